@@ -1,0 +1,180 @@
+"""Throughput of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  attn_fwd -> attn_bwd (row pass, column pass; GProj on) -> attn_bob (row
+  pass, column pass), causal, on the BoB workload B=4, H=12, N=4096, d=64,
+  bf16 inputs with fp32 accumulation (Q, K, V, dO ~ 0.5 N(0,1), cotangents
+  ~ N(0,1), seeded).  Inputs are resident in device memory before timing.
+
+Prints ONE JSON line.  `value` is the step's model TFLOP/s under the FLOP
+convention (per unmasked causal (query, key) pair and head: forward 4d,
+backward 10d, backward-over-backward 38d); `roofline` is the dominant kernel's
+executed contraction FLOPs per launch over its HIP-event-timed duration against
+the bf16 dense MFMA peak; `cpu_baseline` is the fp64 oracle timed on a bounded
+sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBS = 8000.0
+METRIC = "attn fwd/bwd/BoB TFLOP/s & % bf16 MFMA peak, GPT-2S head shape, N≤262k"
+
+# Contraction units (N x N x d products, 2d FLOP per unmasked pair) executed
+# by each kernel; GProj adds one unit to each backward pass.
+UNITS = {"fwd": 2, "bwd_row": 4, "bwd_col": 5, "bob_row": 11, "bob_col": 8}
+# FLOP convention per unmasked pair, in units of d
+CONV = {"fwd": 4, "bwd": 10, "bob": 38}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=48,
+                   help="heads of the workload the oracle baseline runs on")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fwd_bwd_double_amd as fbd
+    import synthetic
+
+    w = synthetic.WORKLOADS[4]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = synthetic.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4))
+    ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
+    ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
+    sc = w.scale
+
+    names = ["fwd", "bwd_row", "bwd_col", "bob_row", "bob_col"]
+
+    def step(ev):
+        ev[0].record()
+        fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse)
+        ev[1].record()
+        fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=sc, gproj=True, workspace=ws_b,
+                     outs=(dq, dk, dv), passes=1)
+        ev[2].record()
+        fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=sc, gproj=True, workspace=ws_b,
+                     outs=(dq, dk, dv), passes=2)
+        ev[3].record()
+        fbd.attn_bob(q, k, v, o, lse, do, g["g_dq"], g["g_dk"], g["g_dv"], causal=True,
+                     scale=sc, workspace=ws_bb, outs=(gq, gk, gv, gdo), passes=1)
+        ev[4].record()
+        fbd.attn_bob(q, k, v, o, lse, do, g["g_dq"], g["g_dk"], g["g_dv"], causal=True,
+                     scale=sc, workspace=ws_bb, outs=(gq, gk, gv, gdo), passes=2)
+        ev[5].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+           for _ in range(max(args.steps, 1))]
+    for _ in range(args.warmup):
+        step(evs[0])
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    kern_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs[:args.steps]]))
+               for i, n in enumerate(names)}
+
+    pairs = B * H * N * (N + 1) / 2          # unmasked causal pairs over all heads
+    unit = 2 * d * pairs                     # FLOP of one N x N x d contraction unit
+    step_flop = sum(CONV.values()) * d * pairs
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    per_kernel = {n: {"ms": kern_ms[n],
+                      "executed_tflops": UNITS[n] * unit / (kern_ms[n] * 1e-3) / 1e12}
+                  for n in names}
+    for n in names:
+        per_kernel[n]["frac_mfma_peak"] = per_kernel[n]["executed_tflops"] / PEAK_BF16_TFLOPS
+    op_ms = {"fwd": kern_ms["fwd"], "bwd": kern_ms["bwd_row"] + kern_ms["bwd_col"],
+             "bob": kern_ms["bob_row"] + kern_ms["bob_col"]}
+    per_op = {op: {"ms": op_ms[op],
+                   "conv_tflops": CONV[op] * d * pairs / (op_ms[op] * 1e-3) / 1e12}
+              for op in op_ms}
+    for op in per_op:
+        per_op[op]["frac_mfma_peak"] = per_op[op]["conv_tflops"] / PEAK_BF16_TFLOPS
+    dom = max(names, key=lambda n: kern_ms[n])
+    ach = per_kernel[dom]["executed_tflops"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "flop_per_launch": UNITS[dom] * unit}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, w, args.cpu_heads)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": True,
+                   "gproj": True, "step": "fwd + bwd(row, col) + bob(row, col)",
+                   "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "per_kernel": per_kernel, "per_op": per_op,
+        "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(x, w, nheads):
+    """The fp64 oracle (fwd + bwd + BoB, untuned) on the first `nheads` heads."""
+    import numpy as np
+    import oracle
+    from synthetic import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    heads = [(hh // w.H, hh % w.H) for hh in range(nheads)]
+    a = {k: to_f64(v) for k, v in x.items()}
+    t0 = time.perf_counter()
+    oracle.bob(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"], heads=heads,
+               with_bwd=True)
+    dt = time.perf_counter() - t0
+    pairs = nheads * w.N * (w.N + 1) / 2
+    flop = sum(CONV.values()) * w.d * pairs
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{nheads} of {w.B * w.H} heads of {w.name}: fwd+bwd+BoB in fp64 NumPy, "
+                      f"same FLOP convention"}
+
+
+if __name__ == "__main__":
+    main()

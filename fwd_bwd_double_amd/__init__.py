@@ -1,0 +1,14 @@
+"""Exact causal multi-head softmax attention for MI355X (gfx950): forward,
+backward with optional GProj, and backward-over-backward, as hand-written HIP
+kernels behind the C ABI of libfbd.so (include/fbd.h).
+
+    from fwd_bwd_double_amd import attn_fwd, attn_bwd, attn_bob
+
+The functions take torch tensors shaped (B, H, N, 64) in bf16 or fp32 on the
+GPU; torch provides device memory and the stream, the kernels do the work.
+"""
+from ._lib import (AttnError, attn_bob, attn_bwd, attn_fwd,  # noqa: F401
+                   bob_workspace_bytes, bwd_workspace_bytes, load, LIB_PATH)
+
+__all__ = ["attn_fwd", "attn_bwd", "attn_bob", "bwd_workspace_bytes",
+           "bob_workspace_bytes", "AttnError", "load", "LIB_PATH"]

@@ -1,0 +1,192 @@
+"""ctypes binding of libfbd.so.
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity), their device pointers and torch's current HIP stream are handed to
+the C ABI, and the status is turned into an exception.  Every step of the
+computation runs in the library's HIP kernels; if the library is missing or
+fails to load, every call raises -- there is no other implementation here.
+
+torch is imported before the library is loaded so that the HIP runtime torch
+already holds (same soname) is the one the library binds to.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfbd.so")
+
+ATTN_BF16, ATTN_F32 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype or shape",
+          3: "pointer not 16-byte aligned", 4: "workspace missing or too small",
+          5: "HIP kernel launch failed"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        msg = f"{fn}: {STATUS.get(status, 'unknown status')} (status {status})"
+        if status == 5:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+        self.status = status
+        self.hip_error = hip_error
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once).  Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run `python -m fwd_bwd_double_amd.build`)")
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+    i64, f32, vp, i32, sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, i32, f32, vp, vp, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, i32, f32, i32,
+                             vp, vp, vp, vp, sz, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_bob_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_bob_workspace_bytes.restype = sz
+    lib.attn_bob.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                             f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_bob.restype = i32
+    lib.attn_bwd_passes.argtypes = [i32] + lib.attn_bwd.argtypes
+    lib.attn_bwd_passes.restype = i32
+    lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
+    lib.attn_bob_passes.restype = i32
+    lib.attn_status_str.argtypes = [i32]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = i32
+    _lib = lib
+    return lib
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; bf16 or fp32 only")
+
+
+def _check(name: str, t: torch.Tensor, like: torch.Tensor, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != like.device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU device of q ({like.device})")
+    if t.dtype != (like.dtype if dtype is None else dtype):
+        raise TypeError(f"{name} has dtype {t.dtype}")
+    if tuple(t.shape) != tuple(like.shape if shape is None else shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _raise(fn: str, st: int):
+    if st != 0:
+        raise AttnError(fn, st, load().attn_last_hip_error())
+
+
+def _scale(q: torch.Tensor, scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load().attn_bwd_workspace_bytes(B, H, N))
+
+
+def bob_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load().attn_bob_workspace_bytes(B, H, N))
+
+
+def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O, LSE = attention(q, k, v); q, k, v shaped (B, H, N, d), bf16 or fp32."""
+    lib = load()
+    for n, t in (("k", k), ("v", v)):
+        _check(n, t, q)
+    _check("q", q, q)
+    B, H, N, d = q.shape
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check("out", out, q)
+    _check("lse", lse, q, torch.float32, (B, H, N))
+    st = lib.attn_fwd(_dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                      1 if causal else 0, _scale(q, scale), out.data_ptr(), lse.data_ptr(),
+                      _stream(q.device))
+    _raise("attn_fwd", st)
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
+             gproj: bool = False, workspace: Optional[torch.Tensor] = None, outs=None,
+             passes: int = 3) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV of <dO, O>.  `workspace` (fp32, >= bwd_workspace_bytes) holds
+    D then r afterwards when given.  passes: 1 row pass, 2 column pass, 3 both."""
+    lib = load()
+    for n, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(n, t, q)
+    B, H, N, d = q.shape
+    _check("lse", lse, q, torch.float32, (B, H, N))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if outs is None else outs
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(n, t, q)
+    need = lib.attn_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_bwd_passes(passes, _dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), do.data_ptr(), 1 if causal else 0, _scale(q, scale),
+                      1 if gproj else 0, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      workspace.data_ptr(), ws_bytes, _stream(q.device))
+    _raise("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, outs=None,
+             passes: int = 3) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
+    cotangents (g_dq, g_dk, g_dv).  `workspace` holds D, alpha, beta after."""
+    lib = load()
+    for n, t in (("k", k), ("v", v), ("o", o), ("do", do), ("g_dq", g_dq), ("g_dk", g_dk),
+                 ("g_dv", g_dv)):
+        _check(n, t, q)
+    B, H, N, d = q.shape
+    _check("lse", lse, q, torch.float32, (B, H, N))
+    gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4)) if outs is None else outs
+    for n, t in (("g_q", gq), ("g_k", gk), ("g_v", gv), ("g_do", gdo)):
+        _check(n, t, q)
+    need = lib.attn_bob_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), do.data_ptr(), g_dq.data_ptr(), g_dk.data_ptr(),
+                      g_dv.data_ptr(), 1 if causal else 0, _scale(q, scale), gq.data_ptr(),
+                      gk.data_ptr(), gv.data_ptr(), gdo.data_ptr(), workspace.data_ptr(),
+                      ws_bytes, _stream(q.device))
+    _raise("attn_bob", st)
+    return gq, gk, gv, gdo

@@ -1,0 +1,184 @@
+// C ABI of libfbd.so (declared in include/fbd.h): argument validation, then
+// the kernel launches.  Every check runs before anything is enqueued, so a
+// call that returns an error has written nothing.  There is no fallback.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/fbd.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Span {
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+bool overlaps(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+size_t elem_size(attn_dtype dt) { return dt == ATTN_BF16 ? 2 : 4; }
+
+// Shape checks shared by all entry points.  The kernels index one head's
+// N x 64 matrix with 32-bit integers and launch ceil(N/128) * B * H
+// workgroups on a 1-D grid.
+attn_status check_shape(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, float scale) {
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return ATTN_EUNSUPPORTED;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return ATTN_EINVAL;
+  if (d != 64) return ATTN_EUNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  if (N > (int64_t)INT_MAX / 64) return ATTN_EUNSUPPORTED;
+  if (B > INT_MAX || H > INT_MAX) return ATTN_EUNSUPPORTED;
+  const int64_t bh = B * H;
+  if (bh > INT_MAX) return ATTN_EUNSUPPORTED;
+  if (bh > (int64_t)INT_MAX / N) return ATTN_EUNSUPPORTED;     // B*H*N fits int
+  const int64_t nblk = (N + 127) / 128;
+  if (bh > (int64_t)INT_MAX / nblk) return ATTN_EUNSUPPORTED;  // grid size
+  return ATTN_OK;
+}
+
+struct Arg {
+  const void* p;
+  size_t bytes;
+};
+
+// Null, alignment and overlap checks.  `ins` are read-only, `outs` written.
+attn_status check_ptrs(const std::vector<Arg>& ins, const std::vector<Arg>& outs) {
+  for (const Arg& a : ins) {
+    if (!a.p) return ATTN_EINVAL;
+    if (reinterpret_cast<uintptr_t>(a.p) % 16) return ATTN_EALIGN;
+  }
+  for (const Arg& a : outs) {
+    if (!a.p) return ATTN_EINVAL;
+    if (reinterpret_cast<uintptr_t>(a.p) % 16) return ATTN_EALIGN;
+  }
+  for (size_t i = 0; i < outs.size(); ++i) {
+    const Span so{reinterpret_cast<uintptr_t>(outs[i].p),
+                  reinterpret_cast<uintptr_t>(outs[i].p) + outs[i].bytes};
+    for (const Arg& a : ins) {
+      const Span si{reinterpret_cast<uintptr_t>(a.p), reinterpret_cast<uintptr_t>(a.p) + a.bytes};
+      if (overlaps(so, si)) return ATTN_EINVAL;
+    }
+    for (size_t k = i + 1; k < outs.size(); ++k) {
+      const Span sk{reinterpret_cast<uintptr_t>(outs[k].p),
+                    reinterpret_cast<uintptr_t>(outs[k].p) + outs[k].bytes};
+      if (overlaps(so, sk)) return ATTN_EINVAL;
+    }
+  }
+  return ATTN_OK;
+}
+
+attn_status finish(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_EHIP;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported dtype or shape";
+    case ATTN_EALIGN: return "pointer not 16-byte aligned";
+    case ATTN_EWORKSPACE: return "workspace missing or too small";
+    case ATTN_EHIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)3 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+attn_status attn_fwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
+                     const void* K, const void* V, int causal, float scale, void* O, float* LSE,
+                     void* stream) {
+  attn_status st = check_shape(dt, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
+  st = check_ptrs({{Q, t}, {K, t}, {V, t}}, {{O, t}, {LSE, s}});
+  if (st != ATTN_OK) return st;
+  return finish(fbd::launch_fwd((int)dt, Q, K, V, O, LSE, (int)(B * H), (int)N, causal ? 1 : 0,
+                                scale, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
+                            const void* Q, const void* K, const void* V, const void* O,
+                            const float* LSE, const void* dO, int causal, float scale, int gproj,
+                            void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (passes < 1 || passes > 3) return ATTN_EINVAL;
+  attn_status st = check_shape(dt, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_bwd_workspace_bytes(B, H, N);
+  if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
+  st = check_ptrs({{Q, t}, {K, t}, {V, t}, {O, t}, {LSE, s}, {dO, t}},
+                  {{dQ, t}, {dK, t}, {dV, t}, {ws, need}});
+  if (st != ATTN_OK) return st;
+  float* Dws = static_cast<float*>(ws);
+  float* Rws = Dws + (size_t)B * H * N;
+  return finish(fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, (int)(B * H),
+                                (int)N, causal ? 1 : 0, scale, gproj ? 1 : 0, passes,
+                                (hipStream_t)stream));
+}
+
+attn_status attn_bwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
+                     const void* K, const void* V, const void* O, const float* LSE,
+                     const void* dO, int causal, float scale, int gproj, void* dQ, void* dK,
+                     void* dV, void* ws, size_t ws_bytes, void* stream) {
+  return attn_bwd_passes(3, dt, B, H, N, d, Q, K, V, O, LSE, dO, causal, scale, gproj, dQ, dK,
+                         dV, ws, ws_bytes, stream);
+}
+
+attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
+                            const void* Q, const void* K, const void* V, const void* O,
+                            const float* LSE, const void* dO, const void* g_dQ, const void* g_dK,
+                            const void* g_dV, int causal, float scale, void* g_Q, void* g_K,
+                            void* g_V, void* g_dO, void* ws, size_t ws_bytes, void* stream) {
+  if (passes < 1 || passes > 3) return ATTN_EINVAL;
+  attn_status st = check_shape(dt, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_bob_workspace_bytes(B, H, N);
+  if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
+  st = check_ptrs({{Q, t}, {K, t}, {V, t}, {O, t}, {LSE, s}, {dO, t}, {g_dQ, t}, {g_dK, t},
+                   {g_dV, t}},
+                  {{g_Q, t}, {g_K, t}, {g_V, t}, {g_dO, t}, {ws, need}});
+  if (st != ATTN_OK) return st;
+  float* Dws = static_cast<float*>(ws);
+  float* Aws = Dws + (size_t)B * H * N;
+  float* Bws = Aws + (size_t)B * H * N;
+  return finish(fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, g_Q, g_K, g_V,
+                                g_dO, Dws, Aws, Bws, (int)(B * H), (int)N, causal ? 1 : 0, scale,
+                                passes, (hipStream_t)stream));
+}
+
+attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
+                     const void* K, const void* V, const void* O, const float* LSE,
+                     const void* dO, const void* g_dQ, const void* g_dK, const void* g_dV,
+                     int causal, float scale, void* g_Q, void* g_K, void* g_V, void* g_dO,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return attn_bob_passes(3, dt, B, H, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, scale,
+                         g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,384 @@
+// Backward-over-backward: the vector-Jacobian product of the first backward
+// map (Q, K, V, dO) -> (dQ, dK, dV) with cotangents (A, Bk, C) =
+// (g_dQ, g_dK, g_dV), computed in two passes as on the FlashBoB page
+// (rit.work, flashbob-second-order-attention, section "Two scalar states
+// replace quadratic tensors").
+//
+// With P, dP = dO V^T, D = rowsum(dO o O) and dS = P o (dP - D) as in the
+// first backward, and
+//   W = scale (A K^T + Q Bk^T),  U = dO C^T,
+//   alpha_i = sum_j P_ij W_ij,
+//   G = W o (dP - D) - alpha o dP + U,   beta_i = sum_j P_ij G_ij,
+//   Sh = P o (G - beta),  H = P o (W - alpha),
+// the result is
+//   gQ = scale (Sh K + dS Bk),   gK = scale (Sh^T Q + dS^T A),
+//   gV = H^T dO,                 gdO = H V + P C.
+// (The pages state the operation, not these formulas; they follow from the
+// definition by differentiating <A, dQ> + <Bk, dK> + <C, dV>.)
+//
+// Row pass (lane = query i).  alpha_i and beta_i need the whole row, but
+// everything else is linear in them, so the pass accumulates
+//   X = sum_j R(P (W (dP - D) + U)) K_j,  Y = sum_j R(P) K_j,
+//   Z = sum_j R(P dP) K_j,  E = sum_j R(dS) Bk_j,  F = sum_j R(P W) V_j,
+//   Gc = sum_j R(P) C_j,
+// plus the row sums alpha_i and b_i = sum_j P (W dP + U), and after the last
+// key block applies the corrections once:
+//   beta_i = b_i - 2 alpha_i D_i,
+//   gQ = scale (X - alpha Z - beta Y + E),   gdO = F - alpha O + Gc
+// (sum_j P_ij V_j = O_i).  It writes gQ, gdO and the row states D, alpha, beta.
+//
+// Column pass (lane = key j).  K, V, Bk, C of the workgroup's keys stay in
+// registers; query blocks stream past them with their row states, and
+// gK, gV are accumulated and written once.
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace fbd {
+
+template <class T, int BN>
+__global__ __launch_bounds__(NT) void bob_row_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
+    const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
+    T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
+    float* __restrict__ Bws, int N, int BH, int nblk, int causal, float scale) {
+  constexpr int RS = Lay<T>::RS;
+  using Stage = TileStage<T, BN>;
+  constexpr int TS = Stage::TS;
+  __shared__ __attribute__((aligned(16))) T Ks[BN * RS];
+  __shared__ __attribute__((aligned(16))) T Vs[BN * RS];
+  __shared__ __attribute__((aligned(16))) T Bs[BN * RS];
+  __shared__ __attribute__((aligned(16))) T Cs[BN * RS];
+  __shared__ __attribute__((aligned(16))) T Kt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T Vt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T Bt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T Ct[HD * TS];
+
+  const Work wk = row_work(BH, nblk);
+  const size_t hoff = (size_t)wk.head * N * HD;
+  const size_t soff = (size_t)wk.head * N;
+  const T* Kh = K + hoff;
+  const T* Vh = V + hoff;
+  const T* Bh = Bk + hoff;
+  const T* Ch = C + hoff;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q0 = wk.blk * BLK;
+  const int qw = q0 + wave * WROWS;
+  const int my_i = qw + (lane & 31);
+  const int h = lane >> 5;
+  const float sl2 = scale * LOG2E;
+
+  Frag<T> qf[4], dof[4], af[4];
+  ld_frags(Q + hoff, N, qw, lane, qf);
+  ld_frags(dO + hoff, N, qw, lane, dof);
+  ld_frags(A + hoff, N, qw, lane, af);
+  float Di;
+  {
+    Frag<T> of[4];
+    ld_frags(O + hoff, N, qw, lane, of);
+    Di = row_dot(dof, of);
+  }
+  const float lse2 = my_i < N ? LSE[soff + my_i] * LOG2E : 0.f;
+
+  f32x16 X0 = zero16(), X1 = zero16(), Y0 = zero16(), Y1 = zero16();
+  f32x16 Z0 = zero16(), Z1 = zero16(), E0 = zero16(), E1 = zero16();
+  f32x16 F0 = zero16(), F1 = zero16(), G0 = zero16(), G1 = zero16();
+  float alpha = 0.f, bsum = 0.f;
+
+  const int jend = causal ? min(N, q0 + BLK) : N;
+  const int ntiles = (jend + BN - 1) / BN;
+  Stage sk, sv, sb, sc;
+  sk.load(Kh, N, 0, tid);
+  sv.load(Vh, N, 0, tid);
+  sb.load(Bh, N, 0, tid);
+  sc.load(Ch, N, 0, tid);
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BN;
+    __syncthreads();
+    sk.store_rows(Ks, tid);
+    sk.store_tr(Kt, tid);
+    sv.store_rows(Vs, tid);
+    sv.store_tr(Vt, tid);
+    sb.store_rows(Bs, tid);
+    sb.store_tr(Bt, tid);
+    sc.store_rows(Cs, tid);
+    sc.store_tr(Ct, tid);
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      sk.load(Kh, N, j0 + BN, tid);
+      sv.load(Vh, N, j0 + BN, tid);
+      sb.load(Bh, N, j0 + BN, tid);
+      sc.load(Ch, N, j0 + BN, tid);
+    }
+#pragma unroll
+    for (int jb = 0; jb < BN; jb += 32) {
+      const int js = j0 + jb;
+      if (qw >= N || (causal ? (js > qw + 31) : (js >= N))) break;
+      f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const Frag<T> kr = ld_row(Ks, jb, kb, lane);
+        mma(s, kr, qf[kb]);
+        mma(w, kr, af[kb]);
+        mma(w, ld_row(Bs, jb, kb, lane), qf[kb]);
+        const Frag<T> vr = ld_row(Vs, jb, kb, lane);
+        mma(dp, vr, dof[kb]);
+        mma(u, ld_row(Cs, jb, kb, lane), dof[kb]);
+      }
+      const bool edge = causal ? (js + 31 > qw) : (js + 32 > N);
+      float xs[16], ps[16], zs[16], es[16], fs[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
+        if (edge) {
+          const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (causal ? (j > my_i) : (j >= N)) pv = 0.f;
+        }
+        const float W = scale * w[v];
+        const float dpd = dp[v] - Di;
+        const float pw = pv * W;
+        alpha += pw;
+        bsum += pv * (W * dp[v] + u[v]);
+        ps[v] = pv;
+        xs[v] = pv * (W * dpd + u[v]);
+        zs[v] = pv * dp[v];
+        es[v] = pv * dpd;
+        fs[v] = pw;
+      }
+      const int jt = jb / 16;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const Frag<T> xf = pack8<T>(xs + 8 * tt), pf = pack8<T>(ps + 8 * tt);
+        const Frag<T> zf = pack8<T>(zs + 8 * tt), ef = pack8<T>(es + 8 * tt);
+        const Frag<T> ff = pack8<T>(fs + 8 * tt);
+        {
+          const Frag<T> a0 = ld_tr(Kt, TS, 0, jt + tt, lane), a1 = ld_tr(Kt, TS, 32, jt + tt, lane);
+          mma(X0, a0, xf);
+          mma(X1, a1, xf);
+          mma(Y0, a0, pf);
+          mma(Y1, a1, pf);
+          mma(Z0, a0, zf);
+          mma(Z1, a1, zf);
+        }
+        {
+          const Frag<T> a0 = ld_tr(Bt, TS, 0, jt + tt, lane), a1 = ld_tr(Bt, TS, 32, jt + tt, lane);
+          mma(E0, a0, ef);
+          mma(E1, a1, ef);
+        }
+        {
+          const Frag<T> a0 = ld_tr(Vt, TS, 0, jt + tt, lane), a1 = ld_tr(Vt, TS, 32, jt + tt, lane);
+          mma(F0, a0, ff);
+          mma(F1, a1, ff);
+        }
+        {
+          const Frag<T> a0 = ld_tr(Ct, TS, 0, jt + tt, lane), a1 = ld_tr(Ct, TS, 32, jt + tt, lane);
+          mma(G0, a0, pf);
+          mma(G1, a1, pf);
+        }
+      }
+    }
+  }
+  alpha += other_half(alpha);
+  bsum += other_half(bsum);
+  const float beta = bsum - 2.f * alpha * Di;
+  float out[16], ov[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - beta * Y0[v] + E0[v]);
+  st_cols(gQ + hoff, N, qw, 0, lane, out);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = scale * (X1[v] - alpha * Z1[v] - beta * Y1[v] + E1[v]);
+  st_cols(gQ + hoff, N, qw, 32, lane, out);
+  ld_cols(O + hoff, N, qw, 0, lane, ov);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = F0[v] - alpha * ov[v] + G0[v];
+  st_cols(gdO + hoff, N, qw, 0, lane, out);
+  ld_cols(O + hoff, N, qw, 32, lane, ov);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = F1[v] - alpha * ov[v] + G1[v];
+  st_cols(gdO + hoff, N, qw, 32, lane, out);
+  if (h == 0 && my_i < N) {
+    Dws[soff + my_i] = Di;
+    Aws[soff + my_i] = alpha;
+    Bws[soff + my_i] = beta;
+  }
+}
+
+template <class T, int BM>
+__global__ __launch_bounds__(NT) void bob_col_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ LSE, const T* __restrict__ dO, const T* __restrict__ A,
+    const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
+    const float* __restrict__ Aws, const float* __restrict__ Bws, T* __restrict__ gK,
+    T* __restrict__ gV, int N, int BH, int causal, float scale) {
+  constexpr int RS = Lay<T>::RS;
+  using Stage = TileStage<T, BM>;
+  constexpr int TS = Stage::TS;
+  __shared__ __attribute__((aligned(16))) T Qs[BM * RS];
+  __shared__ __attribute__((aligned(16))) T Qt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T dOs[BM * RS];
+  __shared__ __attribute__((aligned(16))) T dOt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T As[BM * RS];
+  __shared__ __attribute__((aligned(16))) T At[HD * TS];
+  __shared__ __attribute__((aligned(16))) float sL[BM];
+  __shared__ __attribute__((aligned(16))) float sD[BM];
+  __shared__ __attribute__((aligned(16))) float sA[BM];
+  __shared__ __attribute__((aligned(16))) float sB[BM];
+
+  const Work wk = col_work(BH);
+  const size_t hoff = (size_t)wk.head * N * HD;
+  const size_t soff = (size_t)wk.head * N;
+  const T* Qh = Q + hoff;
+  const T* dOh = dO + hoff;
+  const T* Ah = A + hoff;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k0 = wk.blk * BLK;
+  const int kw = k0 + wave * WROWS;
+  const int my_j = kw + (lane & 31);
+  const int h = lane >> 5;
+  const float sl2 = scale * LOG2E;
+
+  Frag<T> kf[4], vf[4], bf[4], cf[4];
+  ld_frags(K + hoff, N, kw, lane, kf);
+  ld_frags(V + hoff, N, kw, lane, vf);
+  ld_frags(Bk + hoff, N, kw, lane, bf);
+  ld_frags(C + hoff, N, kw, lane, cf);
+  f32x16 gk0 = zero16(), gk1 = zero16(), gv0 = zero16(), gv1 = zero16();
+
+  const int istart = causal ? k0 : 0;
+  const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
+  Stage sq, sdo, sa;
+  float lrow = INFINITY, drow = 0.f, arow = 0.f, brow = 0.f;
+  auto prefetch = [&](int i0) {
+    sq.load(Qh, N, i0, tid);
+    sdo.load(dOh, N, i0, tid);
+    sa.load(Ah, N, i0, tid);
+    if (tid < BM) {
+      const int row = i0 + tid;
+      const bool ok = row < N;
+      lrow = ok ? LSE[soff + row] * LOG2E : INFINITY;   // padded rows: P = 0
+      drow = ok ? Dws[soff + row] : 0.f;
+      arow = ok ? Aws[soff + row] : 0.f;
+      brow = ok ? Bws[soff + row] : 0.f;
+    }
+  };
+  if (ntiles > 0) prefetch(istart);
+  for (int t = 0; t < ntiles; ++t) {
+    const int i0 = istart + t * BM;
+    __syncthreads();
+    sq.store_rows(Qs, tid);
+    sq.store_tr(Qt, tid);
+    sdo.store_rows(dOs, tid);
+    sdo.store_tr(dOt, tid);
+    sa.store_rows(As, tid);
+    sa.store_tr(At, tid);
+    if (tid < BM) {
+      sL[tid] = lrow;
+      sD[tid] = drow;
+      sA[tid] = arow;
+      sB[tid] = brow;
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) prefetch(i0 + BM);
+#pragma unroll
+    for (int ib = 0; ib < BM; ib += 32) {
+      const int is = i0 + ib;
+      if (kw >= N || is >= N) break;
+      if (causal && is + 31 < kw) continue;
+      f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const Frag<T> qr = ld_row(Qs, ib, kb, lane);
+        mma(s, qr, kf[kb]);
+        mma(w, qr, bf[kb]);
+        mma(w, ld_row(As, ib, kb, lane), kf[kb]);
+        const Frag<T> dr = ld_row(dOs, ib, kb, lane);
+        mma(dp, dr, vf[kb]);
+        mma(u, dr, cf[kb]);
+      }
+      const bool diag = causal && (is == kw);
+      float shs[16], dss[16], hs[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rbase = ib + 8 * q + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[rbase]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[rbase]);
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[rbase]);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sB[rbase]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * q + r;
+          float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - l4[r]);
+          if (diag && my_j > i0 + rbase + r) pv = 0.f;
+          const float W = scale * w[v];
+          const float dpd = dp[v] - d4[r];
+          dss[v] = pv * dpd;
+          hs[v] = pv * (W - a4[r]);
+          shs[v] = pv * (W * dpd + u[v] - a4[r] * dp[v] - b4[r]);
+        }
+      }
+      const int it = ib / 16;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const Frag<T> shf = pack8<T>(shs + 8 * tt), dsf = pack8<T>(dss + 8 * tt);
+        const Frag<T> hf = pack8<T>(hs + 8 * tt);
+        mma(gk0, ld_tr(Qt, TS, 0, it + tt, lane), shf);
+        mma(gk1, ld_tr(Qt, TS, 32, it + tt, lane), shf);
+        mma(gk0, ld_tr(At, TS, 0, it + tt, lane), dsf);
+        mma(gk1, ld_tr(At, TS, 32, it + tt, lane), dsf);
+        mma(gv0, ld_tr(dOt, TS, 0, it + tt, lane), hf);
+        mma(gv1, ld_tr(dOt, TS, 32, it + tt, lane), hf);
+      }
+    }
+  }
+  float out[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = scale * gk0[v];
+  st_cols(gK + hoff, N, kw, 0, lane, out);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = scale * gk1[v];
+  st_cols(gK + hoff, N, kw, 32, lane, out);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = gv0[v];
+  st_cols(gV + hoff, N, kw, 0, lane, out);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = gv1[v];
+  st_cols(gV + hoff, N, kw, 32, lane, out);
+}
+
+template <class T>
+static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, const void* O,
+                               const float* LSE, const void* dO, const void* gdQ, const void* gdK,
+                               const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
+                               float* Dws, float* Aws, float* Bws, int BH, int N, int causal,
+                               float scale, int passes, hipStream_t st) {
+  constexpr int BN = 32, BM = 64;
+  const int nblk = (N + BLK - 1) / BLK;
+  if (passes & 1) {
+    hipLaunchKernelGGL((bob_row_kernel<T, BN>), dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q,
+                       (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO, (const T*)gdQ,
+                       (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws, N, BH,
+                       nblk, causal, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(passes & 2)) return hipSuccess;
+  hipLaunchKernelGGL((bob_col_kernel<T, BM>), dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q,
+                     (const T*)K, (const T*)V, LSE, (const T*)dO, (const T*)gdQ, (const T*)gdK,
+                     (const T*)gdV, (const float*)Dws, (const float*)Aws, (const float*)Bws,
+                     (T*)gK, (T*)gV, N, BH, causal, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
+                      const float* LSE, const void* dO, const void* gdQ, const void* gdK,
+                      const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
+                      float* Aws, float* Bws, int BH, int N, int causal, float scale, int passes,
+                      hipStream_t st) {
+  if (dt == 0)
+    return launch_bob_t<bf16>(Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws,
+                              BH, N, causal, scale, passes, st);
+  return launch_bob_t<float>(Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws,
+                             BH, N, causal, scale, passes, st);
+}
+
+}  // namespace fbd

@@ -1,0 +1,318 @@
+// Backward pass with optional GProj.
+//
+// Recompute instead of store (FlashAttention explainer page, marketmaker.cc
+// flash-attention-trading-models, section "Backward pass: recompute instead of
+// store"): only O and the row LSE are kept from the forward; every tile of P
+// is recomputed as exp(scale * S - LSE) from Q and K.
+//
+//   row pass    (lane = query i): D_i = sum_d dO_id O_id,
+//               dS = P o (dO V^T - D),  dQ = scale * R(dS) K
+//   column pass (lane = key j):  dV = R(P)^T dO,  dK = scale * R(dS)^T Q
+//
+// R() is the rounding of an operand to bf16 for the matrix cores (identity for
+// fp32 inputs).  With GProj (GProj page, rit.work
+// flashattention-bf16-gradient-gproj, section "How a zero sum turns into a
+// false gradient") the row pass also accumulates r_i = sum_j R(dS_ij) over
+// exactly those bf16 values and R(P) K, and finishes
+//   dQ = scale * (R(dS) K - r_i R(P) K);
+// the column pass reads r and adds the key correction
+//   dK = scale * (R(dS)^T Q - R(P)^T R(r o Q))
+// as a separate fp32-accumulated product; the projected dS is never re-rounded.
+// Each output block is written once by one workgroup; there are no atomics.
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace fbd {
+
+template <class T, int BN, bool GPROJ>
+__global__ __launch_bounds__(NT) void bwd_row_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
+    T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, int N, int BH, int nblk,
+    int causal, float scale) {
+  constexpr int RS = Lay<T>::RS;
+  using Stage = TileStage<T, BN>;
+  constexpr int TS = Stage::TS;
+  __shared__ __attribute__((aligned(16))) T Ks[BN * RS];
+  __shared__ __attribute__((aligned(16))) T Vs[BN * RS];
+  __shared__ __attribute__((aligned(16))) T Kt[HD * TS];
+
+  const Work wk = row_work(BH, nblk);
+  const size_t hoff = (size_t)wk.head * N * HD;
+  const size_t soff = (size_t)wk.head * N;
+  const T* Kh = K + hoff;
+  const T* Vh = V + hoff;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q0 = wk.blk * BLK;
+  const int qw = q0 + wave * WROWS;
+  const int my_i = qw + (lane & 31);
+  const int h = lane >> 5;
+  const float sl2 = scale * LOG2E;
+
+  Frag<T> qf[4], dof[4];
+  ld_frags(Q + hoff, N, qw, lane, qf);
+  ld_frags(dO + hoff, N, qw, lane, dof);
+  float Di;
+  {
+    Frag<T> of[4];
+    ld_frags(O + hoff, N, qw, lane, of);
+    Di = row_dot(dof, of);
+  }
+  const float lse2 = my_i < N ? LSE[soff + my_i] * LOG2E : 0.f;
+
+  f32x16 dq0 = zero16(), dq1 = zero16();
+  f32x16 pk0 = zero16(), pk1 = zero16();
+  float r = 0.f;
+
+  const int jend = causal ? min(N, q0 + BLK) : N;
+  const int ntiles = (jend + BN - 1) / BN;
+  Stage sk, sv;
+  sk.load(Kh, N, 0, tid);
+  sv.load(Vh, N, 0, tid);
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BN;
+    __syncthreads();
+    sk.store_rows(Ks, tid);
+    sk.store_tr(Kt, tid);
+    sv.store_rows(Vs, tid);
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      sk.load(Kh, N, j0 + BN, tid);
+      sv.load(Vh, N, j0 + BN, tid);
+    }
+#pragma unroll
+    for (int jb = 0; jb < BN; jb += 32) {
+      const int js = j0 + jb;
+      if (qw >= N || (causal ? (js > qw + 31) : (js >= N))) break;
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        mma(s, ld_row(Ks, jb, kb, lane), qf[kb]);
+        mma(dp, ld_row(Vs, jb, kb, lane), dof[kb]);
+      }
+      const bool edge = causal ? (js + 31 > qw) : (js + 32 > N);
+      float p[16], ds[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
+        if (edge) {
+          const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (causal ? (j > my_i) : (j >= N)) pv = 0.f;
+        }
+        p[v] = pv;
+        ds[v] = pv * (dp[v] - Di);
+      }
+      const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
+      const int jt = jb / 16;
+      const Frag<T> a00 = ld_tr(Kt, TS, 0, jt, lane), a01 = ld_tr(Kt, TS, 0, jt + 1, lane);
+      const Frag<T> a10 = ld_tr(Kt, TS, 32, jt, lane), a11 = ld_tr(Kt, TS, 32, jt + 1, lane);
+      mma(dq0, a00, df0);
+      mma(dq0, a01, df1);
+      mma(dq1, a10, df0);
+      mma(dq1, a11, df1);
+      if constexpr (GPROJ) {
+        r += frag_sum(df0) + frag_sum(df1);
+        const Frag<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
+        mma(pk0, a00, pf0);
+        mma(pk0, a01, pf1);
+        mma(pk1, a10, pf0);
+        mma(pk1, a11, pf1);
+      }
+    }
+  }
+  float out[16];
+  if constexpr (GPROJ) {
+    r += other_half(r);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = scale * (dq0[v] - r * pk0[v]);
+    st_cols(dQ + hoff, N, qw, 0, lane, out);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = scale * (dq1[v] - r * pk1[v]);
+    st_cols(dQ + hoff, N, qw, 32, lane, out);
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = scale * dq0[v];
+    st_cols(dQ + hoff, N, qw, 0, lane, out);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = scale * dq1[v];
+    st_cols(dQ + hoff, N, qw, 32, lane, out);
+  }
+  if (h == 0 && my_i < N) {
+    Dws[soff + my_i] = Di;
+    if constexpr (GPROJ) Rws[soff + my_i] = r;
+  }
+}
+
+template <class T, int BM, bool GPROJ>
+__global__ __launch_bounds__(NT) void bwd_col_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ LSE, const T* __restrict__ dO, const float* __restrict__ Dws,
+    const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
+    int causal, float scale) {
+  constexpr int RS = Lay<T>::RS;
+  using Stage = TileStage<T, BM>;
+  constexpr int TS = Stage::TS;
+  __shared__ __attribute__((aligned(16))) T Qs[BM * RS];
+  __shared__ __attribute__((aligned(16))) T Qt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T dOs[BM * RS];
+  __shared__ __attribute__((aligned(16))) T dOt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T rQt[GPROJ ? HD * TS : 8];
+  __shared__ __attribute__((aligned(16))) float sL[BM];
+  __shared__ __attribute__((aligned(16))) float sD[BM];
+
+  const Work wk = col_work(BH);
+  const size_t hoff = (size_t)wk.head * N * HD;
+  const size_t soff = (size_t)wk.head * N;
+  const T* Qh = Q + hoff;
+  const T* dOh = dO + hoff;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k0 = wk.blk * BLK;
+  const int kw = k0 + wave * WROWS;
+  const int my_j = kw + (lane & 31);
+  const int h = lane >> 5;
+  const float sl2 = scale * LOG2E;
+
+  Frag<T> kf[4], vf[4];
+  ld_frags(K + hoff, N, kw, lane, kf);
+  ld_frags(V + hoff, N, kw, lane, vf);
+  f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
+
+  const int istart = causal ? k0 : 0;   // k0 is a multiple of BM
+  const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
+  Stage sq, sdo;
+  float lrow = INFINITY, drow = 0.f;
+  auto prefetch = [&](int i0) {
+    sq.load(Qh, N, i0, tid);
+    sdo.load(dOh, N, i0, tid);
+    if (tid < BM) {
+      const int row = i0 + tid;
+      lrow = row < N ? LSE[soff + row] * LOG2E : INFINITY;   // padded rows: P = 0
+      drow = row < N ? Dws[soff + row] : 0.f;
+    }
+  };
+  if (ntiles > 0) prefetch(istart);
+  for (int t = 0; t < ntiles; ++t) {
+    const int i0 = istart + t * BM;
+    __syncthreads();
+    sq.store_rows(Qs, tid);
+    sq.store_tr(Qt, tid);
+    sdo.store_rows(dOs, tid);
+    sdo.store_tr(dOt, tid);
+    if (tid < BM) {
+      sL[tid] = lrow;
+      sD[tid] = drow;
+    }
+    if constexpr (GPROJ) {
+      // rQt = R(-r_i * Q_i), transposed
+#pragma unroll
+      for (int u = 0; u < Stage::U; ++u) {
+        const int unit = tid + NT * u;
+        const int p = unit % (BM / 2);
+        const int row = i0 + 2 * p;
+        float fac[2] = {row < N ? -Rws[soff + row] : 0.f, row + 1 < N ? -Rws[soff + row + 1] : 0.f};
+        sq.scale_rows(fac, u);
+      }
+      sq.store_tr(rQt, tid);
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) prefetch(i0 + BM);
+#pragma unroll
+    for (int ib = 0; ib < BM; ib += 32) {
+      const int is = i0 + ib;
+      if (kw >= N || is >= N) break;
+      if (causal && is + 31 < kw) continue;
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        mma(s, ld_row(Qs, ib, kb, lane), kf[kb]);
+        mma(dp, ld_row(dOs, ib, kb, lane), vf[kb]);
+      }
+      const bool diag = causal && (is == kw);
+      float p[16], ds[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[ib + 8 * q + 4 * h]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[ib + 8 * q + 4 * h]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * q + r;
+          float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - l4[r]);
+          if (diag && my_j > is + 8 * q + 4 * h + r) pv = 0.f;
+          p[v] = pv;
+          ds[v] = pv * (dp[v] - d4[r]);
+        }
+      }
+      const Frag<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
+      const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
+      const int it = ib / 16;
+      mma(dv0, ld_tr(dOt, TS, 0, it, lane), pf0);
+      mma(dv0, ld_tr(dOt, TS, 0, it + 1, lane), pf1);
+      mma(dv1, ld_tr(dOt, TS, 32, it, lane), pf0);
+      mma(dv1, ld_tr(dOt, TS, 32, it + 1, lane), pf1);
+      mma(dk0, ld_tr(Qt, TS, 0, it, lane), df0);
+      mma(dk0, ld_tr(Qt, TS, 0, it + 1, lane), df1);
+      mma(dk1, ld_tr(Qt, TS, 32, it, lane), df0);
+      mma(dk1, ld_tr(Qt, TS, 32, it + 1, lane), df1);
+      if constexpr (GPROJ) {
+        mma(dk0, ld_tr(rQt, TS, 0, it, lane), pf0);
+        mma(dk0, ld_tr(rQt, TS, 0, it + 1, lane), pf1);
+        mma(dk1, ld_tr(rQt, TS, 32, it, lane), pf0);
+        mma(dk1, ld_tr(rQt, TS, 32, it + 1, lane), pf1);
+      }
+    }
+  }
+  float out[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = scale * dk0[v];
+  st_cols(dK + hoff, N, kw, 0, lane, out);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = scale * dk1[v];
+  st_cols(dK + hoff, N, kw, 32, lane, out);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = dv0[v];
+  st_cols(dV + hoff, N, kw, 0, lane, out);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[v] = dv1[v];
+  st_cols(dV + hoff, N, kw, 32, lane, out);
+}
+
+template <class T, bool GPROJ>
+static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void* O,
+                               const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+                               float* Dws, float* Rws, int BH, int N, int causal, float scale,
+                               int passes, hipStream_t st) {
+  constexpr int BN = 64, BM = 64;
+  const int nblk = (N + BLK - 1) / BLK;
+  if (passes & 1) {
+    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ>), dim3(nblk * BH), dim3(NT), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
+                       (T*)dQ, Dws, Rws, N, BH, nblk, causal, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(passes & 2)) return hipSuccess;
+  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ>), dim3(nblk * BH), dim3(NT), 0, st,
+                     (const T*)Q, (const T*)K, (const T*)V, LSE, (const T*)dO, (const float*)Dws,
+                     (const float*)Rws, (T*)dK, (T*)dV, N, BH, causal, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
+                      const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
+                      float* Rws, int BH, int N, int causal, float scale, int gproj, int passes,
+                      hipStream_t st) {
+  if (dt == 0) {
+    if (gproj)
+      return launch_bwd_t<bf16, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+                                      scale, passes, st);
+    return launch_bwd_t<bf16, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+                                     scale, passes, st);
+  }
+  if (gproj)
+    return launch_bwd_t<float, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+                                     scale, passes, st);
+  return launch_bwd_t<float, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+                                    scale, passes, st);
+}
+
+}  // namespace fbd

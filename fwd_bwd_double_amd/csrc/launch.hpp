@@ -1,0 +1,25 @@
+// Internal launch entry points of the attention kernels (host side).  The
+// public C ABI in include/fbd.h validates every argument and then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fbd {
+
+// dt: 0 = bf16, 1 = fp32.  BH = batch * heads.  Pointers are device pointers.
+// passes (backward and BoB): bit 0 = row pass, bit 1 = column pass.
+hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      int BH, int N, int causal, float scale, hipStream_t st);
+
+hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
+                      const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
+                      float* Rws, int BH, int N, int causal, float scale, int gproj, int passes,
+                      hipStream_t st);
+
+hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
+                      const float* LSE, const void* dO, const void* gdQ, const void* gdK,
+                      const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
+                      float* Aws, float* Bws, int BH, int N, int causal, float scale, int passes,
+                      hipStream_t st);
+
+}  // namespace fbd

@@ -1,0 +1,178 @@
+/*
+ * fbd.h -- exact causal multi-head softmax attention on MI355X (gfx950):
+ * forward, backward (optionally with GProj) and backward-over-backward.
+ *
+ * C ABI of libfbd.so.  No torch or C++ types cross this boundary: plain
+ * integers, floats and pointers.
+ *
+ * Layout.  Q, K, V, O, dO and every gradient and cotangent are (B, H, N, d)
+ * contiguous row-major arrays (d fastest) of the element type `dt` -- the
+ * (batch, heads, seq, head_dim) operand order of the attention call on the
+ * FlashAttention explainer page (marketmaker.cc, flash-attention-trading-models,
+ * section "Integration is eight lines").  LSE and the workspaces are fp32
+ * arrays.  Only d = 64 is supported; any N >= 1 is.
+ *
+ * Pointers.  Every array pointer is a DEVICE pointer owned by the caller,
+ * 16-byte aligned.  The library never allocates, frees, synchronises, or reads
+ * device memory from the host.  Inputs are never written.  Outputs are fully
+ * overwritten (never accumulated into) and must not overlap any input, any
+ * other output or the workspace.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Each call only enqueues kernels on that stream and returns; it is
+ * asynchronous with respect to the host.  Calls on one stream run in order, so
+ * attn_bwd / attn_bob may be enqueued right after the attn_fwd whose O and LSE
+ * they read.
+ *
+ * Errors.  Every argument check runs before anything is enqueued, so on any
+ * status other than ATTN_OK from validation nothing has been written.  There is
+ * no fallback path: an unsupported request returns an error instead of being
+ * computed some other way (the explainer page, section "Integration is eight
+ * lines", warns that a silent fallback only looks like a slow working model).
+ * ATTN_EHIP reports a failed kernel launch; attn_last_hip_error() then
+ * returns the hipError_t value (per calling thread).
+ *
+ * Causal mask.  causal = 1 keeps key j for query i iff j <= i (equal query
+ * and key lengths, top-left aligned), and key blocks entirely in the future
+ * of a query block are skipped, never loaded (explainer page, section
+ * "Causal masking is where trading gets a discount").  causal = 0 is full
+ * attention.
+ */
+#ifndef FBD_H
+#define FBD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,       /* null pointer, size <= 0, non-finite or <= 0 scale, overlap */
+  ATTN_EUNSUPPORTED = 2, /* d != 64, unknown dtype, sizes beyond the index limits */
+  ATTN_EALIGN = 3,       /* a pointer that is not 16-byte aligned */
+  ATTN_EWORKSPACE = 4,   /* workspace pointer null or smaller than required */
+  ATTN_EHIP = 5          /* a kernel launch failed; see attn_last_hip_error() */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+
+/*
+ * Forward pass.  Explainer page, sections "The Flash Attention algorithm" and
+ * "The online softmax recurrence": queries are processed in row blocks, key
+ * and value blocks are streamed through LDS, and a running row max m and row
+ * sum l rescale the output accumulator; no N x N matrix is written.  The max
+ * is subtracted before the scale is applied, so the largest weight of a row is
+ * exactly 1 (GProj page, rit.work flashattention-bf16-gradient-gproj, section
+ * "Why the error shows up at the end of training").
+ *
+ *   O   = softmax(scale * Q K^T + mask) V                 (B, H, N, d), dtype dt
+ *   LSE = scale * m + ln l   (natural log, per row)       (B, H, N) fp32
+ *
+ * scale must be finite and > 0 (1/sqrt(d) is the usual value).
+ */
+attn_status attn_fwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
+                     const void* Q, const void* K, const void* V,
+                     int causal, float scale,
+                     void* O, float* LSE, void* stream);
+
+/* Workspace of attn_bwd in bytes: D then r, each B*H*N fp32 (D at offset 0,
+ * r at offset B*H*N floats).  r is written only when gproj != 0. */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
+
+/*
+ * Backward pass.  Explainer page, section "Backward pass: recompute instead of
+ * store": P is recomputed tile by tile from Q, K and the saved LSE,
+ *   P = exp(scale * S - LSE),  dP = dO V^T,  D = rowsum(dO o O),
+ *   dS = P o (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO.
+ * A row-block pass computes D and dQ; a column-block pass computes dK and dV.
+ *
+ * gproj != 0 applies GProj (GProj page, section "How a zero sum turns into a
+ * false gradient"): dS is fed to the matrix cores in bf16, so its rows no
+ * longer sum to zero; the residual r_i = sum_j R(dS_ij) of exactly those
+ * bf16 values is removed in proportion to the probabilities:
+ *   dQ = scale * (R(dS) K - r o (R(P) K)),
+ *   dK = scale * (R(dS)^T Q - R(P)^T R(r o Q)).
+ * The dQ correction rides in the row pass; the dK correction needs r and is
+ * applied in the column pass.  For fp32 inputs R is the identity.
+ *
+ * O and LSE must be the outputs of attn_fwd with the same causal and scale.
+ * ws must hold attn_bwd_workspace_bytes(B, H, N) bytes (fp32, device).
+ */
+attn_status attn_bwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
+                     const void* Q, const void* K, const void* V, const void* O,
+                     const float* LSE, const void* dO,
+                     int causal, float scale, int gproj,
+                     void* dQ, void* dK, void* dV,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace of attn_bob in bytes: D, alpha, beta, each B*H*N fp32, in that
+ * order. */
+size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N);
+
+/*
+ * Backward-over-backward: the vector-Jacobian product of the first backward
+ * map (Q, K, V, dO) -> (dQ, dK, dV) with cotangents (g_dQ, g_dK, g_dV), i.e.
+ * the gradient of <g_dQ, dQ> + <g_dK, dK> + <g_dV, dV> with respect to
+ * (Q, K, V, dO).  FlashBoB page (rit.work, flashbob-second-order-attention),
+ * sections "Why go backward through an already computed gradient" and "Two
+ * scalar states replace quadratic tensors": a row-block pass streams key
+ * blocks, reduces each row's global dependence to two fp32 states
+ *   alpha_i = sum_j P_ij W_ij,
+ *   beta_i  = sum_j P_ij (W_ij (dP_ij - D_i) - alpha_i dP_ij + U_ij),
+ * with W = scale (g_dQ K^T + Q g_dK^T) and U = dO g_dV^T, and finishes g_Q and
+ * g_dO; a column-block pass streams query blocks past resident key blocks,
+ * reads the row states and finishes g_K and g_V.  Each output block is
+ * written once and no N x N matrix reaches device memory.
+ *
+ * O and LSE must be the outputs of attn_fwd with the same causal and scale.
+ * ws must hold attn_bob_workspace_bytes(B, H, N) bytes; after the call it
+ * holds D, alpha and beta.
+ */
+attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
+                     const void* Q, const void* K, const void* V, const void* O,
+                     const float* LSE, const void* dO,
+                     const void* g_dQ, const void* g_dK, const void* g_dV,
+                     int causal, float scale,
+                     void* g_Q, void* g_K, void* g_V, void* g_dO,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two passes of attn_bwd / attn_bob as separate calls, for callers that
+ * schedule or time them on their own.  `passes` is 1 (row-block pass only),
+ * 2 (column-block pass only) or 3 (both; identical to attn_bwd / attn_bob).
+ * The column pass reads the row states the row pass left in `ws` (D and r,
+ * or D, alpha and beta), so a pass-2 call must follow a pass-1 call with the
+ * same arguments on the same stream.  The row pass writes dQ (g_Q, g_dO),
+ * the column pass dK, dV (g_K, g_V); all output pointers are validated in
+ * either case.  Other arguments and errors as for attn_bwd / attn_bob;
+ * passes outside 1..3 is ATTN_EINVAL.
+ */
+attn_status attn_bwd_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t N,
+                            int64_t d, const void* Q, const void* K, const void* V,
+                            const void* O, const float* LSE, const void* dO,
+                            int causal, float scale, int gproj,
+                            void* dQ, void* dK, void* dV,
+                            void* ws, size_t ws_bytes, void* stream);
+
+attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t N,
+                            int64_t d, const void* Q, const void* K, const void* V,
+                            const void* O, const float* LSE, const void* dO,
+                            const void* g_dQ, const void* g_dK, const void* g_dV,
+                            int causal, float scale,
+                            void* g_Q, void* g_K, void* g_V, void* g_dO,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Text of a status code (static storage). */
+const char* attn_status_str(attn_status s);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FBD_H */

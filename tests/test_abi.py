@@ -1,0 +1,81 @@
+"""The C ABI library: it loads, exports every function include/fbd.h declares,
+and its host-side argument checks reject bad calls before any launch.
+Runs without a GPU: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (the library binds to the HIP runtime torch loads)
+
+import fwd_bwd_double_amd as fbd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fbd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fbd.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"attn_fwd", "attn_bwd", "attn_bob", "attn_bwd_workspace_bytes",
+            "attn_bob_workspace_bytes", "attn_status_str", "attn_last_hip_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_sizes(lib):
+    assert fbd.bwd_workspace_bytes(2, 3, 5) == 2 * 2 * 3 * 5 * 4
+    assert fbd.bob_workspace_bytes(2, 3, 5) == 3 * 2 * 3 * 5 * 4
+    assert fbd.bwd_workspace_bytes(0, 3, 5) == 0
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.attn_status_str(s)
+    assert lib.attn_status_str(0) == b"ok"
+
+
+FAKE = 1 << 20   # an aligned address that is never dereferenced: checks fail first
+
+
+def fwd_call(lib, dt=0, B=1, H=1, N=8, d=64, ptrs=(FAKE, FAKE * 2, FAKE * 3), causal=1,
+             scale=0.125, out=(FAKE * 4, FAKE * 5)):
+    return lib.attn_fwd(dt, B, H, N, d, *ptrs, causal, scale, *out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=32), 2), (dict(d=128), 2), (dict(dt=7), 2), (dict(N=0), 1), (dict(B=-1), 1),
+    (dict(H=0), 1), (dict(scale=0.0), 1), (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=-1.0), 1),
+    (dict(ptrs=(0, FAKE * 2, FAKE * 3)), 1), (dict(out=(0, FAKE * 5)), 1),
+    (dict(ptrs=(FAKE + 8, FAKE * 2, FAKE * 3)), 3),
+    (dict(out=(FAKE * 2, FAKE * 5)), 1),           # output aliases an input
+    (dict(N=1 << 30), 2),                          # N * 64 beyond 32-bit indexing
+])
+def test_fwd_rejects_bad_arguments_before_launch(lib, kw, status):
+    assert fwd_call(lib, **kw) == status
+
+
+def test_bwd_and_bob_reject_small_workspace(lib):
+    p = [FAKE * (i + 1) for i in range(12)]
+    need = fbd.bwd_workspace_bytes(1, 1, 8)
+    st = lib.attn_bwd(0, 1, 1, 8, 64, *p[:5], p[5], 1, 0.125, 0, p[6], p[7], p[8], p[9],
+                      need - 4, None)
+    assert st == 4
+    st = lib.attn_bwd(0, 1, 1, 8, 64, *p[:5], p[5], 1, 0.125, 0, p[6], p[7], p[8], None,
+                      need, None)
+    assert st == 4
+    need = fbd.bob_workspace_bytes(1, 1, 8)
+    st = lib.attn_bob(0, 1, 1, 8, 64, *p[:6], p[6], p[7], p[8], 1, 0.125, p[9], p[10], p[11],
+                      FAKE * 20, FAKE * 30, need - 1, None)
+    assert st == 4
