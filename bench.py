@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=48,
                    help="heads of the workload the oracle baseline runs on")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="first run one device-to-device copy of this many MiB (a plain copy "
+                        "kernel of known size, to calibrate memory counters)")
     return p.parse_args()
 
 
@@ -95,6 +98,14 @@ def main():
         fbd.attn_bob(q, k, v, o, lse, do, g["g_dq"], g["g_dk"], g["g_dv"], causal=True,
                      scale=sc, workspace=ws_bb, outs=(gq, gk, gv, gdo), passes=2)
         ev[5].record()
+
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
            for _ in range(max(args.steps, 1))]

@@ -19,6 +19,10 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfbd.so")
 SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bob.hip"]
+# MFMA results are kept in the architectural VGPRs, so the element-wise work
+# between products needs no accumulator-register moves.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+PER_SOURCE = {"fwd.hip": VGPR_FORM, "bwd.hip": VGPR_FORM, "bob.hip": VGPR_FORM}
 ARCH = "gfx950"
 
 
@@ -39,7 +43,8 @@ def common_flags():
 def compile_one(src: str, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *PER_SOURCE.get(src, []), *extra, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -17,14 +17,14 @@
 // definition by differentiating <A, dQ> + <Bk, dK> + <C, dV>.)
 //
 // Row pass (lane = query i).  alpha_i and beta_i need the whole row, but
-// everything else is linear in them, so the pass accumulates
-//   X = sum_j R(P (W (dP - D) + U)) K_j,  Y = sum_j R(P) K_j,
-//   Z = sum_j R(P dP) K_j,  E = sum_j R(dS) Bk_j,  F = sum_j R(P W) V_j,
-//   Gc = sum_j R(P) C_j,
+// everything else is linear in them, so the pass accumulates four fp32
+// d-vectors per row
+//   XE = sum_j R(P (W (dP - D) + U)) K_j + R(dS) Bk_j,   Y = sum_j R(P) K_j,
+//   Z  = sum_j R(P dP) K_j,   FG = sum_j R(P W) V_j + R(P) C_j,
 // plus the row sums alpha_i and b_i = sum_j P (W dP + U), and after the last
 // key block applies the corrections once:
 //   beta_i = b_i - 2 alpha_i D_i,
-//   gQ = scale (X - alpha Z - beta Y + E),   gdO = F - alpha O + Gc
+//   gQ = scale (XE - alpha Z - beta Y),   gdO = FG - alpha O
 // (sum_j P_ij V_j = O_i).  It writes gQ, gdO and the row states D, alpha, beta.
 //
 // Column pass (lane = key j).  K, V, Bk, C of the workgroup's keys stay in
@@ -35,13 +35,13 @@
 
 namespace fbd {
 
-template <class T, int BN>
+template <class T, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NT) void bob_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
-    float* __restrict__ Bws, int N, int BH, int nblk, int causal, float scale) {
+    float* __restrict__ Bws, int N, int BH, int nblk, float scale) {
   constexpr int RS = Lay<T>::RS;
   using Stage = TileStage<T, BN>;
   constexpr int TS = Stage::TS;
@@ -81,11 +81,10 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
   const float lse2 = my_i < N ? LSE[soff + my_i] * LOG2E : 0.f;
 
   f32x16 X0 = zero16(), X1 = zero16(), Y0 = zero16(), Y1 = zero16();
-  f32x16 Z0 = zero16(), Z1 = zero16(), E0 = zero16(), E1 = zero16();
-  f32x16 F0 = zero16(), F1 = zero16(), G0 = zero16(), G1 = zero16();
+  f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
   float alpha = 0.f, bsum = 0.f;
 
-  const int jend = causal ? min(N, q0 + BLK) : N;
+  const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
   Stage sk, sv, sb, sc;
   sk.load(Kh, N, 0, tid);
@@ -112,8 +111,7 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
     }
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
-      const int js = j0 + jb;
-      if (qw >= N || (causal ? (js > qw + 31) : (js >= N))) break;
+      const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
       f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -125,21 +123,24 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
         mma(dp, vr, dof[kb]);
         mma(u, ld_row(Cs, jb, kb, lane), dof[kb]);
       }
-      const bool edge = causal ? (js + 31 > qw) : (js + 32 > N);
       float xs[16], ps[16], zs[16], es[16], fs[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
-        if (edge) {
+      for (int v = 0; v < 16; ++v) ps[v] = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
+      if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
           const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (causal ? (j > my_i) : (j >= N)) pv = 0.f;
+          ps[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? 0.f : ps[v];
         }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = ps[v];
         const float W = scale * w[v];
         const float dpd = dp[v] - Di;
         const float pw = pv * W;
         alpha += pw;
         bsum += pv * (W * dp[v] + u[v]);
-        ps[v] = pv;
         xs[v] = pv * (W * dpd + u[v]);
         zs[v] = pv * dp[v];
         es[v] = pv * dpd;
@@ -162,8 +163,8 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
         }
         {
           const Frag<T> a0 = ld_tr(Bt, TS, 0, jt + tt, lane), a1 = ld_tr(Bt, TS, 32, jt + tt, lane);
-          mma(E0, a0, ef);
-          mma(E1, a1, ef);
+          mma(X0, a0, ef);
+          mma(X1, a1, ef);
         }
         {
           const Frag<T> a0 = ld_tr(Vt, TS, 0, jt + tt, lane), a1 = ld_tr(Vt, TS, 32, jt + tt, lane);
@@ -172,8 +173,8 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
         }
         {
           const Frag<T> a0 = ld_tr(Ct, TS, 0, jt + tt, lane), a1 = ld_tr(Ct, TS, 32, jt + tt, lane);
-          mma(G0, a0, pf);
-          mma(G1, a1, pf);
+          mma(F0, a0, pf);
+          mma(F1, a1, pf);
         }
       }
     }
@@ -183,18 +184,18 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
   const float beta = bsum - 2.f * alpha * Di;
   float out[16], ov[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - beta * Y0[v] + E0[v]);
+  for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - beta * Y0[v]);
   st_cols(gQ + hoff, N, qw, 0, lane, out);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = scale * (X1[v] - alpha * Z1[v] - beta * Y1[v] + E1[v]);
+  for (int v = 0; v < 16; ++v) out[v] = scale * (X1[v] - alpha * Z1[v] - beta * Y1[v]);
   st_cols(gQ + hoff, N, qw, 32, lane, out);
   ld_cols(O + hoff, N, qw, 0, lane, ov);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = F0[v] - alpha * ov[v] + G0[v];
+  for (int v = 0; v < 16; ++v) out[v] = F0[v] - alpha * ov[v];
   st_cols(gdO + hoff, N, qw, 0, lane, out);
   ld_cols(O + hoff, N, qw, 32, lane, ov);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = F1[v] - alpha * ov[v] + G1[v];
+  for (int v = 0; v < 16; ++v) out[v] = F1[v] - alpha * ov[v];
   st_cols(gdO + hoff, N, qw, 32, lane, out);
   if (h == 0 && my_i < N) {
     Dws[soff + my_i] = Di;
@@ -203,13 +204,13 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
   }
 }
 
-template <class T, int BM>
+template <class T, int BM, bool CAUSAL>
 __global__ __launch_bounds__(NT) void bob_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ LSE, const T* __restrict__ dO, const T* __restrict__ A,
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
     const float* __restrict__ Aws, const float* __restrict__ Bws, T* __restrict__ gK,
-    T* __restrict__ gV, int N, int BH, int causal, float scale) {
+    T* __restrict__ gV, int N, int BH, float scale) {
   constexpr int RS = Lay<T>::RS;
   using Stage = TileStage<T, BM>;
   constexpr int TS = Stage::TS;
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
   ld_frags(C + hoff, N, kw, lane, cf);
   f32x16 gk0 = zero16(), gk1 = zero16(), gv0 = zero16(), gv1 = zero16();
 
-  const int istart = causal ? k0 : 0;
+  const int istart = CAUSAL ? k0 : 0;
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
   Stage sq, sdo, sa;
   float lrow = INFINITY, drow = 0.f, arow = 0.f, brow = 0.f;
@@ -282,8 +283,8 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
-      if (kw >= N || is >= N) break;
-      if (causal && is + 31 < kw) continue;
+      // all waves compute all sub-blocks: rows before a key (causal) are masked
+      // below, rows past N have LSE = +inf and so P = 0
       f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -295,8 +296,7 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
         mma(dp, dr, vf[kb]);
         mma(u, dr, cf[kb]);
       }
-      const bool diag = causal && (is == kw);
-      float shs[16], dss[16], hs[16];
+      float shs[16], dss[16], hs[16], ps[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rbase = ib + 8 * q + 4 * h;
@@ -305,10 +305,15 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
         const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[rbase]);
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sB[rbase]);
 #pragma unroll
+        for (int r = 0; r < 4; ++r) ps[4 * q + r] = __builtin_amdgcn_exp2f(s[4 * q + r] * sl2 - l4[r]);
+        if (CAUSAL && is <= kw) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ps[4 * q + r] = (my_j > i0 + rbase + r) ? 0.f : ps[4 * q + r];
+        }
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * q + r;
-          float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - l4[r]);
-          if (diag && my_j > i0 + rbase + r) pv = 0.f;
+          const float pv = ps[v];
           const float W = scale * w[v];
           const float dpd = dp[v] - d4[r];
           dss[v] = pv * dpd;
@@ -345,27 +350,27 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
   st_cols(gV + hoff, N, kw, 32, lane, out);
 }
 
-template <class T>
+template <class T, bool CAUSAL>
 static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
-                               float* Dws, float* Aws, float* Bws, int BH, int N, int causal,
-                               float scale, int passes, hipStream_t st) {
+                               float* Dws, float* Aws, float* Bws, int BH, int N, float scale,
+                               int passes, hipStream_t st) {
   constexpr int BN = 32, BM = 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
-    hipLaunchKernelGGL((bob_row_kernel<T, BN>), dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q,
-                       (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO, (const T*)gdQ,
-                       (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws, N, BH,
-                       nblk, causal, scale);
+    hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
+                       (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws,
+                       N, BH, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bob_col_kernel<T, BM>), dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q,
-                     (const T*)K, (const T*)V, LSE, (const T*)dO, (const T*)gdQ, (const T*)gdK,
-                     (const T*)gdV, (const float*)Dws, (const float*)Aws, (const float*)Bws,
-                     (T*)gK, (T*)gV, N, BH, causal, scale);
+  hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
+                     (const T*)Q, (const T*)K, (const T*)V, LSE, (const T*)dO, (const T*)gdQ,
+                     (const T*)gdK, (const T*)gdV, (const float*)Dws, (const float*)Aws,
+                     (const float*)Bws, (T*)gK, (T*)gV, N, BH, scale);
   return hipGetLastError();
 }
 
@@ -374,11 +379,12 @@ hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, int BH, int N, int causal, float scale, int passes,
                       hipStream_t st) {
+#define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, BH, N, \
+                     scale, passes, st
   if (dt == 0)
-    return launch_bob_t<bf16>(Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws,
-                              BH, N, causal, scale, passes, st);
-  return launch_bob_t<float>(Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws,
-                             BH, N, causal, scale, passes, st);
+    return causal ? launch_bob_t<bf16, true>(FBD_BOB_ARGS) : launch_bob_t<bf16, false>(FBD_BOB_ARGS);
+  return causal ? launch_bob_t<float, true>(FBD_BOB_ARGS) : launch_bob_t<float, false>(FBD_BOB_ARGS);
+#undef FBD_BOB_ARGS
 }
 
 }  // namespace fbd

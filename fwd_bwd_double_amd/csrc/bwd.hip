@@ -24,12 +24,12 @@
 
 namespace fbd {
 
-template <class T, int BN, bool GPROJ>
+template <class T, int BN, bool GPROJ, bool CAUSAL>
 __global__ __launch_bounds__(NT) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, int N, int BH, int nblk,
-    int causal, float scale) {
+    float scale) {
   constexpr int RS = Lay<T>::RS;
   using Stage = TileStage<T, BN>;
   constexpr int TS = Stage::TS;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
   f32x16 pk0 = zero16(), pk1 = zero16();
   float r = 0.f;
 
-  const int jend = causal ? min(N, q0 + BLK) : N;
+  const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
   Stage sk, sv;
   sk.load(Kh, N, 0, tid);
@@ -82,26 +82,25 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
     }
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
-      const int js = j0 + jb;
-      if (qw >= N || (causal ? (js > qw + 31) : (js >= N))) break;
-      f32x16 s = zero16(), dp = zero16();
+      const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
+      f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        mma(s, ld_row(Ks, jb, kb, lane), qf[kb]);
-        mma(dp, ld_row(Vs, jb, kb, lane), dof[kb]);
+        mma(sacc, ld_row(Ks, jb, kb, lane), qf[kb]);
+        mma(dpacc, ld_row(Vs, jb, kb, lane), dof[kb]);
       }
-      const bool edge = causal ? (js + 31 > qw) : (js + 32 > N);
       float p[16], ds[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
-        if (edge) {
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - lse2);
+      if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
           const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (causal ? (j > my_i) : (j >= N)) pv = 0.f;
+          p[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? 0.f : p[v];
         }
-        p[v] = pv;
-        ds[v] = pv * (dp[v] - Di);
       }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ds[v] = p[v] * (dpacc[v] - Di);
       const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
       const int jt = jb / 16;
       const Frag<T> a00 = ld_tr(Kt, TS, 0, jt, lane), a01 = ld_tr(Kt, TS, 0, jt + 1, lane);
@@ -143,12 +142,12 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
   }
 }
 
-template <class T, int BM, bool GPROJ>
+template <class T, int BM, bool GPROJ, bool CAUSAL>
 __global__ __launch_bounds__(NT) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ LSE, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
-    int causal, float scale) {
+    float scale) {
   constexpr int RS = Lay<T>::RS;
   using Stage = TileStage<T, BM>;
   constexpr int TS = Stage::TS;
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
   ld_frags(V + hoff, N, kw, lane, vf);
   f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
 
-  const int istart = causal ? k0 : 0;   // k0 is a multiple of BM
+  const int istart = CAUSAL ? k0 : 0;   // k0 is a multiple of BM
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
   Stage sq, sdo;
   float lrow = INFINITY, drow = 0.f;
@@ -219,15 +218,14 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
-      if (kw >= N || is >= N) break;
-      if (causal && is + 31 < kw) continue;
-      f32x16 s = zero16(), dp = zero16();
+      // all waves compute all sub-blocks: rows before a key (causal) are masked
+      // below, rows past N have LSE = +inf and so P = 0
+      f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        mma(s, ld_row(Qs, ib, kb, lane), kf[kb]);
-        mma(dp, ld_row(dOs, ib, kb, lane), vf[kb]);
+        mma(sacc, ld_row(Qs, ib, kb, lane), kf[kb]);
+        mma(dpacc, ld_row(dOs, ib, kb, lane), vf[kb]);
       }
-      const bool diag = causal && (is == kw);
       float p[16], ds[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -236,12 +234,19 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * q + r;
-          float pv = __builtin_amdgcn_exp2f(s[v] * sl2 - l4[r]);
-          if (diag && my_j > is + 8 * q + 4 * h + r) pv = 0.f;
-          p[v] = pv;
-          ds[v] = pv * (dp[v] - d4[r]);
+          p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - l4[r]);
+          ds[v] = dpacc[v] - d4[r];
         }
       }
+      if (CAUSAL && is <= kw) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
+          p[v] = (my_j > i) ? 0.f : p[v];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ds[v] *= p[v];
       const Frag<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
       const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
       const int it = ib / 16;
@@ -276,25 +281,37 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
   st_cols(dV + hoff, N, kw, 32, lane, out);
 }
 
-template <class T, bool GPROJ>
+template <class T, bool GPROJ, bool CAUSAL>
 static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
-                               float* Dws, float* Rws, int BH, int N, int causal, float scale,
-                               int passes, hipStream_t st) {
+                               float* Dws, float* Rws, int BH, int N, float scale, int passes,
+                               hipStream_t st) {
   constexpr int BN = 64, BM = 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
-    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ>), dim3(nblk * BH), dim3(NT), 0, st,
+    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
-                       (T*)dQ, Dws, Rws, N, BH, nblk, causal, scale);
+                       (T*)dQ, Dws, Rws, N, BH, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ>), dim3(nblk * BH), dim3(NT), 0, st,
+  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                      (const T*)Q, (const T*)K, (const T*)V, LSE, (const T*)dO, (const float*)Dws,
-                     (const float*)Rws, (T*)dK, (T*)dV, N, BH, causal, scale);
+                     (const float*)Rws, (T*)dK, (T*)dV, N, BH, scale);
   return hipGetLastError();
+}
+
+template <class T, bool GPROJ>
+static hipError_t launch_bwd_c(int causal, const void* Q, const void* K, const void* V,
+                               const void* O, const float* LSE, const void* dO, void* dQ,
+                               void* dK, void* dV, float* Dws, float* Rws, int BH, int N,
+                               float scale, int passes, hipStream_t st) {
+  if (causal)
+    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, scale,
+                                        passes, st);
+  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, scale,
+                                       passes, st);
 }
 
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
@@ -303,15 +320,15 @@ hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const
                       hipStream_t st) {
   if (dt == 0) {
     if (gproj)
-      return launch_bwd_t<bf16, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
                                       scale, passes, st);
-    return launch_bwd_t<bf16, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
                                      scale, passes, st);
   }
   if (gproj)
-    return launch_bwd_t<float, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
                                      scale, passes, st);
-  return launch_bwd_t<float, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, causal,
+  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
                                     scale, passes, st);
 }
 

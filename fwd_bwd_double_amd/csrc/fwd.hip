@@ -18,11 +18,11 @@
 
 namespace fbd {
 
-template <class T, int BN>
+template <class T, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NT) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                  const T* __restrict__ V, T* __restrict__ O,
                                                  float* __restrict__ LSE, int N, int BH, int nblk,
-                                                 int causal, float scale) {
+                                                 float scale) {
   constexpr int RS = Lay<T>::RS;
   using Stage = TileStage<T, BN>;
   constexpr int TS = Stage::TS;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(NT) void fwd_kernel(const T* __restrict__ Q, const 
   float m = -INFINITY, l = 0.f;
   f32x16 o0 = zero16(), o1 = zero16();
 
-  const int jend = causal ? min(N, q0 + BLK) : N;
+  const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
   Stage sk, sv;
   sk.load(Kh, N, 0, tid);
@@ -64,29 +64,37 @@ __global__ __launch_bounds__(NT) void fwd_kernel(const T* __restrict__ Q, const 
     }
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
+      // Every wave computes every sub-block of the workgroup's key range; keys
+      // after a row (causal) or past N are masked to -inf.  Keeping the waves'
+      // control flow identical keeps the accumulators in fixed registers.
       const int js = j0 + jb;
-      if (qw >= N || (causal ? (js > qw + 31) : (js >= N))) break;
-      f32x16 s = zero16();
+      f32x16 sacc = zero16();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(s, ld_row(Ks, jb, kb, lane), qf[kb]);
-      if (causal ? (js + 31 > qw) : (js + 32 > N)) {
+      for (int kb = 0; kb < 4; ++kb) mma(sacc, ld_row(Ks, jb, kb, lane), qf[kb]);
+      float s[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = sacc[v];
+      if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (causal ? (j > my_i) : (j >= N)) s[v] = -INFINITY;
+          s[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? -INFINITY : s[v];
         }
       }
       float mt = s[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s[v]);
       mt = fmaxf(mt, other_half(mt));
+      // the first sub-block (key 0) is visible to every row, so m is finite
+      // from then on and a fully masked sub-block leaves it unchanged
       const float mn = fmaxf(m, mt);
-      // every row sees key js here (js <= its index, or js < N), so mn is finite
-      const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
-      m = mn;
-      l *= alpha;
-      o0 *= alpha;
-      o1 *= alpha;
+      if (__any(mn > m)) {
+        const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
+        l *= alpha;
+        o0 *= alpha;
+        o1 *= alpha;
+        m = mn;
+      }
       float p[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -114,20 +122,24 @@ __global__ __launch_bounds__(NT) void fwd_kernel(const T* __restrict__ Q, const 
     LSE[(size_t)wk.head * N + my_i] = scale * m + __builtin_amdgcn_logf(l) * LN2;
 }
 
-template <class T>
+template <class T, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               int BH, int N, int causal, float scale, hipStream_t st) {
+                               int BH, int N, float scale, hipStream_t st) {
   constexpr int BN = 64;
   const int nblk = (N + BLK - 1) / BLK;
-  hipLaunchKernelGGL((fwd_kernel<T, BN>), dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q,
-                     (const T*)K, (const T*)V, (T*)O, LSE, N, BH, nblk, causal, scale);
+  hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q,
+                     (const T*)K, (const T*)V, (T*)O, LSE, N, BH, nblk, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
                       int BH, int N, int causal, float scale, hipStream_t st) {
-  if (dt == 0) return launch_fwd_t<bf16>(Q, K, V, O, LSE, BH, N, causal, scale, st);
-  return launch_fwd_t<float>(Q, K, V, O, LSE, BH, N, causal, scale, st);
+  if (dt == 0) {
+    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, N, scale, st);
+    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, N, scale, st);
+  }
+  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, N, scale, st);
+  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, N, scale, st);
 }
 
 }  // namespace fbd
