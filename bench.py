@@ -142,7 +142,8 @@ def main():
     dom = max(names, key=lambda n: kern_ms[n])
     ach = per_kernel[dom]["executed_tflops"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "traffic": stored_traffic(dom, w.name), "traffic_unit": "bytes per launch",
                 "flop_per_launch": UNITS[dom] * unit}
 
     cpu = None
@@ -161,6 +162,41 @@ def main():
         "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9,
     }
     print(json.dumps(line), flush=True)
+
+
+# Which sources define each kernel: a stored counter figure is used only while
+# these files are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "fwd": ["fwd.hip"], "bwd_row": ["bwd.hip"], "bwd_col": ["bwd.hip"],
+    "bob_row": ["bob.hip"], "bob_col": ["bob.hip"],
+}
+COMMON_SOURCES = ["tile.hpp", "launch.hpp", "../build.py"]
+
+
+def kernel_source_sha(kernel):
+    import hashlib
+    csrc = os.path.join(HERE, "fwd_bwd_double_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the stored rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (each scaled by the same counter's reading for a copy
+    kernel of known size), or None when no summary exists for the current
+    kernel source."""
+    path = os.path.join(HERE, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(x, w, nheads):
@@ -188,4 +224,7 @@ def cpu_baseline(x, w, nheads):
 
 
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 2 and sys.argv[1] == "--source-sha":
+        print(kernel_source_sha(sys.argv[2]))
+    else:
+        main()

@@ -179,8 +179,8 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
       }
     }
   }
-  alpha += other_half(alpha);
-  bsum += other_half(bsum);
+  alpha = half_sum(alpha);
+  bsum = half_sum(bsum);
   const float beta = bsum - 2.f * alpha * Di;
   float out[16], ov[16];
 #pragma unroll
@@ -356,7 +356,8 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
                                float* Dws, float* Aws, float* Bws, int BH, int N, float scale,
                                int passes, hipStream_t st) {
-  constexpr int BN = 32, BM = 64;
+  // fp32 operands take twice the LDS per row: they keep the smallest tiles
+  constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
     hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,

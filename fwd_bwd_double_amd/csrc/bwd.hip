@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
   }
   float out[16];
   if constexpr (GPROJ) {
-    r += other_half(r);
+    r = half_sum(r);
 #pragma unroll
     for (int v = 0; v < 16; ++v) out[v] = scale * (dq0[v] - r * pk0[v]);
     st_cols(dQ + hoff, N, qw, 0, lane, out);
@@ -286,7 +286,8 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
                                float* Dws, float* Rws, int BH, int N, float scale, int passes,
                                hipStream_t st) {
-  constexpr int BN = 64, BM = 64;
+  // fp32 operands take twice the LDS per row: they keep the smallest tiles
+  constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
     hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,

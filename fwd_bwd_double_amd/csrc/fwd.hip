@@ -2,52 +2,68 @@
 //
 // Tiled online softmax as on the FlashAttention explainer page (marketmaker.cc,
 // flash-attention-trading-models), sections "The Flash Attention algorithm"
-// and "The online softmax recurrence": a workgroup owns 128 query rows (32 per
-// wave, one query per lane), streams 64-key tiles of K and V through LDS and
-// keeps per row a running raw-score max m, a running sum l and an fp32 output
-// accumulator, rescaling both by exp(scale*(m_old - m_new)) whenever the max
-// grows.  The division by l happens once, after the last tile.  The exponent
-// is formed as (S - m) * scale: subtracting the max before scaling makes the
-// largest weight exactly 1 (GProj page, rit.work
+// and "The online softmax recurrence": a workgroup owns 128 query rows, streams
+// 64-key tiles of K and V through LDS, and keeps per row a running raw-score
+// max m, a running sum l and an fp32 output accumulator, rescaling both by
+// exp(scale*(m_old - m_new)) whenever the max grows (a wave skips the rescale
+// when none of its rows' max moved).  The division by l happens once, after
+// the last tile.  The exponent is formed as (S - m) * scale: subtracting the
+// max before scaling makes the largest weight exactly 1 (GProj page, rit.work
 // flashattention-bf16-gradient-gproj, section "Why the error shows up at the
 // end of training").  Key tiles entirely in the future of the workgroup's rows
 // are never loaded (explainer page, section "Causal masking is where trading
 // gets a discount").
+//
+// Layout: 2 waves per workgroup, 64 queries per wave as two groups of 32, one
+// query per lane in each group.  Both groups use every K and V fragment a wave
+// reads from LDS, which halves LDS traffic per FLOP against one group per
+// wave.  The row sum l adds the bf16-rounded probabilities -- the values the
+// P V product uses -- with v_dot2_f32_bf16.
 #include "launch.hpp"
 #include "tile.hpp"
 
 namespace fbd {
 
+constexpr int FWD_WAVES = 2;
+constexpr int FWD_NT = 64 * FWD_WAVES;
+constexpr int FWD_G = 2;                              // 32-query groups per wave
+constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;    // 128 query rows per workgroup
+
 template <class T, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NT) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                 const T* __restrict__ V, T* __restrict__ O,
-                                                 float* __restrict__ LSE, int N, int BH, int nblk,
-                                                 float scale) {
+__global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
+                                                     const T* __restrict__ K,
+                                                     const T* __restrict__ V, T* __restrict__ O,
+                                                     float* __restrict__ LSE, int N, int BH,
+                                                     int nblk, float scale) {
   constexpr int RS = Lay<T>::RS;
-  using Stage = TileStage<T, BN>;
+  using Stage = TileStage<T, BN, FWD_NT>;
   constexpr int TS = Stage::TS;
   __shared__ __attribute__((aligned(16))) T Ks[BN * RS];
   __shared__ __attribute__((aligned(16))) T Vt[HD * TS];
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
-  const T* Qh = Q + hoff;
   const T* Kh = K + hoff;
   const T* Vh = V + hoff;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q0 = wk.blk * BLK;
-  const int qw = q0 + wave * WROWS;
-  const int my_i = qw + (lane & 31);
+  const int q0 = wk.blk * FWD_BLK;
+  const int qw = q0 + wave * FWD_G * WROWS;
   const int h = lane >> 5;
   const float sl2 = scale * LOG2E;
 
-  Frag<T> qf[4];
-  ld_frags(Qh, N, qw, lane, qf);
+  Frag<T> qf[FWD_G][4];
+  float m[FWD_G], l[FWD_G];
+  f32x16 o[FWD_G][2];
+#pragma unroll
+  for (int g = 0; g < FWD_G; ++g) {
+    ld_frags(Q + hoff, N, qw + g * WROWS, lane, qf[g]);
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+    o[g][0] = zero16();
+    o[g][1] = zero16();
+  }
 
-  float m = -INFINITY, l = 0.f;
-  f32x16 o0 = zero16(), o1 = zero16();
-
-  const int jend = CAUSAL ? min(N, q0 + BLK) : N;
+  const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
   Stage sk, sv;
   sk.load(Kh, N, 0, tid);
@@ -62,73 +78,93 @@ __global__ __launch_bounds__(NT) void fwd_kernel(const T* __restrict__ Q, const 
       sk.load(Kh, N, j0 + BN, tid);
       sv.load(Vh, N, j0 + BN, tid);
     }
+    // Every wave computes every 32-key sub-block of the tile; keys after a
+    // row (causal) or past N are masked to -inf.  Identical control flow in
+    // all waves keeps the accumulators in fixed registers.
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
-      // Every wave computes every sub-block of the workgroup's key range; keys
-      // after a row (causal) or past N are masked to -inf.  Keeping the waves'
-      // control flow identical keeps the accumulators in fixed registers.
       const int js = j0 + jb;
-      f32x16 sacc = zero16();
+      Frag<T> kr[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(sacc, ld_row(Ks, jb, kb, lane), qf[kb]);
-      float s[16];
+      for (int kb = 0; kb < 4; ++kb) kr[kb] = ld_row(Ks, jb, kb, lane);
+      Frag<T> pf[FWD_G][2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = sacc[v];
-      if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
+      for (int g = 0; g < FWD_G; ++g) {
+        const int qg = qw + g * WROWS;
+        const int my_i = qg + (lane & 31);
+        f32x16 sacc = zero16();
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          s[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? -INFINITY : s[v];
+        for (int kb = 0; kb < 4; ++kb) mma(sacc, kr[kb], qf[g][kb]);
+        float s[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = sacc[v];
+        if (CAUSAL ? (js + 31 > qg) : (js + 32 > N)) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
+            s[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? -INFINITY : s[v];
+          }
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s[v]);
+        mt = half_max(mt);
+        // key 0 is visible to every row, so m is finite after the first
+        // sub-block and a fully masked sub-block leaves it unchanged
+        const float mn = fmaxf(m[g], mt);
+        if (__any(mn > m[g])) {
+          const float alpha = __builtin_amdgcn_exp2f((m[g] - mn) * sl2);
+          l[g] *= alpha;
+          o[g][0] *= alpha;
+          o[g][1] *= alpha;
+          m[g] = mn;
+        }
+        float p[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f((s[v] - mn) * sl2);
+        pf[g][0] = pack8<T>(p);
+        pf[g][1] = pack8<T>(p + 8);
+        l[g] = frag_acc_sum(pf[g][0], l[g]);
+        l[g] = frag_acc_sum(pf[g][1], l[g]);
+      }
+      const int jt = jb / 16;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const Frag<T> v0 = ld_tr(Vt, TS, 0, jt + tt, lane);
+        const Frag<T> v1 = ld_tr(Vt, TS, 32, jt + tt, lane);
+#pragma unroll
+        for (int g = 0; g < FWD_G; ++g) {
+          mma(o[g][0], v0, pf[g][tt]);
+          mma(o[g][1], v1, pf[g][tt]);
         }
       }
-      float mt = s[0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s[v]);
-      mt = fmaxf(mt, other_half(mt));
-      // the first sub-block (key 0) is visible to every row, so m is finite
-      // from then on and a fully masked sub-block leaves it unchanged
-      const float mn = fmaxf(m, mt);
-      if (__any(mn > m)) {
-        const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
-        l *= alpha;
-        o0 *= alpha;
-        o1 *= alpha;
-        m = mn;
-      }
-      float p[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = __builtin_amdgcn_exp2f((s[v] - mn) * sl2);
-        l += p[v];
-      }
-      const Frag<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
-      const int jt = jb / 16;
-      mma(o0, ld_tr(Vt, TS, 0, jt, lane), pf0);
-      mma(o0, ld_tr(Vt, TS, 0, jt + 1, lane), pf1);
-      mma(o1, ld_tr(Vt, TS, 32, jt, lane), pf0);
-      mma(o1, ld_tr(Vt, TS, 32, jt + 1, lane), pf1);
     }
   }
-  l += other_half(l);
-  const float inv = 1.f / l;
-  float out[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = o0[v] * inv;
-  st_cols(O + hoff, N, qw, 0, lane, out);
+  for (int g = 0; g < FWD_G; ++g) {
+    const int qg = qw + g * WROWS;
+    const int my_i = qg + (lane & 31);
+    const float lt = half_sum(l[g]);
+    const float inv = 1.f / lt;
+    float out[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = o1[v] * inv;
-  st_cols(O + hoff, N, qw, 32, lane, out);
-  if (h == 0 && my_i < N)
-    LSE[(size_t)wk.head * N + my_i] = scale * m + __builtin_amdgcn_logf(l) * LN2;
+    for (int v = 0; v < 16; ++v) out[v] = o[g][0][v] * inv;
+    st_cols(O + hoff, N, qg, 0, lane, out);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = o[g][1][v] * inv;
+    st_cols(O + hoff, N, qg, 32, lane, out);
+    if (h == 0 && my_i < N)
+      LSE[(size_t)wk.head * N + my_i] = scale * m[g] + __builtin_amdgcn_logf(lt) * LN2;
+  }
 }
 
 template <class T, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int BH, int N, float scale, hipStream_t st) {
-  constexpr int BN = 64;
-  const int nblk = (N + BLK - 1) / BLK;
-  hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q,
-                     (const T*)K, (const T*)V, (T*)O, LSE, N, BH, nblk, scale);
+  constexpr int BN = sizeof(T) == 2 ? FBD_FWD_BN : 64;
+  const int nblk = (N + FWD_BLK - 1) / FWD_BLK;
+  hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
+                     (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, nblk, scale);
   return hipGetLastError();
 }
 

@@ -4,6 +4,24 @@
 
 #include <hip/hip_runtime.h>
 
+// Streamed tile sizes (rows of the streamed operand per LDS stage): keys per
+// tile for the row passes (BN), queries per tile for the column passes (BM).
+#ifndef FBD_FWD_BN
+#define FBD_FWD_BN 64
+#endif
+#ifndef FBD_BWD_BN
+#define FBD_BWD_BN 64
+#endif
+#ifndef FBD_BWD_BM
+#define FBD_BWD_BM 64
+#endif
+#ifndef FBD_BOB_BN
+#define FBD_BOB_BN 32
+#endif
+#ifndef FBD_BOB_BM
+#define FBD_BOB_BM 64
+#endif
+
 namespace fbd {
 
 // dt: 0 = bf16, 1 = fp32.  BH = batch * heads.  Pointers are device pointers.

@@ -68,6 +68,39 @@ __device__ __forceinline__ f32x16 zero16() {
 // Value held by lane l ^ 32.
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
 
+// Combine a value across the two half-waves (lanes l and l ^ 32) with
+// v_permlane32_swap: the swap of x with itself returns lanes 0..31 of x in
+// both halves of the first result and lanes 32..63 in both halves of the
+// second, so op(first, second) is the same in every lane of a pair.
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum of the eight element-type values of an operand fragment, added to acc
+// (bf16: four v_dot2_f32_bf16 against (1, 1)).
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float frag_acc_sum(const Frag<bf16>& f, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 pr = {f.v[2 * k], f.v[2 * k + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_acc_sum(const Frag<float>& f, float acc) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc += f.v[k];
+  return acc;
+}
+
 // Round to the element type and back (round-to-nearest-even for bf16).
 __device__ __forceinline__ float rnd(float x, bf16*) { return (float)(bf16)x; }
 __device__ __forceinline__ float rnd(float x, float*) { return x; }
@@ -169,7 +202,7 @@ __device__ __forceinline__ float row_dot(const Frag<T> (&x)[4], const Frag<T> (&
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int k = 0; k < 8; ++k) s += (float)x[kb].v[k] * (float)y[kb].v[k];
-  return s + other_half(s);
+  return half_sum(s);
 }
 
 // Store a wave's 32 rows x 32 columns block of a result held in the
@@ -222,18 +255,18 @@ __device__ __forceinline__ void ld_cols(const T* X, int n, int r0, int c0, int l
 // (2p, 2p+1) times one 16-byte column chunk c; the thread holds both rows'
 // chunks so that the transposed store can write two sequence positions per
 // 32-bit word (bf16) or 64-bit word (fp32).
-template <class T, int R>
+template <class T, int R, int NTH = NT>
 struct TileStage {
   static constexpr int E = 16 / sizeof(T);          // elements per chunk
   static constexpr int CPR = HD / E;                 // chunks per row
   static constexpr int UNITS = (R / 2) * CPR;
-  static constexpr int U = (UNITS + NT - 1) / NT;    // units per thread
+  static constexpr int U = (UNITS + NTH - 1) / NTH;  // units per thread
   uint4 a[U], b[U];
 
   __device__ __forceinline__ void load(const T* X, int n, int r0, int tid) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int unit = tid + NT * u;
+      const int unit = tid + NTH * u;
       const int p = unit % (R / 2), c = unit / (R / 2);
       const int row = r0 + 2 * p;
       a[u] = make_uint4(0, 0, 0, 0);
@@ -261,7 +294,7 @@ struct TileStage {
   __device__ __forceinline__ void store_rows(T* tile, int tid) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int unit = tid + NT * u;
+      const int unit = tid + NTH * u;
       if (unit < UNITS) {
         const int p = unit % (R / 2), c = unit / (R / 2);
         *reinterpret_cast<uint4*>(tile + (2 * p) * Lay<T>::RS + c * E) = a[u];
@@ -275,7 +308,7 @@ struct TileStage {
   __device__ __forceinline__ void store_tr(T* tileT, int tid) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int unit = tid + NT * u;
+      const int unit = tid + NTH * u;
       if (unit < UNITS) {
         const int p = unit % (R / 2), c = unit / (R / 2);
         if constexpr (sizeof(T) == 2) {
