@@ -14,20 +14,23 @@
 // are never loaded (explainer page, section "Causal masking is where trading
 // gets a discount").
 //
-// Layout: 2 waves per workgroup, 64 queries per wave as two groups of 32, one
-// query per lane in each group.  Both groups use every K and V fragment a wave
-// reads from LDS, which halves LDS traffic per FLOP against one group per
-// wave.  The row sum l adds the bf16-rounded probabilities -- the values the
-// P V product uses -- with v_dot2_f32_bf16.
+// Global loads run two tiles ahead of the compute: two register stages
+// alternate, each refilled right after it has been written to LDS.
+//
+// Layout: FWD_WAVES waves per workgroup, FWD_G groups of 32 queries per wave,
+// one query per lane in each group (4 x 1 measured fastest on MI355X: more
+// groups per wave halve LDS reads per FLOP but cost occupancy).  The row sum
+// l adds the bf16-rounded probabilities -- the values the P V product uses --
+// with v_dot2_f32_bf16.
 #include "launch.hpp"
 #include "tile.hpp"
 
 namespace fbd {
 
-constexpr int FWD_WAVES = 2;
+constexpr int FWD_WAVES = FBD_FWD_WAVES;
 constexpr int FWD_NT = 64 * FWD_WAVES;
-constexpr int FWD_G = 2;                              // 32-query groups per wave
-constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;    // 128 query rows per workgroup
+constexpr int FWD_G = FBD_FWD_G;                      // 32-query groups per wave
+constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;    // query rows per workgroup
 
 template <class T, int BN, bool CAUSAL>
 __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
@@ -65,18 +68,19 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 
   const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
-  Stage sk, sv;
-  sk.load(Kh, N, 0, tid);
-  sv.load(Vh, N, 0, tid);
-  for (int t = 0; t < ntiles; ++t) {
+
+  // One tile: stage it into LDS from registers, refill those registers with
+  // the tile two steps ahead (so a load has two tiles of compute to land),
+  // then compute.
+  auto tile = [&](int t, Stage& sk, Stage& sv) {
     const int j0 = t * BN;
     __syncthreads();
     sk.store_rows(Ks, tid);
     sv.store_tr(Vt, tid);
     __syncthreads();
-    if (t + 1 < ntiles) {
-      sk.load(Kh, N, j0 + BN, tid);
-      sv.load(Vh, N, j0 + BN, tid);
+    if (t + 2 < ntiles) {
+      sk.load(Kh, N, j0 + 2 * BN, tid);
+      sv.load(Vh, N, j0 + 2 * BN, tid);
     }
     // Every wave computes every 32-key sub-block of the tile; keys after a
     // row (causal) or past N are masked to -inf.  Identical control flow in
@@ -139,6 +143,18 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
         }
       }
     }
+  };
+
+  Stage sk0, sv0, sk1, sv1;
+  sk0.load(Kh, N, 0, tid);
+  sv0.load(Vh, N, 0, tid);
+  if (ntiles > 1) {
+    sk1.load(Kh, N, BN, tid);
+    sv1.load(Vh, N, BN, tid);
+  }
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, sk0, sv0);
+    if (t + 1 < ntiles) tile(t + 1, sk1, sv1);
   }
 #pragma unroll
   for (int g = 0; g < FWD_G; ++g) {

@@ -9,6 +9,13 @@
 #ifndef FBD_FWD_BN
 #define FBD_FWD_BN 64
 #endif
+// forward: waves per workgroup and 32-query groups per wave
+#ifndef FBD_FWD_WAVES
+#define FBD_FWD_WAVES 4
+#endif
+#ifndef FBD_FWD_G
+#define FBD_FWD_G 1
+#endif
 #ifndef FBD_BWD_BN
 #define FBD_BWD_BN 64
 #endif
