@@ -38,6 +38,10 @@ attn_status check_shape(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t 
   if (bh > (int64_t)INT_MAX / N) return ATTN_EUNSUPPORTED;     // B*H*N fits int
   const int64_t nblk = (N + 127) / 128;
   if (bh > (int64_t)INT_MAX / nblk) return ATTN_EUNSUPPORTED;  // grid size
+  // tiles are fetched through buffer resources with 32-bit byte offsets that
+  // may run one tile past the head's last row
+  const int64_t head_bytes = N * 64 * (dt == ATTN_BF16 ? 2 : 4);
+  if (head_bytes + (int64_t)(1 << 20) > (int64_t)UINT32_MAX) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 

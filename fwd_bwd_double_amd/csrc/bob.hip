@@ -30,6 +30,11 @@
 // Column pass (lane = key j).  K, V, Bk, C of the workgroup's keys stay in
 // registers; query blocks stream past them with their row states, and
 // gK, gV are accumulated and written once.
+//
+// Streamed tiles reach LDS by buffer -> LDS DMA into two alternating buffers
+// (the copy of tile t+1 runs while tile t is computed) and are stored once,
+// row-major; products over the sequence index read them with the transposing
+// LDS read.
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -42,25 +47,19 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
     float* __restrict__ Bws, int N, int BH, int nblk, float scale) {
-  constexpr int RS = Lay<T>::RS;
-  using Stage = TileStage<T, BN>;
-  constexpr int TS = Stage::TS;
-  __shared__ __attribute__((aligned(16))) T Ks[BN * RS];
-  __shared__ __attribute__((aligned(16))) T Vs[BN * RS];
-  __shared__ __attribute__((aligned(16))) T Bs[BN * RS];
-  __shared__ __attribute__((aligned(16))) T Cs[BN * RS];
-  __shared__ __attribute__((aligned(16))) T Kt[HD * TS];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * TS];
-  __shared__ __attribute__((aligned(16))) T Bt[HD * TS];
-  __shared__ __attribute__((aligned(16))) T Ct[HD * TS];
+  __shared__ __attribute__((aligned(16))) T Kb[2][BN * HD];
+  __shared__ __attribute__((aligned(16))) T Vb[2][BN * HD];
+  __shared__ __attribute__((aligned(16))) T Bb[2][BN * HD];
+  __shared__ __attribute__((aligned(16))) T Cb[2][BN * HD];
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
   const size_t soff = (size_t)wk.head * N;
-  const T* Kh = K + hoff;
-  const T* Vh = V + hoff;
-  const T* Bh = Bk + hoff;
-  const T* Ch = C + hoff;
+  const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
+  const auto rk = make_rsrc(K + hoff, hbytes);
+  const auto rv = make_rsrc(V + hoff, hbytes);
+  const auto rb = make_rsrc(Bk + hoff, hbytes);
+  const auto rc = make_rsrc(C + hoff, hbytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q0 = wk.blk * BLK;
   const int qw = q0 + wave * WROWS;
@@ -86,29 +85,23 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
 
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
-  Stage sk, sv, sb, sc;
-  sk.load(Kh, N, 0, tid);
-  sv.load(Vh, N, 0, tid);
-  sb.load(Bh, N, 0, tid);
-  sc.load(Ch, N, 0, tid);
+  auto stage = [&](int j0, int buf) {
+    dma_tile<T, BN, NT / 64>(rk, j0, Kb[buf], wave, lane);
+    dma_tile<T, BN, NT / 64>(rv, j0, Vb[buf], wave, lane);
+    dma_tile<T, BN, NT / 64>(rb, j0, Bb[buf], wave, lane);
+    dma_tile<T, BN, NT / 64>(rc, j0, Cb[buf], wave, lane);
+  };
+  stage(0, 0);
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BN;
-    __syncthreads();
-    sk.store_rows(Ks, tid);
-    sk.store_tr(Kt, tid);
-    sv.store_rows(Vs, tid);
-    sv.store_tr(Vt, tid);
-    sb.store_rows(Bs, tid);
-    sb.store_tr(Bt, tid);
-    sc.store_rows(Cs, tid);
-    sc.store_tr(Ct, tid);
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      sk.load(Kh, N, j0 + BN, tid);
-      sv.load(Vh, N, j0 + BN, tid);
-      sb.load(Bh, N, j0 + BN, tid);
-      sc.load(Ch, N, j0 + BN, tid);
-    }
+    const int cur = t & 1;
+    wait_dma();
+    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
+    if (t + 1 < ntiles) stage(j0 + BN, cur ^ 1);
+    const T* Ks = Kb[cur];
+    const T* Vs = Vb[cur];
+    const T* Bs = Bb[cur];
+    const T* Cs = Cb[cur];
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
@@ -153,7 +146,7 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
         const Frag<T> zf = pack8<T>(zs + 8 * tt), ef = pack8<T>(es + 8 * tt);
         const Frag<T> ff = pack8<T>(fs + 8 * tt);
         {
-          const Frag<T> a0 = ld_tr(Kt, TS, 0, jt + tt, lane), a1 = ld_tr(Kt, TS, 32, jt + tt, lane);
+          const Frag<T> a0 = ld_tr(Ks, 0, jt + tt, lane), a1 = ld_tr(Ks, 32, jt + tt, lane);
           mma(X0, a0, xf);
           mma(X1, a1, xf);
           mma(Y0, a0, pf);
@@ -162,17 +155,17 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
           mma(Z1, a1, zf);
         }
         {
-          const Frag<T> a0 = ld_tr(Bt, TS, 0, jt + tt, lane), a1 = ld_tr(Bt, TS, 32, jt + tt, lane);
+          const Frag<T> a0 = ld_tr(Bs, 0, jt + tt, lane), a1 = ld_tr(Bs, 32, jt + tt, lane);
           mma(X0, a0, ef);
           mma(X1, a1, ef);
         }
         {
-          const Frag<T> a0 = ld_tr(Vt, TS, 0, jt + tt, lane), a1 = ld_tr(Vt, TS, 32, jt + tt, lane);
+          const Frag<T> a0 = ld_tr(Vs, 0, jt + tt, lane), a1 = ld_tr(Vs, 32, jt + tt, lane);
           mma(F0, a0, ff);
           mma(F1, a1, ff);
         }
         {
-          const Frag<T> a0 = ld_tr(Ct, TS, 0, jt + tt, lane), a1 = ld_tr(Ct, TS, 32, jt + tt, lane);
+          const Frag<T> a0 = ld_tr(Cs, 0, jt + tt, lane), a1 = ld_tr(Cs, 32, jt + tt, lane);
           mma(F0, a0, pf);
           mma(F1, a1, pf);
         }
@@ -211,26 +204,26 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
     const float* __restrict__ Aws, const float* __restrict__ Bws, T* __restrict__ gK,
     T* __restrict__ gV, int N, int BH, float scale) {
-  constexpr int RS = Lay<T>::RS;
-  using Stage = TileStage<T, BM>;
-  constexpr int TS = Stage::TS;
-  __shared__ __attribute__((aligned(16))) T Qs[BM * RS];
-  __shared__ __attribute__((aligned(16))) T Qt[HD * TS];
-  __shared__ __attribute__((aligned(16))) T dOs[BM * RS];
-  __shared__ __attribute__((aligned(16))) T dOt[HD * TS];
-  __shared__ __attribute__((aligned(16))) T As[BM * RS];
-  __shared__ __attribute__((aligned(16))) T At[HD * TS];
-  __shared__ __attribute__((aligned(16))) float sL[BM];
-  __shared__ __attribute__((aligned(16))) float sD[BM];
-  __shared__ __attribute__((aligned(16))) float sA[BM];
-  __shared__ __attribute__((aligned(16))) float sB[BM];
+  static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
+  __shared__ __attribute__((aligned(16))) T Qb[2][BM * HD];
+  __shared__ __attribute__((aligned(16))) T dOb[2][BM * HD];
+  __shared__ __attribute__((aligned(16))) T Ab[2][BM * HD];
+  __shared__ __attribute__((aligned(16))) float sLb[2][BM];   // LSE, D, alpha, beta of the rows
+  __shared__ __attribute__((aligned(16))) float sDb[2][BM];
+  __shared__ __attribute__((aligned(16))) float sAb[2][BM];
+  __shared__ __attribute__((aligned(16))) float sBb[2][BM];
 
   const Work wk = col_work(BH);
   const size_t hoff = (size_t)wk.head * N * HD;
   const size_t soff = (size_t)wk.head * N;
-  const T* Qh = Q + hoff;
-  const T* dOh = dO + hoff;
-  const T* Ah = A + hoff;
+  const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
+  const auto rq = make_rsrc(Q + hoff, hbytes);
+  const auto rdo = make_rsrc(dO + hoff, hbytes);
+  const auto ra = make_rsrc(A + hoff, hbytes);
+  const auto rl = make_rsrc(LSE + soff, (uint32_t)N * 4u);
+  const auto rd = make_rsrc(Dws + soff, (uint32_t)N * 4u);
+  const auto ral = make_rsrc(Aws + soff, (uint32_t)N * 4u);
+  const auto rbe = make_rsrc(Bws + soff, (uint32_t)N * 4u);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = wk.blk * BLK;
   const int kw = k0 + wave * WROWS;
@@ -247,44 +240,37 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
 
   const int istart = CAUSAL ? k0 : 0;
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
-  Stage sq, sdo, sa;
-  float lrow = INFINITY, drow = 0.f, arow = 0.f, brow = 0.f;
-  auto prefetch = [&](int i0) {
-    sq.load(Qh, N, i0, tid);
-    sdo.load(dOh, N, i0, tid);
-    sa.load(Ah, N, i0, tid);
-    if (tid < BM) {
-      const int row = i0 + tid;
-      const bool ok = row < N;
-      lrow = ok ? LSE[soff + row] * LOG2E : INFINITY;   // padded rows: P = 0
-      drow = ok ? Dws[soff + row] : 0.f;
-      arow = ok ? Aws[soff + row] : 0.f;
-      brow = ok ? Bws[soff + row] : 0.f;
+  auto stage = [&](int i0, int buf) {
+    dma_tile<T, BM, NT / 64>(rq, i0, Qb[buf], wave, lane);
+    dma_tile<T, BM, NT / 64>(rdo, i0, dOb[buf], wave, lane);
+    dma_tile<T, BM, NT / 64>(ra, i0, Ab[buf], wave, lane);
+#pragma unroll
+    for (int k = 0; k < BM / 64; ++k) {
+      if (wave == 0) dma_rows_f32(rl, i0, sLb[buf], k, lane);
+      if (wave == 1) dma_rows_f32(rd, i0, sDb[buf], k, lane);
+      if (wave == 2) dma_rows_f32(ral, i0, sAb[buf], k, lane);
+      if (wave == 3) dma_rows_f32(rbe, i0, sBb[buf], k, lane);
     }
   };
-  if (ntiles > 0) prefetch(istart);
+  if (ntiles > 0) stage(istart, 0);
   for (int t = 0; t < ntiles; ++t) {
     const int i0 = istart + t * BM;
-    __syncthreads();
-    sq.store_rows(Qs, tid);
-    sq.store_tr(Qt, tid);
-    sdo.store_rows(dOs, tid);
-    sdo.store_tr(dOt, tid);
-    sa.store_rows(As, tid);
-    sa.store_tr(At, tid);
-    if (tid < BM) {
-      sL[tid] = lrow;
-      sD[tid] = drow;
-      sA[tid] = arow;
-      sB[tid] = brow;
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) prefetch(i0 + BM);
+    const int cur = t & 1;
+    wait_dma();
+    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
+    if (t + 1 < ntiles) stage(i0 + BM, cur ^ 1);
+    const T* Qs = Qb[cur];
+    const T* dOs = dOb[cur];
+    const T* As = Ab[cur];
+    const float* sL = sLb[cur];
+    const float* sD = sDb[cur];
+    const float* sA = sAb[cur];
+    const float* sB = sBb[cur];
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
-      // all waves compute all sub-blocks: rows before a key (causal) are masked
-      // below, rows past N have LSE = +inf and so P = 0
+      // all waves compute all sub-blocks: rows before a key (causal) and rows
+      // past N are masked below
       f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -298,18 +284,23 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
       }
       float shs[16], dss[16], hs[16], ps[16];
 #pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rbase = ib + 8 * (v >> 2) + 4 * h;
+        ps[v] = __builtin_amdgcn_exp2f(s[v] * sl2 - sL[rbase + (v & 3)] * LOG2E);
+      }
+      if ((CAUSAL && is <= kw) || is + 32 > N) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
+          ps[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : ps[v];
+        }
+      }
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rbase = ib + 8 * q + 4 * h;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[rbase]);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[rbase]);
         const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[rbase]);
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sB[rbase]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ps[4 * q + r] = __builtin_amdgcn_exp2f(s[4 * q + r] * sl2 - l4[r]);
-        if (CAUSAL && is <= kw) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ps[4 * q + r] = (my_j > i0 + rbase + r) ? 0.f : ps[4 * q + r];
-        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * q + r;
@@ -326,12 +317,12 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
       for (int tt = 0; tt < 2; ++tt) {
         const Frag<T> shf = pack8<T>(shs + 8 * tt), dsf = pack8<T>(dss + 8 * tt);
         const Frag<T> hf = pack8<T>(hs + 8 * tt);
-        mma(gk0, ld_tr(Qt, TS, 0, it + tt, lane), shf);
-        mma(gk1, ld_tr(Qt, TS, 32, it + tt, lane), shf);
-        mma(gk0, ld_tr(At, TS, 0, it + tt, lane), dsf);
-        mma(gk1, ld_tr(At, TS, 32, it + tt, lane), dsf);
-        mma(gv0, ld_tr(dOt, TS, 0, it + tt, lane), hf);
-        mma(gv1, ld_tr(dOt, TS, 32, it + tt, lane), hf);
+        mma(gk0, ld_tr(Qs, 0, it + tt, lane), shf);
+        mma(gk1, ld_tr(Qs, 32, it + tt, lane), shf);
+        mma(gk0, ld_tr(As, 0, it + tt, lane), dsf);
+        mma(gk1, ld_tr(As, 32, it + tt, lane), dsf);
+        mma(gv0, ld_tr(dOs, 0, it + tt, lane), hf);
+        mma(gv1, ld_tr(dOs, 32, it + tt, lane), hf);
       }
     }
   }

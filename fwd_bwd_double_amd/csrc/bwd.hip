@@ -16,8 +16,11 @@
 // exactly those bf16 values and R(P) K, and finishes
 //   dQ = scale * (R(dS) K - r_i R(P) K);
 // the column pass reads r and adds the key correction
-//   dK = scale * (R(dS)^T Q - R(P)^T R(r o Q))
+//   dK = scale * (R(dS)^T Q - Q^T R(r o P))
 // as a separate fp32-accumulated product; the projected dS is never re-rounded.
+// Tiles reach LDS by buffer -> LDS DMA into two alternating buffers, and the
+// operands contracted over the sequence index are read with the transposing
+// LDS read, so every tile is stored once, row-major.
 // Each output block is written once by one workgroup; there are no atomics.
 #include "launch.hpp"
 #include "tile.hpp"
@@ -30,18 +33,15 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, int N, int BH, int nblk,
     float scale) {
-  constexpr int RS = Lay<T>::RS;
-  using Stage = TileStage<T, BN>;
-  constexpr int TS = Stage::TS;
-  __shared__ __attribute__((aligned(16))) T Ks[BN * RS];
-  __shared__ __attribute__((aligned(16))) T Vs[BN * RS];
-  __shared__ __attribute__((aligned(16))) T Kt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T Kb[2][BN * HD];
+  __shared__ __attribute__((aligned(16))) T Vb[2][BN * HD];
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
   const size_t soff = (size_t)wk.head * N;
-  const T* Kh = K + hoff;
-  const T* Vh = V + hoff;
+  const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
+  const auto rk = make_rsrc(K + hoff, hbytes);
+  const auto rv = make_rsrc(V + hoff, hbytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q0 = wk.blk * BLK;
   const int qw = q0 + wave * WROWS;
@@ -66,20 +66,19 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
 
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
-  Stage sk, sv;
-  sk.load(Kh, N, 0, tid);
-  sv.load(Vh, N, 0, tid);
+  dma_tile<T, BN, NT / 64>(rk, 0, Kb[0], wave, lane);
+  dma_tile<T, BN, NT / 64>(rv, 0, Vb[0], wave, lane);
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BN;
-    __syncthreads();
-    sk.store_rows(Ks, tid);
-    sk.store_tr(Kt, tid);
-    sv.store_rows(Vs, tid);
-    __syncthreads();
+    const int cur = t & 1;
+    wait_dma();
+    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
     if (t + 1 < ntiles) {
-      sk.load(Kh, N, j0 + BN, tid);
-      sv.load(Vh, N, j0 + BN, tid);
+      dma_tile<T, BN, NT / 64>(rk, j0 + BN, Kb[cur ^ 1], wave, lane);
+      dma_tile<T, BN, NT / 64>(rv, j0 + BN, Vb[cur ^ 1], wave, lane);
     }
+    const T* Ks = Kb[cur];
+    const T* Vs = Vb[cur];
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
@@ -103,8 +102,8 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
       for (int v = 0; v < 16; ++v) ds[v] = p[v] * (dpacc[v] - Di);
       const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
       const int jt = jb / 16;
-      const Frag<T> a00 = ld_tr(Kt, TS, 0, jt, lane), a01 = ld_tr(Kt, TS, 0, jt + 1, lane);
-      const Frag<T> a10 = ld_tr(Kt, TS, 32, jt, lane), a11 = ld_tr(Kt, TS, 32, jt + 1, lane);
+      const Frag<T> a00 = ld_tr(Ks, 0, jt, lane), a01 = ld_tr(Ks, 0, jt + 1, lane);
+      const Frag<T> a10 = ld_tr(Ks, 32, jt, lane), a11 = ld_tr(Ks, 32, jt + 1, lane);
       mma(dq0, a00, df0);
       mma(dq0, a01, df1);
       mma(dq1, a10, df0);
@@ -148,22 +147,22 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
     const float* __restrict__ LSE, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
     float scale) {
-  constexpr int RS = Lay<T>::RS;
-  using Stage = TileStage<T, BM>;
-  constexpr int TS = Stage::TS;
-  __shared__ __attribute__((aligned(16))) T Qs[BM * RS];
-  __shared__ __attribute__((aligned(16))) T Qt[HD * TS];
-  __shared__ __attribute__((aligned(16))) T dOs[BM * RS];
-  __shared__ __attribute__((aligned(16))) T dOt[HD * TS];
-  __shared__ __attribute__((aligned(16))) T rQt[GPROJ ? HD * TS : 8];
-  __shared__ __attribute__((aligned(16))) float sL[BM];
-  __shared__ __attribute__((aligned(16))) float sD[BM];
+  static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
+  __shared__ __attribute__((aligned(16))) T Qb[2][BM * HD];
+  __shared__ __attribute__((aligned(16))) T dOb[2][BM * HD];
+  __shared__ __attribute__((aligned(16))) float sLb[2][BM];   // LSE, D, r of the tile's rows
+  __shared__ __attribute__((aligned(16))) float sDb[2][BM];
+  __shared__ __attribute__((aligned(16))) float sRb[2][GPROJ ? BM : 4];
 
   const Work wk = col_work(BH);
   const size_t hoff = (size_t)wk.head * N * HD;
   const size_t soff = (size_t)wk.head * N;
-  const T* Qh = Q + hoff;
-  const T* dOh = dO + hoff;
+  const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
+  const auto rq = make_rsrc(Q + hoff, hbytes);
+  const auto rdo = make_rsrc(dO + hoff, hbytes);
+  const auto rl = make_rsrc(LSE + soff, (uint32_t)N * 4u);
+  const auto rd = make_rsrc(Dws + soff, (uint32_t)N * 4u);
+  const auto rr = make_rsrc(Rws + soff, (uint32_t)N * 4u);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = wk.blk * BLK;
   const int kw = k0 + wave * WROWS;
@@ -178,71 +177,62 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
 
   const int istart = CAUSAL ? k0 : 0;   // k0 is a multiple of BM
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
-  Stage sq, sdo;
-  float lrow = INFINITY, drow = 0.f;
-  auto prefetch = [&](int i0) {
-    sq.load(Qh, N, i0, tid);
-    sdo.load(dOh, N, i0, tid);
-    if (tid < BM) {
-      const int row = i0 + tid;
-      lrow = row < N ? LSE[soff + row] * LOG2E : INFINITY;   // padded rows: P = 0
-      drow = row < N ? Dws[soff + row] : 0.f;
+  auto stage = [&](int i0, int buf) {
+    dma_tile<T, BM, NT / 64>(rq, i0, Qb[buf], wave, lane);
+    dma_tile<T, BM, NT / 64>(rdo, i0, dOb[buf], wave, lane);
+#pragma unroll
+    for (int k = 0; k < BM / 64; ++k) {
+      if (wave == 0) dma_rows_f32(rl, i0, sLb[buf], k, lane);
+      if (wave == 1) dma_rows_f32(rd, i0, sDb[buf], k, lane);
+      if (GPROJ && wave == 2) dma_rows_f32(rr, i0, sRb[buf], k, lane);
     }
   };
-  if (ntiles > 0) prefetch(istart);
+  if (ntiles > 0) stage(istart, 0);
   for (int t = 0; t < ntiles; ++t) {
     const int i0 = istart + t * BM;
-    __syncthreads();
-    sq.store_rows(Qs, tid);
-    sq.store_tr(Qt, tid);
-    sdo.store_rows(dOs, tid);
-    sdo.store_tr(dOt, tid);
-    if (tid < BM) {
-      sL[tid] = lrow;
-      sD[tid] = drow;
-    }
-    if constexpr (GPROJ) {
-      // rQt = R(-r_i * Q_i), transposed
-#pragma unroll
-      for (int u = 0; u < Stage::U; ++u) {
-        const int unit = tid + NT * u;
-        const int p = unit % (BM / 2);
-        const int row = i0 + 2 * p;
-        float fac[2] = {row < N ? -Rws[soff + row] : 0.f, row + 1 < N ? -Rws[soff + row + 1] : 0.f};
-        sq.scale_rows(fac, u);
-      }
-      sq.store_tr(rQt, tid);
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) prefetch(i0 + BM);
+    const int cur = t & 1;
+    wait_dma();
+    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
+    if (t + 1 < ntiles) stage(i0 + BM, cur ^ 1);
+    const T* Qs = Qb[cur];
+    const T* dOs = dOb[cur];
+    const float* sL = sLb[cur];
+    const float* sD = sDb[cur];
+    const float* sR = sRb[cur];
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
-      // all waves compute all sub-blocks: rows before a key (causal) are masked
-      // below, rows past N have LSE = +inf and so P = 0
+      // all waves compute all sub-blocks: rows before a key (causal) and rows
+      // past N are masked below
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         mma(sacc, ld_row(Qs, ib, kb, lane), kf[kb]);
         mma(dpacc, ld_row(dOs, ib, kb, lane), vf[kb]);
       }
-      float p[16], ds[16];
+      float p[16], ds[16], rp[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[ib + 8 * q + 4 * h]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[ib + 8 * q + 4 * h]);
+        const int rbase = ib + 8 * q + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[rbase]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[rbase]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = 4 * q + r;
-          p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - l4[r]);
-          ds[v] = dpacc[v] - d4[r];
+        for (int u = 0; u < 4; ++u) {
+          const int v = 4 * q + u;
+          p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - l4[u] * LOG2E);
+          ds[v] = dpacc[v] - d4[u];
+        }
+        if constexpr (GPROJ) {
+          const f32x4 r4 = *reinterpret_cast<const f32x4*>(&sR[rbase]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rp[4 * q + u] = -r4[u];
         }
       }
-      if (CAUSAL && is <= kw) {
+      if ((CAUSAL && is <= kw) || is + 32 > N) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
-          p[v] = (my_j > i) ? 0.f : p[v];
+          p[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : p[v];
         }
       }
 #pragma unroll
@@ -250,19 +240,26 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
       const Frag<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
       const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
       const int it = ib / 16;
-      mma(dv0, ld_tr(dOt, TS, 0, it, lane), pf0);
-      mma(dv0, ld_tr(dOt, TS, 0, it + 1, lane), pf1);
-      mma(dv1, ld_tr(dOt, TS, 32, it, lane), pf0);
-      mma(dv1, ld_tr(dOt, TS, 32, it + 1, lane), pf1);
-      mma(dk0, ld_tr(Qt, TS, 0, it, lane), df0);
-      mma(dk0, ld_tr(Qt, TS, 0, it + 1, lane), df1);
-      mma(dk1, ld_tr(Qt, TS, 32, it, lane), df0);
-      mma(dk1, ld_tr(Qt, TS, 32, it + 1, lane), df1);
+      const Frag<T> q00 = ld_tr(Qs, 0, it, lane), q01 = ld_tr(Qs, 0, it + 1, lane);
+      const Frag<T> q10 = ld_tr(Qs, 32, it, lane), q11 = ld_tr(Qs, 32, it + 1, lane);
+      mma(dv0, ld_tr(dOs, 0, it, lane), pf0);
+      mma(dv0, ld_tr(dOs, 0, it + 1, lane), pf1);
+      mma(dv1, ld_tr(dOs, 32, it, lane), pf0);
+      mma(dv1, ld_tr(dOs, 32, it + 1, lane), pf1);
+      mma(dk0, q00, df0);
+      mma(dk0, q01, df1);
+      mma(dk1, q10, df0);
+      mma(dk1, q11, df1);
       if constexpr (GPROJ) {
-        mma(dk0, ld_tr(rQt, TS, 0, it, lane), pf0);
-        mma(dk0, ld_tr(rQt, TS, 0, it + 1, lane), pf1);
-        mma(dk1, ld_tr(rQt, TS, 32, it, lane), pf0);
-        mma(dk1, ld_tr(rQt, TS, 32, it + 1, lane), pf1);
+        // key correction  - R(P)^T (r o Q)  as  Q^T R(-r o P): a separate
+        // fp32-accumulated product, so the projected dS is never re-rounded
+#pragma unroll
+        for (int v = 0; v < 16; ++v) rp[v] *= p[v];
+        const Frag<T> rf0 = pack8<T>(rp), rf1 = pack8<T>(rp + 8);
+        mma(dk0, q00, rf0);
+        mma(dk0, q01, rf1);
+        mma(dk1, q10, rf0);
+        mma(dk1, q11, rf1);
       }
     }
   }

@@ -14,8 +14,9 @@
 // are never loaded (explainer page, section "Causal masking is where trading
 // gets a discount").
 //
-// Global loads run two tiles ahead of the compute: two register stages
-// alternate, each refilled right after it has been written to LDS.
+// K and V tiles reach LDS by buffer -> LDS DMA into two alternating buffers:
+// the copy of tile t+1 runs while tile t is computed.  V is read along the
+// key index with the transposing LDS read, so both stay row-major.
 //
 // Layout: FWD_WAVES waves per workgroup, FWD_G groups of 32 queries per wave,
 // one query per lane in each group (4 x 1 measured fastest on MI355X: more
@@ -38,16 +39,14 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,
                                                      int nblk, float scale) {
-  constexpr int RS = Lay<T>::RS;
-  using Stage = TileStage<T, BN, FWD_NT>;
-  constexpr int TS = Stage::TS;
-  __shared__ __attribute__((aligned(16))) T Ks[BN * RS];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * TS];
+  __shared__ __attribute__((aligned(16))) T Kb[2][BN * HD];
+  __shared__ __attribute__((aligned(16))) T Vb[2][BN * HD];
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
-  const T* Kh = K + hoff;
-  const T* Vh = V + hoff;
+  const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
+  const auto rk = make_rsrc(K + hoff, hbytes);
+  const auto rv = make_rsrc(V + hoff, hbytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q0 = wk.blk * FWD_BLK;
   const int qw = q0 + wave * FWD_G * WROWS;
@@ -68,20 +67,19 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 
   const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
-
-  // One tile: stage it into LDS from registers, refill those registers with
-  // the tile two steps ahead (so a load has two tiles of compute to land),
-  // then compute.
-  auto tile = [&](int t, Stage& sk, Stage& sv) {
+  dma_tile<T, BN, FWD_WAVES>(rk, 0, Kb[0], wave, lane);
+  dma_tile<T, BN, FWD_WAVES>(rv, 0, Vb[0], wave, lane);
+  for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BN;
-    __syncthreads();
-    sk.store_rows(Ks, tid);
-    sv.store_tr(Vt, tid);
-    __syncthreads();
-    if (t + 2 < ntiles) {
-      sk.load(Kh, N, j0 + 2 * BN, tid);
-      sv.load(Vh, N, j0 + 2 * BN, tid);
+    const int cur = t & 1;
+    wait_dma();
+    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
+    if (t + 1 < ntiles) {
+      dma_tile<T, BN, FWD_WAVES>(rk, j0 + BN, Kb[cur ^ 1], wave, lane);
+      dma_tile<T, BN, FWD_WAVES>(rv, j0 + BN, Vb[cur ^ 1], wave, lane);
     }
+    const T* Ks = Kb[cur];
+    const T* Vs = Vb[cur];
     // Every wave computes every 32-key sub-block of the tile; keys after a
     // row (causal) or past N are masked to -inf.  Identical control flow in
     // all waves keeps the accumulators in fixed registers.
@@ -134,8 +132,8 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
       const int jt = jb / 16;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const Frag<T> v0 = ld_tr(Vt, TS, 0, jt + tt, lane);
-        const Frag<T> v1 = ld_tr(Vt, TS, 32, jt + tt, lane);
+        const Frag<T> v0 = ld_tr(Vs, 0, jt + tt, lane);
+        const Frag<T> v1 = ld_tr(Vs, 32, jt + tt, lane);
 #pragma unroll
         for (int g = 0; g < FWD_G; ++g) {
           mma(o[g][0], v0, pf[g][tt]);
@@ -143,18 +141,6 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
         }
       }
     }
-  };
-
-  Stage sk0, sv0, sk1, sv1;
-  sk0.load(Kh, N, 0, tid);
-  sv0.load(Vh, N, 0, tid);
-  if (ntiles > 1) {
-    sk1.load(Kh, N, BN, tid);
-    sv1.load(Vh, N, BN, tid);
-  }
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, sk0, sv0);
-    if (t + 1 < ntiles) tile(t + 1, sk1, sv1);
   }
 #pragma unroll
   for (int g = 0; g < FWD_G; ++g) {

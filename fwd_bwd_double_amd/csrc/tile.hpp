@@ -14,9 +14,9 @@
 // owns one query (row passes) or one key (column passes) and the other index
 // runs down its registers.  Products that contract over that other index
 // then take the probability tile straight from registers as the B operand;
-// the A operand must be the streamed tile read along its row index, which is
-// why streamed tiles are kept in LDS twice: row-major (for contractions over
-// d) and transposed (for contractions over the sequence).
+// their A operand is the streamed tile read along its sequence index, which
+// the transposing LDS read (ds_read_b64_tr_b16) delivers from the same
+// row-major tile the contractions over d read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,11 +43,6 @@ template <class T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
 template <> struct Frag<float> { f32x8 v; };
 
-template <class T> struct Lay;
-// Row-major LDS tiles: row stride in elements.  The padding keeps the 16-lane
-// groups of an operand read on distinct banks.
-template <> struct Lay<bf16> { static constexpr int RS = HD + 8; static constexpr int TP = 4; };
-template <> struct Lay<float> { static constexpr int RS = HD + 4; static constexpr int TP = 4; };
 
 __device__ __forceinline__ void mma(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
@@ -135,39 +130,114 @@ __device__ __forceinline__ float frag_sum(const Frag<float>& f) {
   return s;
 }
 
-// Operand for a contraction over d, read from a row-major LDS tile:
-// lane -> tile row r0 + (l & 31), slots d = 16*kb + 8*(l >> 5) + s.
+// ---------------------------------------------------------------------------
+// LDS tiles.  A tile holds R consecutive rows (sequence positions) of one
+// head's N x 64 matrix, row-major and unpadded (128 B per row for bf16, 256 B
+// for fp32).  Within a row the 16-byte chunks are XOR-swizzled by a function
+// of the row so that both operand reads below are spread over all banks.
+// Tiles are filled by buffer -> LDS DMA (no register staging): rows at or past
+// N read as zero because the buffer resource covers exactly the head's N rows.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <class T> struct TileFmt {
+  static constexpr int CPR = HD * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  static constexpr int ROWB = CPR * 16;                    // bytes per row
+};
+template <class T> __device__ __forceinline__ int swz(int row) {
+  if constexpr (sizeof(T) == 2) return (row >> 1) & 7;
+  else return row & 15;
+}
+template <class T> __device__ __forceinline__ int chunk_off(int row, int chunk) {
+  return row * TileFmt<T>::ROWB + ((chunk ^ swz<T>(row)) << 4);
+}
+
+// Buffer resource over `bytes` bytes at `base`; loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Issue the DMA of rows [r0, r0 + R) of a head's matrix into `tile`.  The NW
+// waves of the workgroup share the work; each wave instruction moves 64
+// chunks (1 KB).  Completion: s_waitcnt vmcnt(0) in every wave, then a barrier.
+template <class T, int R, int NW>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int r0, T* tile, int wave,
+                                         int lane) {
+  constexpr int CPR = TileFmt<T>::CPR;
+  constexpr int INSTR = R * CPR / 64;
+  static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < INSTR / NW; ++i) {
+    const int k = wave + NW * i;
+    const int L = k * 64 + lane;
+    const int r = L / CPR, cl = L % CPR;
+    const uint32_t voff = (uint32_t)((r0 + r) * CPR + (cl ^ swz<T>(r))) * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((char*)tile + k * 1024), 16, voff, 0,
+                                             0, 0);
+  }
+}
+
+// DMA of `n64` x 64 consecutive fp32 row statistics starting at row r0 (one
+// wave instruction per 64 rows).
+__device__ __forceinline__ void dma_rows_f32(__amdgpu_buffer_rsrc_t rs, int r0, float* dst,
+                                             int k, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 64 * k), 4,
+                                           (uint32_t)(r0 + 64 * k + lane) * 4u, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
+
+// Operand for a contraction over d from a tile: lane -> tile row r0 + (l & 31),
+// slots d = 16*kb + 8*(l >> 5) + s.
 template <class T>
 __device__ __forceinline__ Frag<T> ld_row(const T* tile, int r0, int kb, int lane) {
-  const T* p = tile + (r0 + (lane & 31)) * Lay<T>::RS + kb * 16 + 8 * (lane >> 5);
+  const int r = r0 + (lane & 31);
+  const char* base = reinterpret_cast<const char*>(tile);
   Frag<T> f;
   if constexpr (sizeof(T) == 2) {
-    f.v = *reinterpret_cast<const bf16x8*>(p);
+    f.v = *reinterpret_cast<const bf16x8*>(base + chunk_off<T>(r, 2 * kb + (lane >> 5)));
   } else {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    const int c = 4 * kb + 2 * (lane >> 5);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(base + chunk_off<T>(r, c));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(base + chunk_off<T>(r, c + 1));
     f.v = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
   return f;
 }
 
-// Operand for a contraction over the sequence index, read from a transposed
-// LDS tile Xt[d][j] with row stride ts: lane -> d = d0 + (l & 31); its slots
-// are the sequence positions 16*jt + {4h .. 4h+3, 8+4h .. 8+4h+3} (h = l>>5),
-// which are exactly the positions that registers 8t .. 8t+7 of a 32x32 result
-// hold for the sub-block's 16-row group t (jt = sub-block/16 + t).
+// Operand for a contraction over the sequence index from a tile: lane -> d =
+// d0 + (l & 31); its slots are the sequence positions 16*jt + {4h .. 4h+3,
+// 8+4h .. 8+4h+3} (h = l >> 5) -- exactly the positions registers 8t .. 8t+7
+// of a 32x32 result hold for the sub-block's 16-row group t (jt = sub/16 + t).
+// bf16: two ds_read_b64_tr_b16.  Within each 16-lane group that instruction
+// hands result lane p, slot k, element p%4 of the 8 bytes source lane p/4+4k
+// addressed; so source lane q addresses row (base + q/4) at columns
+// d0 + 16*(group%2) + 4*(q%4) .. +3, and lane l receives four consecutive
+// sequence positions of column d0 + (l & 31).  fp32: eight scalar reads.
+typedef bf16 bf16x4v __attribute__((ext_vector_type(4)));
 template <class T>
-__device__ __forceinline__ Frag<T> ld_tr(const T* tileT, int ts, int d0, int jt, int lane) {
-  const T* p = tileT + (d0 + (lane & 31)) * ts + jt * 16 + 4 * (lane >> 5);
+__device__ __forceinline__ Frag<T> ld_tr(const T* tile, int d0, int jt, int lane) {
+  const char* base = reinterpret_cast<const char*>(tile);
+  const int h = lane >> 5;
   Frag<T> f;
   if constexpr (sizeof(T) == 2) {
-    bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
-    bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 8);
-    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const int q = lane & 15;
+    const int d = d0 + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+    const int ra = 16 * jt + 4 * h + (q >> 2), rb = ra + 8;
+    const int off = (d & 7) * 2;
+    const bf16x4v x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4v*)(base + chunk_off<T>(ra, d >> 3) + off));
+    const bf16x4v y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4v*)(base + chunk_off<T>(rb, d >> 3) + off));
+    f.v = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
   } else {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 8);
-    f.v = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const int d = d0 + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int pos = 16 * jt + 8 * (s >> 2) + 4 * h + (s & 3);
+      f.v[s] = *reinterpret_cast<const float*>(base + chunk_off<T>(pos, d >> 2) + (d & 3) * 4);
+    }
   }
   return f;
 }
@@ -249,88 +319,6 @@ __device__ __forceinline__ void ld_cols(const T* X, int n, int r0, int c0, int l
     }
   }
 }
-
-// Global -> registers -> LDS staging of an R x 64 tile (R rows of one head's
-// matrix starting at row r0; rows >= n are zero).  A unit is a pair of rows
-// (2p, 2p+1) times one 16-byte column chunk c; the thread holds both rows'
-// chunks so that the transposed store can write two sequence positions per
-// 32-bit word (bf16) or 64-bit word (fp32).
-template <class T, int R, int NTH = NT>
-struct TileStage {
-  static constexpr int E = 16 / sizeof(T);          // elements per chunk
-  static constexpr int CPR = HD / E;                 // chunks per row
-  static constexpr int UNITS = (R / 2) * CPR;
-  static constexpr int U = (UNITS + NTH - 1) / NTH;  // units per thread
-  uint4 a[U], b[U];
-
-  __device__ __forceinline__ void load(const T* X, int n, int r0, int tid) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int unit = tid + NTH * u;
-      const int p = unit % (R / 2), c = unit / (R / 2);
-      const int row = r0 + 2 * p;
-      a[u] = make_uint4(0, 0, 0, 0);
-      b[u] = make_uint4(0, 0, 0, 0);
-      if (unit < UNITS) {
-        const T* src = X + (size_t)row * HD + c * E;
-        if (row < n) a[u] = *reinterpret_cast<const uint4*>(src);
-        if (row + 1 < n) b[u] = *reinterpret_cast<const uint4*>(src + HD);
-      }
-    }
-  }
-
-  // Multiply every element of both rows by a per-row factor (rounded back to
-  // the element type).  Used for the GProj key correction term.
-  __device__ __forceinline__ void scale_rows(const float* fac2, int u) {
-    T* pa = reinterpret_cast<T*>(&a[u]);
-    T* pb = reinterpret_cast<T*>(&b[u]);
-#pragma unroll
-    for (int k = 0; k < E; ++k) {
-      pa[k] = (T)((float)pa[k] * fac2[0]);
-      pb[k] = (T)((float)pb[k] * fac2[1]);
-    }
-  }
-
-  __device__ __forceinline__ void store_rows(T* tile, int tid) const {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int unit = tid + NTH * u;
-      if (unit < UNITS) {
-        const int p = unit % (R / 2), c = unit / (R / 2);
-        *reinterpret_cast<uint4*>(tile + (2 * p) * Lay<T>::RS + c * E) = a[u];
-        *reinterpret_cast<uint4*>(tile + (2 * p + 1) * Lay<T>::RS + c * E) = b[u];
-      }
-    }
-  }
-
-  // tileT[d][row] with row stride TS = R + Lay<T>::TP.
-  static constexpr int TS = R + Lay<T>::TP;
-  __device__ __forceinline__ void store_tr(T* tileT, int tid) const {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int unit = tid + NTH * u;
-      if (unit < UNITS) {
-        const int p = unit % (R / 2), c = unit / (R / 2);
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t* wa = reinterpret_cast<const uint32_t*>(&a[u]);
-          const uint32_t* wb = reinterpret_cast<const uint32_t*>(&b[u]);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const uint32_t lo = (k & 1) ? (wa[k >> 1] >> 16) : (wa[k >> 1] & 0xffffu);
-            const uint32_t hi = (k & 1) ? (wb[k >> 1] & 0xffff0000u) : (wb[k >> 1] << 16);
-            *reinterpret_cast<uint32_t*>(tileT + (c * 8 + k) * TS + 2 * p) = lo | hi;
-          }
-        } else {
-          const float* fa = reinterpret_cast<const float*>(&a[u]);
-          const float* fb = reinterpret_cast<const float*>(&b[u]);
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            *reinterpret_cast<f32x2*>(tileT + (c * 4 + k) * TS + 2 * p) = f32x2{fa[k], fb[k]};
-        }
-      }
-    }
-  }
-};
 
 // Work-item order shared by all launches: a 1-D grid of nblk * BH workgroups
 // with the heads varying fastest, so the first wave of workgroups takes the

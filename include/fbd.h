@@ -94,7 +94,7 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
  * longer sum to zero; the residual r_i = sum_j R(dS_ij) of exactly those
  * bf16 values is removed in proportion to the probabilities:
  *   dQ = scale * (R(dS) K - r o (R(P) K)),
- *   dK = scale * (R(dS)^T Q - R(P)^T R(r o Q)).
+ *   dK = scale * (R(dS)^T Q - Q^T R(r o P)).
  * The dQ correction rides in the row pass; the dK correction needs r and is
  * applied in the column pass.  For fp32 inputs R is the identity.
  *

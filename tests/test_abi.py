@@ -61,6 +61,8 @@ def fwd_call(lib, dt=0, B=1, H=1, N=8, d=64, ptrs=(FAKE, FAKE * 2, FAKE * 3), ca
     (dict(ptrs=(FAKE + 8, FAKE * 2, FAKE * 3)), 3),
     (dict(out=(FAKE * 2, FAKE * 5)), 1),           # output aliases an input
     (dict(N=1 << 30), 2),                          # N * 64 beyond 32-bit indexing
+    (dict(N=1 << 25), 2),                          # head bytes beyond 32-bit buffer offsets
+    (dict(dt=1, N=1 << 24), 2),
 ])
 def test_fwd_rejects_bad_arguments_before_launch(lib, kw, status):
     assert fwd_call(lib, **kw) == status
