@@ -47,10 +47,13 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
     float* __restrict__ Bws, int N, int BH, int nblk, float scale) {
-  __shared__ __attribute__((aligned(16))) T Kb[2][BN * HD];
-  __shared__ __attribute__((aligned(16))) T Vb[2][BN * HD];
-  __shared__ __attribute__((aligned(16))) T Bb[2][BN * HD];
-  __shared__ __attribute__((aligned(16))) T Cb[2][BN * HD];
+  // two buffers as separate objects (loop unrolled by two): the copy of the
+  // next tile provably never aliases the reads of the current one
+  struct Buf {
+    T k[BN * HD], v[BN * HD], b[BN * HD], c[BN * HD];
+  };
+  __shared__ __attribute__((aligned(16))) Buf B0;
+  __shared__ __attribute__((aligned(16))) Buf B1;
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
@@ -85,23 +88,21 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
 
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
-  auto stage = [&](int j0, int buf) {
-    dma_tile<T, BN, NT / 64>(rk, j0, Kb[buf], wave, lane);
-    dma_tile<T, BN, NT / 64>(rv, j0, Vb[buf], wave, lane);
-    dma_tile<T, BN, NT / 64>(rb, j0, Bb[buf], wave, lane);
-    dma_tile<T, BN, NT / 64>(rc, j0, Cb[buf], wave, lane);
+  auto stage = [&](int j0, Buf& bf) {
+    dma_tile<T, BN, NT / 64>(rk, j0, bf.k, wave, lane);
+    dma_tile<T, BN, NT / 64>(rv, j0, bf.v, wave, lane);
+    dma_tile<T, BN, NT / 64>(rb, j0, bf.b, wave, lane);
+    dma_tile<T, BN, NT / 64>(rc, j0, bf.c, wave, lane);
   };
-  stage(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, const Buf& cb, Buf& nb) {
     const int j0 = t * BN;
-    const int cur = t & 1;
     wait_dma();
-    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
-    if (t + 1 < ntiles) stage(j0 + BN, cur ^ 1);
-    const T* Ks = Kb[cur];
-    const T* Vs = Vb[cur];
-    const T* Bs = Bb[cur];
-    const T* Cs = Cb[cur];
+    __syncthreads();   // tile t is in cb; every wave is done with nb
+    if (t + 1 < ntiles) stage(j0 + BN, nb);
+    const T* Ks = cb.k;
+    const T* Vs = cb.v;
+    const T* Bs = cb.b;
+    const T* Cs = cb.c;
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
@@ -171,6 +172,11 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
         }
       }
     }
+  };
+  stage(0, B0);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, B0, B1);
+    if (t + 1 < ntiles) tile(t + 1, B1, B0);
   }
   alpha = half_sum(alpha);
   bsum = half_sum(bsum);
@@ -205,13 +211,14 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
     const float* __restrict__ Aws, const float* __restrict__ Bws, T* __restrict__ gK,
     T* __restrict__ gV, int N, int BH, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
-  __shared__ __attribute__((aligned(16))) T Qb[2][BM * HD];
-  __shared__ __attribute__((aligned(16))) T dOb[2][BM * HD];
-  __shared__ __attribute__((aligned(16))) T Ab[2][BM * HD];
-  __shared__ __attribute__((aligned(16))) float sLb[2][BM];   // LSE, D, alpha, beta of the rows
-  __shared__ __attribute__((aligned(16))) float sDb[2][BM];
-  __shared__ __attribute__((aligned(16))) float sAb[2][BM];
-  __shared__ __attribute__((aligned(16))) float sBb[2][BM];
+  // two buffers as separate objects (loop unrolled by two); each holds the
+  // Q, dO, g_dQ tiles and the LSE, D, alpha, beta of the tile's rows
+  struct Buf {
+    T q[BM * HD], dO[BM * HD], a[BM * HD];
+    float lse[BM], D[BM], al[BM], be[BM];
+  };
+  __shared__ __attribute__((aligned(16))) Buf B0;
+  __shared__ __attribute__((aligned(16))) Buf B1;
 
   const Work wk = col_work(BH);
   const size_t hoff = (size_t)wk.head * N * HD;
@@ -240,32 +247,30 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
 
   const int istart = CAUSAL ? k0 : 0;
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
-  auto stage = [&](int i0, int buf) {
-    dma_tile<T, BM, NT / 64>(rq, i0, Qb[buf], wave, lane);
-    dma_tile<T, BM, NT / 64>(rdo, i0, dOb[buf], wave, lane);
-    dma_tile<T, BM, NT / 64>(ra, i0, Ab[buf], wave, lane);
+  auto stage = [&](int i0, Buf& b) {
+    dma_tile<T, BM, NT / 64>(rq, i0, b.q, wave, lane);
+    dma_tile<T, BM, NT / 64>(rdo, i0, b.dO, wave, lane);
+    dma_tile<T, BM, NT / 64>(ra, i0, b.a, wave, lane);
 #pragma unroll
     for (int k = 0; k < BM / 64; ++k) {
-      if (wave == 0) dma_rows_f32(rl, i0, sLb[buf], k, lane);
-      if (wave == 1) dma_rows_f32(rd, i0, sDb[buf], k, lane);
-      if (wave == 2) dma_rows_f32(ral, i0, sAb[buf], k, lane);
-      if (wave == 3) dma_rows_f32(rbe, i0, sBb[buf], k, lane);
+      if (wave == 0) dma_rows_f32(rl, i0, b.lse, k, lane);
+      if (wave == 1) dma_rows_f32(rd, i0, b.D, k, lane);
+      if (wave == 2) dma_rows_f32(ral, i0, b.al, k, lane);
+      if (wave == 3) dma_rows_f32(rbe, i0, b.be, k, lane);
     }
   };
-  if (ntiles > 0) stage(istart, 0);
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, const Buf& cb, Buf& nb) {
     const int i0 = istart + t * BM;
-    const int cur = t & 1;
     wait_dma();
-    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
-    if (t + 1 < ntiles) stage(i0 + BM, cur ^ 1);
-    const T* Qs = Qb[cur];
-    const T* dOs = dOb[cur];
-    const T* As = Ab[cur];
-    const float* sL = sLb[cur];
-    const float* sD = sDb[cur];
-    const float* sA = sAb[cur];
-    const float* sB = sBb[cur];
+    __syncthreads();   // tile t is in cb; every wave is done with nb
+    if (t + 1 < ntiles) stage(i0 + BM, nb);
+    const T* Qs = cb.q;
+    const T* dOs = cb.dO;
+    const T* As = cb.a;
+    const float* sL = cb.lse;
+    const float* sD = cb.D;
+    const float* sA = cb.al;
+    const float* sB = cb.be;
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
@@ -325,6 +330,11 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
         mma(gv1, ld_tr(dOs, 32, it + tt, lane), hf);
       }
     }
+  };
+  if (ntiles > 0) stage(istart, B0);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, B0, B1);
+    if (t + 1 < ntiles) tile(t + 1, B1, B0);
   }
   float out[16];
 #pragma unroll

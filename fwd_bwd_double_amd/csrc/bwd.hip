@@ -33,8 +33,12 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, int N, int BH, int nblk,
     float scale) {
-  __shared__ __attribute__((aligned(16))) T Kb[2][BN * HD];
-  __shared__ __attribute__((aligned(16))) T Vb[2][BN * HD];
+  // two buffers as separate objects (loop unrolled by two): the copy of the
+  // next tile provably never aliases the reads of the current one
+  __shared__ __attribute__((aligned(16))) T K0[BN * HD];
+  __shared__ __attribute__((aligned(16))) T V0[BN * HD];
+  __shared__ __attribute__((aligned(16))) T K1[BN * HD];
+  __shared__ __attribute__((aligned(16))) T V1[BN * HD];
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
@@ -66,19 +70,14 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
 
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
-  dma_tile<T, BN, NT / 64>(rk, 0, Kb[0], wave, lane);
-  dma_tile<T, BN, NT / 64>(rv, 0, Vb[0], wave, lane);
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
     const int j0 = t * BN;
-    const int cur = t & 1;
     wait_dma();
-    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
+    __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
     if (t + 1 < ntiles) {
-      dma_tile<T, BN, NT / 64>(rk, j0 + BN, Kb[cur ^ 1], wave, lane);
-      dma_tile<T, BN, NT / 64>(rv, j0 + BN, Vb[cur ^ 1], wave, lane);
+      dma_tile<T, BN, NT / 64>(rk, j0 + BN, Kn, wave, lane);
+      dma_tile<T, BN, NT / 64>(rv, j0 + BN, Vn, wave, lane);
     }
-    const T* Ks = Kb[cur];
-    const T* Vs = Vb[cur];
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
@@ -117,6 +116,12 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
         mma(pk1, a11, pf1);
       }
     }
+  };
+  dma_tile<T, BN, NT / 64>(rk, 0, K0, wave, lane);
+  dma_tile<T, BN, NT / 64>(rv, 0, V0, wave, lane);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, K0, V0, K1, V1);
+    if (t + 1 < ntiles) tile(t + 1, K1, V1, K0, V0);
   }
   float out[16];
   if constexpr (GPROJ) {
@@ -148,11 +153,15 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
     float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
-  __shared__ __attribute__((aligned(16))) T Qb[2][BM * HD];
-  __shared__ __attribute__((aligned(16))) T dOb[2][BM * HD];
-  __shared__ __attribute__((aligned(16))) float sLb[2][BM];   // LSE, D, r of the tile's rows
-  __shared__ __attribute__((aligned(16))) float sDb[2][BM];
-  __shared__ __attribute__((aligned(16))) float sRb[2][GPROJ ? BM : 4];
+  // two buffers as separate objects (loop unrolled by two); each holds the
+  // Q and dO tiles and the LSE, D (, r) of the tile's rows
+  struct Buf {
+    T q[BM * HD];
+    T dO[BM * HD];
+    float lse[BM], D[BM], r[GPROJ ? BM : 4];
+  };
+  __shared__ __attribute__((aligned(16))) Buf B0;
+  __shared__ __attribute__((aligned(16))) Buf B1;
 
   const Work wk = col_work(BH);
   const size_t hoff = (size_t)wk.head * N * HD;
@@ -177,28 +186,26 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
 
   const int istart = CAUSAL ? k0 : 0;   // k0 is a multiple of BM
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
-  auto stage = [&](int i0, int buf) {
-    dma_tile<T, BM, NT / 64>(rq, i0, Qb[buf], wave, lane);
-    dma_tile<T, BM, NT / 64>(rdo, i0, dOb[buf], wave, lane);
+  auto stage = [&](int i0, Buf& b) {
+    dma_tile<T, BM, NT / 64>(rq, i0, b.q, wave, lane);
+    dma_tile<T, BM, NT / 64>(rdo, i0, b.dO, wave, lane);
 #pragma unroll
     for (int k = 0; k < BM / 64; ++k) {
-      if (wave == 0) dma_rows_f32(rl, i0, sLb[buf], k, lane);
-      if (wave == 1) dma_rows_f32(rd, i0, sDb[buf], k, lane);
-      if (GPROJ && wave == 2) dma_rows_f32(rr, i0, sRb[buf], k, lane);
+      if (wave == 0) dma_rows_f32(rl, i0, b.lse, k, lane);
+      if (wave == 1) dma_rows_f32(rd, i0, b.D, k, lane);
+      if (GPROJ && wave == 2) dma_rows_f32(rr, i0, b.r, k, lane);
     }
   };
-  if (ntiles > 0) stage(istart, 0);
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, const Buf& cb, Buf& nb) {
     const int i0 = istart + t * BM;
-    const int cur = t & 1;
     wait_dma();
-    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
-    if (t + 1 < ntiles) stage(i0 + BM, cur ^ 1);
-    const T* Qs = Qb[cur];
-    const T* dOs = dOb[cur];
-    const float* sL = sLb[cur];
-    const float* sD = sDb[cur];
-    const float* sR = sRb[cur];
+    __syncthreads();   // tile t is in cb; every wave is done with nb
+    if (t + 1 < ntiles) stage(i0 + BM, nb);
+    const T* Qs = cb.q;
+    const T* dOs = cb.dO;
+    const float* sL = cb.lse;
+    const float* sD = cb.D;
+    const float* sR = cb.r;
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
@@ -262,6 +269,11 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
         mma(dk1, q11, rf1);
       }
     }
+  };
+  if (ntiles > 0) stage(istart, B0);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, B0, B1);
+    if (t + 1 < ntiles) tile(t + 1, B1, B0);
   }
   float out[16];
 #pragma unroll

@@ -39,8 +39,13 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,
                                                      int nblk, float scale) {
-  __shared__ __attribute__((aligned(16))) T Kb[2][BN * HD];
-  __shared__ __attribute__((aligned(16))) T Vb[2][BN * HD];
+  // two buffers as separate objects, used in a loop unrolled by two, so the
+  // compiler can tell the copy of the next tile never aliases the reads of
+  // the current one (and places no wait between them)
+  __shared__ __attribute__((aligned(16))) T K0[BN * HD];
+  __shared__ __attribute__((aligned(16))) T V0[BN * HD];
+  __shared__ __attribute__((aligned(16))) T K1[BN * HD];
+  __shared__ __attribute__((aligned(16))) T V1[BN * HD];
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
@@ -67,19 +72,14 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 
   const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
-  dma_tile<T, BN, FWD_WAVES>(rk, 0, Kb[0], wave, lane);
-  dma_tile<T, BN, FWD_WAVES>(rv, 0, Vb[0], wave, lane);
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
     const int j0 = t * BN;
-    const int cur = t & 1;
     wait_dma();
-    __syncthreads();   // tile t is in buffer cur; every wave is done with buffer cur ^ 1
+    __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
     if (t + 1 < ntiles) {
-      dma_tile<T, BN, FWD_WAVES>(rk, j0 + BN, Kb[cur ^ 1], wave, lane);
-      dma_tile<T, BN, FWD_WAVES>(rv, j0 + BN, Vb[cur ^ 1], wave, lane);
+      dma_tile<T, BN, FWD_WAVES>(rk, j0 + BN, Kn, wave, lane);
+      dma_tile<T, BN, FWD_WAVES>(rv, j0 + BN, Vn, wave, lane);
     }
-    const T* Ks = Kb[cur];
-    const T* Vs = Vb[cur];
     // Every wave computes every 32-key sub-block of the tile; keys after a
     // row (causal) or past N are masked to -inf.  Identical control flow in
     // all waves keeps the accumulators in fixed registers.
@@ -141,6 +141,12 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
         }
       }
     }
+  };
+  dma_tile<T, BN, FWD_WAVES>(rk, 0, K0, wave, lane);
+  dma_tile<T, BN, FWD_WAVES>(rv, 0, V0, wave, lane);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, K0, V0, K1, V1);
+    if (t + 1 < ntiles) tile(t + 1, K1, V1, K0, V0);
   }
 #pragma unroll
   for (int g = 0; g < FWD_G; ++g) {
