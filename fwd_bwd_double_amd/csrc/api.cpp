@@ -104,12 +104,12 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return (size_t)2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return (size_t)3 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
 size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return (size_t)3 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return (size_t)5 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
 attn_status attn_fwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
@@ -138,9 +138,11 @@ attn_status attn_bwd_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
   st = check_ptrs({{Q, t}, {K, t}, {V, t}, {O, t}, {LSE, s}, {dO, t}},
                   {{dQ, t}, {dK, t}, {dV, t}, {ws, need}});
   if (st != ATTN_OK) return st;
+  const size_t bhn = (size_t)B * H * N;
   float* Dws = static_cast<float*>(ws);
-  float* Rws = Dws + (size_t)B * H * N;
-  return finish(fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, (int)(B * H),
+  float* Rws = Dws + bhn;
+  float* Lws = Rws + bhn;
+  return finish(fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, (int)(B * H),
                                 (int)N, causal ? 1 : 0, scale, gproj ? 1 : 0, passes,
                                 (hipStream_t)stream));
 }
@@ -168,11 +170,14 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                    {g_dV, t}},
                   {{g_Q, t}, {g_K, t}, {g_V, t}, {g_dO, t}, {ws, need}});
   if (st != ATTN_OK) return st;
+  const size_t bhn = (size_t)B * H * N;
   float* Dws = static_cast<float*>(ws);
-  float* Aws = Dws + (size_t)B * H * N;
-  float* Bws = Aws + (size_t)B * H * N;
+  float* Aws = Dws + bhn;
+  float* Bws = Aws + bhn;
+  float* Lws = Bws + bhn;
+  float* Kws = Lws + bhn;
   return finish(fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, g_Q, g_K, g_V,
-                                g_dO, Dws, Aws, Bws, (int)(B * H), (int)N, causal ? 1 : 0, scale,
+                                g_dO, Dws, Aws, Bws, Lws, Kws, (int)(B * H), (int)N, causal ? 1 : 0, scale,
                                 passes, (hipStream_t)stream));
 }
 

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
-    float* __restrict__ Bws, int N, int BH, int nblk, float scale) {
+    float* __restrict__ Bws, float* __restrict__ Lws, float* __restrict__ Kws, int N, int BH,
+    int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   struct Buf {
@@ -200,22 +201,24 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
     Dws[soff + my_i] = Di;
     Aws[soff + my_i] = alpha;
     Bws[soff + my_i] = beta;
+    Lws[soff + my_i] = -lse2;
+    Kws[soff + my_i] = alpha * Di + beta;
   }
 }
 
 template <class T, int BM, bool CAUSAL>
 __global__ __launch_bounds__(NT) void bob_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const float* __restrict__ LSE, const T* __restrict__ dO, const T* __restrict__ A,
+    const float* __restrict__ Lws, const T* __restrict__ dO, const T* __restrict__ A,
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
-    const float* __restrict__ Aws, const float* __restrict__ Bws, T* __restrict__ gK,
+    const float* __restrict__ Aws, const float* __restrict__ Kws, T* __restrict__ gK,
     T* __restrict__ gV, int N, int BH, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
-  // Q, dO, g_dQ tiles and the LSE, D, alpha, beta of the tile's rows
+  // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, kappa of the tile's rows
   struct Buf {
     T q[BM * HD], dO[BM * HD], a[BM * HD];
-    float lse[BM], D[BM], al[BM], be[BM];
+    float nl[BM], D[BM], al[BM], ka[BM];
   };
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
@@ -227,10 +230,10 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
   const auto rq = make_rsrc(Q + hoff, hbytes);
   const auto rdo = make_rsrc(dO + hoff, hbytes);
   const auto ra = make_rsrc(A + hoff, hbytes);
-  const auto rl = make_rsrc(LSE + soff, (uint32_t)N * 4u);
+  const auto rl = make_rsrc(Lws + soff, (uint32_t)N * 4u);
   const auto rd = make_rsrc(Dws + soff, (uint32_t)N * 4u);
   const auto ral = make_rsrc(Aws + soff, (uint32_t)N * 4u);
-  const auto rbe = make_rsrc(Bws + soff, (uint32_t)N * 4u);
+  const auto rka = make_rsrc(Kws + soff, (uint32_t)N * 4u);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = wk.blk * BLK;
   const int kw = k0 + wave * WROWS;
@@ -253,10 +256,10 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
     dma_tile<T, BM, NT / 64>(ra, i0, b.a, wave, lane);
 #pragma unroll
     for (int k = 0; k < BM / 64; ++k) {
-      if (wave == 0) dma_rows_f32(rl, i0, b.lse, k, lane);
+      if (wave == 0) dma_rows_f32(rl, i0, b.nl, k, lane);
       if (wave == 1) dma_rows_f32(rd, i0, b.D, k, lane);
       if (wave == 2) dma_rows_f32(ral, i0, b.al, k, lane);
-      if (wave == 3) dma_rows_f32(rbe, i0, b.be, k, lane);
+      if (wave == 3) dma_rows_f32(rka, i0, b.ka, k, lane);
     }
   };
   auto tile = [&](int t, const Buf& cb, Buf& nb) {
@@ -267,10 +270,10 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
     const T* Qs = cb.q;
     const T* dOs = cb.dO;
     const T* As = cb.a;
-    const float* sL = cb.lse;
+    const float* sL = cb.nl;
     const float* sD = cb.D;
     const float* sA = cb.al;
-    const float* sB = cb.be;
+    const float* sK = cb.ka;
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
@@ -287,11 +290,15 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
         mma(dp, dr, vf[kb]);
         mma(u, dr, cf[kb]);
       }
+      // Sh = P o (W (dP - D) + U - alpha dP - beta) = P o (h (dP - D) + U - kappa)
+      // with h = W - alpha and kappa = alpha D + beta (per row, from the row pass)
       float shs[16], dss[16], hs[16], ps[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rbase = ib + 8 * (v >> 2) + 4 * h;
-        ps[v] = __builtin_amdgcn_exp2f(s[v] * sl2 - sL[rbase + (v & 3)] * LOG2E);
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[ib + 8 * q + 4 * h]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ps[4 * q + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * q + r], sl2, l4[r]));
       }
       if ((CAUSAL && is <= kw) || is + 32 > N) {
 #pragma unroll
@@ -305,16 +312,16 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
         const int rbase = ib + 8 * q + 4 * h;
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[rbase]);
         const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[rbase]);
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sB[rbase]);
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sK[rbase]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * q + r;
           const float pv = ps[v];
-          const float W = scale * w[v];
+          const float hv = __builtin_fmaf(scale, w[v], -a4[r]);
           const float dpd = dp[v] - d4[r];
           dss[v] = pv * dpd;
-          hs[v] = pv * (W - a4[r]);
-          shs[v] = pv * (W * dpd + u[v] - a4[r] * dp[v] - b4[r]);
+          hs[v] = pv * hv;
+          shs[v] = pv * (__builtin_fmaf(hv, dpd, u[v]) - k4[r]);
         }
       }
       const int it = ib / 16;
@@ -355,8 +362,8 @@ template <class T, bool CAUSAL>
 static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
-                               float* Dws, float* Aws, float* Bws, int BH, int N, float scale,
-                               int passes, hipStream_t st) {
+                               float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
+                               int N, float scale, int passes, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
@@ -364,25 +371,25 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
     hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
                        (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws,
-                       N, BH, nblk, scale);
+                       Lws, Kws, N, BH, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
   hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
-                     (const T*)Q, (const T*)K, (const T*)V, LSE, (const T*)dO, (const T*)gdQ,
-                     (const T*)gdK, (const T*)gdV, (const float*)Dws, (const float*)Aws,
-                     (const float*)Bws, (T*)gK, (T*)gV, N, BH, scale);
+                     (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO,
+                     (const T*)gdQ, (const T*)gdK, (const T*)gdV, (const float*)Dws,
+                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
-                      float* Aws, float* Bws, int BH, int N, int causal, float scale, int passes,
-                      hipStream_t st) {
-#define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, BH, N, \
-                     scale, passes, st
+                      float* Aws, float* Bws, float* Lws, float* Kws, int BH, int N, int causal,
+                      float scale, int passes, hipStream_t st) {
+#define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, Lws, Kws, \
+                     BH, N, scale, passes, st
   if (dt == 0)
     return causal ? launch_bob_t<bf16, true>(FBD_BOB_ARGS) : launch_bob_t<bf16, false>(FBD_BOB_ARGS);
   return causal ? launch_bob_t<float, true>(FBD_BOB_ARGS) : launch_bob_t<float, false>(FBD_BOB_ARGS);

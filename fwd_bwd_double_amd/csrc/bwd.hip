@@ -31,8 +31,8 @@ template <class T, int BN, bool GPROJ, bool CAUSAL>
 __global__ __launch_bounds__(NT) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
-    T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, int N, int BH, int nblk,
-    float scale) {
+    T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, float* __restrict__ Lws,
+    int N, int BH, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   __shared__ __attribute__((aligned(16))) T K0[BN * HD];
@@ -142,6 +142,7 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
   }
   if (h == 0 && my_i < N) {
     Dws[soff + my_i] = Di;
+    Lws[soff + my_i] = -lse2;
     if constexpr (GPROJ) Rws[soff + my_i] = r;
   }
 }
@@ -149,16 +150,16 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
 template <class T, int BM, bool GPROJ, bool CAUSAL>
 __global__ __launch_bounds__(NT) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const float* __restrict__ LSE, const T* __restrict__ dO, const float* __restrict__ Dws,
+    const float* __restrict__ Lws, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
     float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
-  // Q and dO tiles and the LSE, D (, r) of the tile's rows
+  // Q and dO tiles and the -LSE*log2(e), D (, r) of the tile's rows
   struct Buf {
     T q[BM * HD];
     T dO[BM * HD];
-    float lse[BM], D[BM], r[GPROJ ? BM : 4];
+    float nl[BM], D[BM], r[GPROJ ? BM : 4];   // -LSE*log2(e), D, r
   };
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
   const auto rq = make_rsrc(Q + hoff, hbytes);
   const auto rdo = make_rsrc(dO + hoff, hbytes);
-  const auto rl = make_rsrc(LSE + soff, (uint32_t)N * 4u);
+  const auto rl = make_rsrc(Lws + soff, (uint32_t)N * 4u);
   const auto rd = make_rsrc(Dws + soff, (uint32_t)N * 4u);
   const auto rr = make_rsrc(Rws + soff, (uint32_t)N * 4u);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
     dma_tile<T, BM, NT / 64>(rdo, i0, b.dO, wave, lane);
 #pragma unroll
     for (int k = 0; k < BM / 64; ++k) {
-      if (wave == 0) dma_rows_f32(rl, i0, b.lse, k, lane);
+      if (wave == 0) dma_rows_f32(rl, i0, b.nl, k, lane);
       if (wave == 1) dma_rows_f32(rd, i0, b.D, k, lane);
       if (GPROJ && wave == 2) dma_rows_f32(rr, i0, b.r, k, lane);
     }
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
     if (t + 1 < ntiles) stage(i0 + BM, nb);
     const T* Qs = cb.q;
     const T* dOs = cb.dO;
-    const float* sL = cb.lse;
+    const float* sL = cb.nl;
     const float* sD = cb.D;
     const float* sR = cb.r;
 #pragma unroll
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int v = 4 * q + u;
-          p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - l4[u] * LOG2E);
+          p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], sl2, l4[u]));
           ds[v] = dpacc[v] - d4[u];
         }
         if constexpr (GPROJ) {
@@ -293,21 +294,21 @@ __global__ __launch_bounds__(NT) void bwd_col_kernel(
 template <class T, bool GPROJ, bool CAUSAL>
 static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
-                               float* Dws, float* Rws, int BH, int N, float scale, int passes,
-                               hipStream_t st) {
+                               float* Dws, float* Rws, float* Lws, int BH, int N, float scale,
+                               int passes, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
     hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
-                       (T*)dQ, Dws, Rws, N, BH, nblk, scale);
+                       (T*)dQ, Dws, Rws, Lws, N, BH, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
   hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
-                     (const T*)Q, (const T*)K, (const T*)V, LSE, (const T*)dO, (const float*)Dws,
+                     (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO, (const float*)Dws,
                      (const float*)Rws, (T*)dK, (T*)dV, N, BH, scale);
   return hipGetLastError();
 }
@@ -315,31 +316,25 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
 template <class T, bool GPROJ>
 static hipError_t launch_bwd_c(int causal, const void* Q, const void* K, const void* V,
                                const void* O, const float* LSE, const void* dO, void* dQ,
-                               void* dK, void* dV, float* Dws, float* Rws, int BH, int N,
-                               float scale, int passes, hipStream_t st) {
+                               void* dK, void* dV, float* Dws, float* Rws, float* Lws, int BH,
+                               int N, float scale, int passes, hipStream_t st) {
   if (causal)
-    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, scale,
-                                        passes, st);
-  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N, scale,
-                                       passes, st);
+    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
+  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
 }
 
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
-                      float* Rws, int BH, int N, int causal, float scale, int gproj, int passes,
-                      hipStream_t st) {
+                      float* Rws, float* Lws, int BH, int N, int causal, float scale, int gproj,
+                      int passes, hipStream_t st) {
   if (dt == 0) {
     if (gproj)
-      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
-                                      scale, passes, st);
-    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
-                                     scale, passes, st);
+      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
+    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
   }
   if (gproj)
-    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
-                                     scale, passes, st);
-  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, BH, N,
-                                    scale, passes, st);
+    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
+  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
 }
 
 }  // namespace fbd

@@ -36,15 +36,18 @@ namespace fbd {
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
                       int BH, int N, int causal, float scale, hipStream_t st);
 
+// Backward workspace: D, r, and -LSE*log2(e) per row (written by the row pass,
+// read by the column pass).
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
-                      float* Rws, int BH, int N, int causal, float scale, int gproj, int passes,
-                      hipStream_t st);
+                      float* Rws, float* Lws, int BH, int N, int causal, float scale, int gproj,
+                      int passes, hipStream_t st);
 
+// BoB workspace: D, alpha, beta, -LSE*log2(e) and kappa = alpha*D + beta per row.
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
-                      float* Aws, float* Bws, int BH, int N, int causal, float scale, int passes,
-                      hipStream_t st);
+                      float* Aws, float* Bws, float* Lws, float* Kws, int BH, int N, int causal,
+                      float scale, int passes, hipStream_t st);
 
 }  // namespace fbd

@@ -78,8 +78,9 @@ attn_status attn_fwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
                      int causal, float scale,
                      void* O, float* LSE, void* stream);
 
-/* Workspace of attn_bwd in bytes: D then r, each B*H*N fp32 (D at offset 0,
- * r at offset B*H*N floats).  r is written only when gproj != 0. */
+/* Workspace of attn_bwd in bytes: three fp32 arrays of B*H*N rows, in order
+ * D = rowsum(dO o O), r (written only when gproj != 0) and -LSE*log2(e), all
+ * written by the row pass for the column pass. */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
 /*
@@ -108,8 +109,9 @@ attn_status attn_bwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
                      void* dQ, void* dK, void* dV,
                      void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace of attn_bob in bytes: D, alpha, beta, each B*H*N fp32, in that
- * order. */
+/* Workspace of attn_bob in bytes: five fp32 arrays of B*H*N rows, in order
+ * D, alpha, beta, -LSE*log2(e) and kappa = alpha*D + beta, all written by the
+ * row pass for the column pass. */
 size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
 /*
@@ -129,7 +131,7 @@ size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N);
  *
  * O and LSE must be the outputs of attn_fwd with the same causal and scale.
  * ws must hold attn_bob_workspace_bytes(B, H, N) bytes; after the call it
- * holds D, alpha and beta.
+ * holds D, alpha and beta (then two derived row arrays).
  */
 attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
                      const void* Q, const void* K, const void* V, const void* O,

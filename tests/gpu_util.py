@@ -73,7 +73,7 @@ def run_all(w, g, gproj=False, ops=("fwd", "bwd", "bob")):
         wsn = to_f64(wsb)
         out["D"] = wsn[:n].reshape(w.B, w.H, w.N)
         out["alpha"] = wsn[n:2 * n].reshape(w.B, w.H, w.N)
-        out["beta"] = wsn[2 * n:].reshape(w.B, w.H, w.N)
+        out["beta"] = wsn[2 * n:3 * n].reshape(w.B, w.H, w.N)
     return out
 
 

@@ -34,8 +34,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_workspace_sizes(lib):
-    assert fbd.bwd_workspace_bytes(2, 3, 5) == 2 * 2 * 3 * 5 * 4
-    assert fbd.bob_workspace_bytes(2, 3, 5) == 3 * 2 * 3 * 5 * 4
+    assert fbd.bwd_workspace_bytes(2, 3, 5) == 3 * 2 * 3 * 5 * 4
+    assert fbd.bob_workspace_bytes(2, 3, 5) == 5 * 2 * 3 * 5 * 4
     assert fbd.bwd_workspace_bytes(0, 3, 5) == 0
 
 
