@@ -5,14 +5,17 @@
 // and "The online softmax recurrence": a workgroup owns 128 query rows, streams
 // 64-key tiles of K and V through LDS, and keeps per row a running raw-score
 // max m, a running sum l and an fp32 output accumulator, rescaling both by
-// exp(scale*(m_old - m_new)) whenever the max grows (a wave skips the rescale
-// when none of its rows' max moved).  The division by l happens once, after
-// the last tile.  The exponent is formed as (S - m) * scale: subtracting the
-// max before scaling makes the largest weight exactly 1 (GProj page, rit.work
-// flashattention-bf16-gradient-gproj, section "Why the error shows up at the
-// end of training").  Key tiles entirely in the future of the workgroup's rows
-// are never loaded (explainer page, section "Causal masking is where trading
-// gets a discount").
+// exp(scale*(m_old - m_new)) when the max grows (once per tile; a wave skips
+// the rescale when none of its rows' max moved).  The division by l happens
+// once, after the last tile.  The exponent is formed as (S - m) * scale:
+// subtracting the max before scaling makes the largest weight exactly 1 (GProj
+// page, rit.work flashattention-bf16-gradient-gproj, section "Why the error
+// shows up at the end of training", on fusing the scale and the max into one
+// operation).  The subtraction of the running max costs no VALU work: the
+// score MFMAs start from -m in their accumulator.  Only when a row's max grows
+// inside a tile is the growth subtracted explicitly.  Key tiles entirely in
+// the future of the workgroup's rows are never loaded (explainer page, section
+// "Causal masking is where trading gets a discount").
 //
 // K and V tiles reach LDS by buffer -> LDS DMA into two alternating buffers:
 // the copy of tile t+1 runs while tile t is computed.  V is read along the
@@ -58,20 +61,28 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
   const int h = lane >> 5;
   const float sl2 = scale * LOG2E;
 
+  // Per query group: running max m (raw score units), running sum l and the
+  // output accumulator o.  The score products of a tile start from -m in the
+  // MFMA accumulator (negm), so they arrive as x = S - m: the max is
+  // subtracted without a VALU op.  The max, and with it the rescale of o and
+  // l, is updated once per key tile.
   Frag<T> qf[FWD_G][4];
   float m[FWD_G], l[FWD_G];
-  f32x16 o[FWD_G][2];
+  f32x16 o[FWD_G][2], negm[FWD_G];
 #pragma unroll
   for (int g = 0; g < FWD_G; ++g) {
     ld_frags(Q + hoff, N, qw + g * WROWS, lane, qf[g]);
-    m[g] = -INFINITY;
+    m[g] = 0.f;
     l[g] = 0.f;
     o[g][0] = zero16();
     o[g][1] = zero16();
+    negm[g] = zero16();
   }
 
   const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
+  constexpr int NS = BN / 32;   // 32-key sub-blocks per tile
+
   auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
     const int j0 = t * BN;
     wait_dma();
@@ -83,63 +94,92 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
     // Every wave computes every 32-key sub-block of the tile; keys after a
     // row (causal) or past N are masked to -inf.  Identical control flow in
     // all waves keeps the accumulators in fixed registers.
+    f32x16 x[NS][FWD_G];
 #pragma unroll
-    for (int jb = 0; jb < BN; jb += 32) {
-      const int js = j0 + jb;
+    for (int sb = 0; sb < NS; ++sb) {
       Frag<T> kr[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) kr[kb] = ld_row(Ks, jb, kb, lane);
-      Frag<T> pf[FWD_G][2];
+      for (int kb = 0; kb < 4; ++kb) kr[kb] = ld_row(Ks, sb * 32, kb, lane);
 #pragma unroll
       for (int g = 0; g < FWD_G; ++g) {
-        const int qg = qw + g * WROWS;
-        const int my_i = qg + (lane & 31);
-        f32x16 sacc = zero16();
+        x[sb][g] = negm[g];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(sacc, kr[kb], qf[g][kb]);
-        float s[16];
+        for (int kb = 0; kb < 4; ++kb) mma(x[sb][g], kr[kb], qf[g][kb]);
+      }
+    }
+    // Online-softmax update per query group.  On the first tile there is no
+    // history: m becomes the exact tile max.  Later, base = max(x) > 0 where
+    // a row's max grew; subtracting base before scaling gives the new row
+    // max weight exactly 1.
+    float base[FWD_G];
+    bool sub[FWD_G];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = sacc[v];
+    for (int g = 0; g < FWD_G; ++g) {
+      const int qg = qw + g * WROWS;
+      const int my_i = qg + (lane & 31);
+#pragma unroll
+      for (int sb = 0; sb < NS; ++sb) {
+        const int js = j0 + sb * 32;
         if (CAUSAL ? (js + 31 > qg) : (js + 32 > N)) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-            s[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? -INFINITY : s[v];
+            x[sb][g][v] = (CAUSAL ? (j > my_i) : (j >= N)) ? -INFINITY : x[sb][g][v];
           }
         }
-        float mt = s[0];
+      }
+      float xm = x[0][g][0];
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s[v]);
-        mt = half_max(mt);
-        // key 0 is visible to every row, so m is finite after the first
-        // sub-block and a fully masked sub-block leaves it unchanged
-        const float mn = fmaxf(m[g], mt);
-        if (__any(mn > m[g])) {
-          const float alpha = __builtin_amdgcn_exp2f((m[g] - mn) * sl2);
-          l[g] *= alpha;
-          o[g][0] *= alpha;
-          o[g][1] *= alpha;
-          m[g] = mn;
-        }
+      for (int sb = 0; sb < NS; ++sb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xm = fmaxf(xm, x[sb][g][v]);
+      xm = half_max(xm);   // key 0 is visible to every row: finite on the first tile
+      base[g] = 0.f;
+      if (t == 0) {
+        m[g] = xm;
+        base[g] = xm;
+      } else if (__any(xm > 0.f)) {
+        base[g] = fmaxf(xm, 0.f);
+        const float alpha = __builtin_amdgcn_exp2f(-base[g] * sl2);
+        l[g] *= alpha;
+        o[g][0] *= alpha;
+        o[g][1] *= alpha;
+        m[g] += base[g];
+      }
+      sub[g] = __any(base[g] != 0.f);
+    }
+#pragma unroll
+    for (int sb = 0; sb < NS; ++sb) {
+      Frag<T> pf[FWD_G][2];
+#pragma unroll
+      for (int g = 0; g < FWD_G; ++g) {
         float p[16];
+        if (sub[g]) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f((s[v] - mn) * sl2);
+          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f((x[sb][g][v] - base[g]) * sl2);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[sb][g][v] * sl2);
+        }
         pf[g][0] = pack8<T>(p);
         pf[g][1] = pack8<T>(p + 8);
         l[g] = frag_acc_sum(pf[g][0], l[g]);
         l[g] = frag_acc_sum(pf[g][1], l[g]);
       }
-      const int jt = jb / 16;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const Frag<T> v0 = ld_tr(Vs, 0, jt + tt, lane);
-        const Frag<T> v1 = ld_tr(Vs, 32, jt + tt, lane);
+        const Frag<T> v0 = ld_tr(Vs, 0, 2 * sb + tt, lane);
+        const Frag<T> v1 = ld_tr(Vs, 32, 2 * sb + tt, lane);
 #pragma unroll
         for (int g = 0; g < FWD_G; ++g) {
           mma(o[g][0], v0, pf[g][tt]);
           mma(o[g][1], v1, pf[g][tt]);
         }
       }
+    }
+#pragma unroll
+    for (int g = 0; g < FWD_G; ++g) {
+      negm[g] = zero16() - m[g];
     }
   };
   dma_tile<T, BN, FWD_WAVES>(rk, 0, K0, wave, lane);
