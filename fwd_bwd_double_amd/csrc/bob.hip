@@ -41,7 +41,7 @@
 namespace fbd {
 
 template <class T, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NT) void bob_row_kernel(
+__global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(NT) void bob_row_kernel(
 }
 
 template <class T, int BM, bool CAUSAL>
-__global__ __launch_bounds__(NT) void bob_col_kernel(
+__global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const T* __restrict__ A,
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
@@ -278,63 +278,93 @@ __global__ __launch_bounds__(NT) void bob_col_kernel(
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
       // all waves compute all sub-blocks: rows before a key (causal) and rows
-      // past N are masked below
-      f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
+      // past N are masked below.  The four score-type products are formed
+      // one after another, each consumed as soon as it is complete, to keep
+      // few of them live at once.
+      const int it = ib / 16;
+      float ps[16];
+      {
+        f32x16 s = zero16();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const Frag<T> qr = ld_row(Qs, ib, kb, lane);
-        mma(s, qr, kf[kb]);
-        mma(w, qr, bf[kb]);
-        mma(w, ld_row(As, ib, kb, lane), kf[kb]);
-        const Frag<T> dr = ld_row(dOs, ib, kb, lane);
-        mma(dp, dr, vf[kb]);
-        mma(u, dr, cf[kb]);
-      }
-      // Sh = P o (W (dP - D) + U - alpha dP - beta) = P o (h (dP - D) + U - kappa)
-      // with h = W - alpha and kappa = alpha D + beta (per row, from the row pass)
-      float shs[16], dss[16], hs[16], ps[16];
+        for (int kb = 0; kb < 4; ++kb) mma(s, ld_row(Qs, ib, kb, lane), kf[kb]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[ib + 8 * q + 4 * h]);
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[ib + 8 * q + 4 * h]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          ps[4 * q + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * q + r], sl2, l4[r]));
-      }
-      if ((CAUSAL && is <= kw) || is + 32 > N) {
+          for (int r = 0; r < 4; ++r)
+            ps[4 * q + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * q + r], sl2, l4[r]));
+        }
+        if ((CAUSAL && is <= kw) || is + 32 > N) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
-          ps[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : ps[v];
+          for (int v = 0; v < 16; ++v) {
+            const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
+            ps[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : ps[v];
+          }
         }
       }
+      // dS = P o (dP - D): gK += dS^T A
+      f32x16 dpd = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(dpd, ld_row(dOs, ib, kb, lane), vf[kb]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int rbase = ib + 8 * q + 4 * h;
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[rbase]);
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[rbase]);
-        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sK[rbase]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[ib + 8 * q + 4 * h]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dpd[4 * q + r] -= d4[r];
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ds[e] = ps[8 * tt + e] * dpd[8 * tt + e];
+        const Frag<T> dsf = pack8<T>(ds);
+        mma(gk0, ld_tr(As, 0, it + tt, lane), dsf);
+        mma(gk1, ld_tr(As, 32, it + tt, lane), dsf);
+      }
+      // h = scale W - alpha with W = Q Bk^T + A K^T:  gV += (P o h)^T dO
+      f32x16 hv = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        mma(hv, ld_row(Qs, ib, kb, lane), bf[kb]);
+        mma(hv, ld_row(As, ib, kb, lane), kf[kb]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sA[ib + 8 * q + 4 * h]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[4 * q + r] = __builtin_fmaf(scale, hv[4 * q + r], -a4[r]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float hs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hs[e] = ps[8 * tt + e] * hv[8 * tt + e];
+        const Frag<T> hf = pack8<T>(hs);
+        mma(gv0, ld_tr(dOs, 0, it + tt, lane), hf);
+        mma(gv1, ld_tr(dOs, 32, it + tt, lane), hf);
+      }
+      // Sh = P o (W (dP - D) + U - alpha dP - beta) = P o (h (dP - D) + U - kappa)
+      // with U = dO C^T and kappa = alpha D + beta per row:  gK += Sh^T Q
+      f32x16 u = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(u, ld_row(dOs, ib, kb, lane), cf[kb]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sK[ib + 8 * q + 4 * h]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * q + r;
-          const float pv = ps[v];
-          const float hv = __builtin_fmaf(scale, w[v], -a4[r]);
-          const float dpd = dp[v] - d4[r];
-          dss[v] = pv * dpd;
-          hs[v] = pv * hv;
-          shs[v] = pv * (__builtin_fmaf(hv, dpd, u[v]) - k4[r]);
+          u[v] = ps[v] * (__builtin_fmaf(hv[v], dpd[v], u[v]) - k4[r]);
         }
       }
-      const int it = ib / 16;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const Frag<T> shf = pack8<T>(shs + 8 * tt), dsf = pack8<T>(dss + 8 * tt);
-        const Frag<T> hf = pack8<T>(hs + 8 * tt);
+        float sh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sh[e] = u[8 * tt + e];
+        const Frag<T> shf = pack8<T>(sh);
         mma(gk0, ld_tr(Qs, 0, it + tt, lane), shf);
         mma(gk1, ld_tr(Qs, 32, it + tt, lane), shf);
-        mma(gk0, ld_tr(As, 0, it + tt, lane), dsf);
-        mma(gk1, ld_tr(As, 32, it + tt, lane), dsf);
-        mma(gv0, ld_tr(dOs, 0, it + tt, lane), hf);
-        mma(gv1, ld_tr(dOs, 32, it + tt, lane), hf);
       }
     }
   };

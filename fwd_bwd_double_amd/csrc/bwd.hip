@@ -28,7 +28,7 @@
 namespace fbd {
 
 template <class T, int BN, bool GPROJ, bool CAUSAL>
-__global__ __launch_bounds__(NT) void bwd_row_kernel(
+__global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, float* __restrict__ Lws,
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NT) void bwd_row_kernel(
 }
 
 template <class T, int BM, bool GPROJ, bool CAUSAL>
-__global__ __launch_bounds__(NT) void bwd_col_kernel(
+__global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH,

@@ -28,6 +28,20 @@
 #ifndef FBD_BOB_BM
 #define FBD_BOB_BM 64
 #endif
+// Minimum resident workgroups per CU the compiler must allow for (register
+// budget); a 256-thread workgroup at 1 per CU may use 512 registers per lane.
+#ifndef FBD_BWD_ROW_OCC
+#define FBD_BWD_ROW_OCC 1
+#endif
+#ifndef FBD_BWD_COL_OCC
+#define FBD_BWD_COL_OCC 1
+#endif
+#ifndef FBD_BOB_ROW_OCC
+#define FBD_BOB_ROW_OCC 1
+#endif
+#ifndef FBD_BOB_COL_OCC
+#define FBD_BOB_COL_OCC 2
+#endif
 
 namespace fbd {
 
