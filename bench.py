@@ -14,6 +14,10 @@ the bf16 dense MFMA peak; `cpu_baseline` is the fp64 oracle timed on a bounded
 sample of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+
+`--sweep` instead times each operation separately over sequence lengths
+1k .. 256k (H=12, d=64, B = max(1, 16384/N), causal, GProj on) and the other
+workload shapes, printing one JSON line per case.
 """
 from __future__ import annotations
 
@@ -45,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=48,
                    help="heads of the workload the oracle baseline runs on")
+    p.add_argument("--sweep", action="store_true",
+                   help="time fwd, bwd and BoB separately over N = 1k .. 256k and the other "
+                        "workload shapes (one JSON line per case) instead of the step")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a plain copy "
                         "kernel of known size, to calibrate memory counters)")
@@ -53,6 +60,8 @@ def parse():
 
 def main():
     args = parse()
+    if args.sweep and args.gpus == 1:
+        return sweep()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(heads would shard across GPUs with no exchange); run with --gpus 1",
@@ -162,6 +171,78 @@ def main():
         "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9,
     }
     print(json.dumps(line), flush=True)
+
+
+def sweep():
+    """Each operation timed on its own (HIP events on the launch stream; median
+    of the repetitions after a warm-up) for N = 1k .. 256k with H = 12, d = 64,
+    B = max(1, 16384 / N), and for the gpt2s-layer (B8 H12 N1024) and
+    large-key (B1 H12 N16384) shapes.  Inputs: seeded device-side normal draws
+    with the BoB workload's distributions (Q, K, V, dO ~ 0.5 N(0,1),
+    cotangents ~ N(0,1)), rounded to bf16."""
+    import numpy as np
+    import torch
+
+    import fwd_bwd_double_amd as fbd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cases = [("gpt2s-layer", 8, 12, 1024), ("large-key", 1, 12, 16384)]
+    cases += [(f"sweep-N{n}", max(1, 16384 // n), 12, n)
+              for n in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
+    d = 64
+    for name, B, H, N in cases:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 + N)
+
+        def draw(std):
+            return (torch.randn((B, H, N, d), generator=gen, device=dev) * std).to(torch.bfloat16)
+
+        q, k, v, do = draw(0.5), draw(0.5), draw(0.5), draw(0.5)
+        a, bk, c = draw(1.0), draw(1.0), draw(1.0)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), device=dev)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4))
+        ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
+        ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
+        sc = 1.0 / 8.0
+        ops = {
+            "fwd": lambda: fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse),
+            "bwd": lambda: fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=sc, gproj=True,
+                                        workspace=ws_b, outs=(dq, dk, dv)),
+            "bob": lambda: fbd.attn_bob(q, k, v, o, lse, do, a, bk, c, causal=True, scale=sc,
+                                        workspace=ws_bb, outs=(gq, gk, gv, gdo)),
+        }
+        pairs = B * H * N * (N + 1) / 2
+        exec_units = {"fwd": UNITS["fwd"], "bwd": UNITS["bwd_row"] + UNITS["bwd_col"],
+                      "bob": UNITS["bob_row"] + UNITS["bob_col"]}
+        reps = 3 if N >= 65536 else 10
+        res = {}
+        for op, fn in ops.items():
+            fn()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            for r in range(reps):
+                ev[r].record()
+                fn()
+            ev[reps].record()
+            torch.cuda.synchronize()
+            ms = float(np.median([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]))
+            res[op] = {"ms": ms,
+                       "conv_tflops": CONV[op] * d * pairs / (ms * 1e-3) / 1e12,
+                       "executed_frac_mfma_peak":
+                           exec_units[op] * 2 * d * pairs / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        line = {"case": name, "B": B, "H": H, "N": N, "d": d, "causal": True, "gproj": True,
+                "dtype": "bf16", "data": "synthetic", "ops": res,
+                "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9}
+        print(json.dumps(line), flush=True)
+        print(f"[sweep] {name:14s} " + "  ".join(
+            f"{op} {r['ms']:9.3f} ms {r['conv_tflops']:7.1f} TF {100 * r['executed_frac_mfma_peak']:5.1f}%"
+            for op, r in res.items()), file=sys.stderr, flush=True)
+        del q, k, v, do, a, bk, c, o, lse, dq, dk, dv, gq, gk, gv, gdo, ws_b, ws_bb
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
 
 
 # Which sources define each kernel: a stored counter figure is used only while

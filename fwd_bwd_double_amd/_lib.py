@@ -140,7 +140,8 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
              gproj: bool = False, workspace: Optional[torch.Tensor] = None, outs=None,
              passes: int = 3) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV of <dO, O>.  `workspace` (fp32, >= bwd_workspace_bytes) holds
-    D then r afterwards when given.  passes: 1 row pass, 2 column pass, 3 both."""
+    the row states D, r and -LSE*log2(e), each B*H*N floats, afterwards.
+    passes: 1 row pass, 2 column pass, 3 both."""
     lib = load()
     for n, t in (("k", k), ("v", v), ("o", o), ("do", do)):
         _check(n, t, q)
@@ -167,7 +168,8 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
              scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, outs=None,
              passes: int = 3) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
-    cotangents (g_dq, g_dk, g_dv).  `workspace` holds D, alpha, beta after."""
+    cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
+    beta, -LSE*log2(e) and kappa = alpha*D + beta afterwards."""
     lib = load()
     for n, t in (("k", k), ("v", v), ("o", o), ("do", do), ("g_dq", g_dq), ("g_dk", g_dk),
                  ("g_dv", g_dv)):
