@@ -2,13 +2,14 @@
 backward with optional GProj, and backward-over-backward, as hand-written HIP
 kernels behind the C ABI of libfbd.so (include/fbd.h).
 
-    from fwd_bwd_double_amd import attn_fwd, attn_bwd, attn_bob
+    from fwd_bwd_double_amd import attn_fwd, attn_bwd, attn_bob, attn_hvp
 
 The functions take torch tensors shaped (B, H, N, 64) in bf16 or fp32 on the
 GPU; torch provides device memory and the stream, the kernels do the work.
 """
-from ._lib import (AttnError, attn_bob, attn_bwd, attn_fwd,  # noqa: F401
-                   bob_workspace_bytes, bwd_workspace_bytes, load, LIB_PATH)
+from ._lib import (AttnError, attn_bob, attn_bwd, attn_fwd, attn_hvp,  # noqa: F401
+                   bob_workspace_bytes, bwd_workspace_bytes, hvp_workspace_bytes, load,
+                   LIB_PATH)
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bob", "bwd_workspace_bytes",
-           "bob_workspace_bytes", "AttnError", "load", "LIB_PATH"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_bob", "attn_hvp", "bwd_workspace_bytes",
+           "bob_workspace_bytes", "hvp_workspace_bytes", "AttnError", "load", "LIB_PATH"]

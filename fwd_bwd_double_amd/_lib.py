@@ -66,6 +66,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_passes.restype = i32
     lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
     lib.attn_bob_passes.restype = i32
+    lib.attn_hvp_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_hvp_workspace_bytes.restype = sz
+    lib.attn_hvp.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32,
+                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_hvp.restype = i32
     lib.attn_status_str.argtypes = [i32]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -114,6 +119,10 @@ def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
 
 def bob_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(load().attn_bob_workspace_bytes(B, H, N))
+
+
+def hvp_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load().attn_hvp_workspace_bytes(B, H, N))
 
 
 def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
@@ -192,3 +201,39 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
                       ws_bytes, _stream(q.device))
     _raise("attn_bob", st)
     return gq, gk, gv, gdo
+
+
+def attn_hvp(q, k, v, do, v_q, v_k, v_v, causal: bool = True, scale: Optional[float] = None,
+             gproj: bool = False, grad: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Hessian-vector product of Phi(q, k, v) = <do, O(q, k, v)> (do fixed) with
+    v = (v_q, v_k, v_v), in one library call (forward, optional backward, BoB).
+    Returns a dict with O, LSE, Hv_q, Hv_k, Hv_v, Hv_do (the derivative of
+    <v, grad Phi> with respect to do) and, when `grad`, dQ, dK, dV."""
+    lib = load()
+    for n, t in (("k", k), ("v", v), ("do", do), ("v_q", v_q), ("v_k", v_k), ("v_v", v_v)):
+        _check(n, t, q)
+    _check("q", q, q)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    hq, hk, hv, hdo = (torch.empty_like(q) for _ in range(4))
+    dq = dk = dv = None
+    if grad:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    need = lib.attn_hvp_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    ptr = (lambda t: None if t is None else t.data_ptr())
+    st = lib.attn_hvp(_dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                      v_q.data_ptr(), v_k.data_ptr(), v_v.data_ptr(), 1 if causal else 0,
+                      _scale(q, scale), 1 if gproj else 0, o.data_ptr(), lse.data_ptr(), ptr(dq),
+                      ptr(dk), ptr(dv), hq.data_ptr(), hk.data_ptr(), hv.data_ptr(),
+                      hdo.data_ptr(), workspace.data_ptr(), ws_bytes, _stream(q.device))
+    _raise("attn_hvp", st)
+    out = {"O": o, "LSE": lse, "Hv_q": hq, "Hv_k": hk, "Hv_v": hv, "Hv_do": hdo}
+    if grad:
+        out.update(dQ=dq, dK=dk, dV=dv)
+    return out

@@ -190,4 +190,44 @@ attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
                          g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
+size_t attn_hvp_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  // the BoB row states; the backward's three arrays fit in the same space
+  return attn_bob_workspace_bytes(B, H, N);
+}
+
+attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
+                     const void* K, const void* V, const void* dO, const void* v_Q,
+                     const void* v_K, const void* v_V, int causal, float scale, int gproj,
+                     void* O, float* LSE, void* dQ, void* dK, void* dV, void* Hv_Q, void* Hv_K,
+                     void* Hv_V, void* Hv_dO, void* ws, size_t ws_bytes, void* stream) {
+  attn_status st = check_shape(dt, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  const int ngrad = (dQ != nullptr) + (dK != nullptr) + (dV != nullptr);
+  if (ngrad != 0 && ngrad != 3) return ATTN_EINVAL;
+  const size_t need = attn_hvp_workspace_bytes(B, H, N);
+  if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
+  std::vector<Arg> outs = {{O, t}, {LSE, s}, {Hv_Q, t}, {Hv_K, t}, {Hv_V, t}, {Hv_dO, t},
+                           {ws, need}};
+  if (ngrad == 3) {
+    outs.push_back({dQ, t});
+    outs.push_back({dK, t});
+    outs.push_back({dV, t});
+  }
+  st = check_ptrs({{Q, t}, {K, t}, {V, t}, {dO, t}, {v_Q, t}, {v_K, t}, {v_V, t}}, outs);
+  if (st != ATTN_OK) return st;
+  const int bh = (int)(B * H), n = (int)N, c = causal ? 1 : 0;
+  const hipStream_t hs = (hipStream_t)stream;
+  const size_t bhn = (size_t)B * H * N;
+  float* w0 = static_cast<float*>(ws);
+  hipError_t e = fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, n, c, scale, hs);
+  if (e == hipSuccess && ngrad == 3)
+    e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, w0, w0 + bhn, w0 + 2 * bhn, bh,
+                        n, c, scale, gproj ? 1 : 0, 3, hs);
+  if (e == hipSuccess)
+    e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, w0,
+                        w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, n, c, scale, 3, hs);
+  return finish(e);
+}
+
 }  // extern "C"

@@ -167,6 +167,37 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             void* g_Q, void* g_K, void* g_V, void* g_dO,
                             void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Hessian-vector product of one attention layer, the product that
+ * second-order training consumes (FlashBoB page, section "Why go backward
+ * through an already computed gradient": Hessian-vector products for methods
+ * such as Sophia need the backward pass differentiated once more).  For
+ *   Phi(Q, K, V) = <dO, O(Q, K, V)>  with dO held fixed,
+ * the gradient is (dQ, dK, dV) (attn_bwd), so the Hessian applied to
+ * v = (v_Q, v_K, v_V) is the vector-Jacobian product of that gradient map
+ * with cotangents v: attn_bob with (g_dQ, g_dK, g_dV) = (v_Q, v_K, v_V).
+ * One call runs
+ *   attn_fwd                 -> O, LSE
+ *   attn_bwd (if dQ != NULL) -> dQ, dK, dV   (GProj when gproj != 0)
+ *   attn_bob                 -> Hv_Q, Hv_K, Hv_V = H v, and Hv_dO = the
+ *      derivative of <v, (dQ, dK, dV)> with respect to dO, the term a
+ *      network-level product adds through dO's own dependence on the inputs.
+ * dQ, dK and dV are all NULL (gradient not computed) or all set.  Every
+ * output is overwritten.  ws must hold attn_hvp_workspace_bytes(B, H, N)
+ * bytes; afterwards it holds the BoB row states as after attn_bob.  Shapes,
+ * layouts, ownership and errors as for attn_bob (the v_* are read-only
+ * inputs); a partial set of gradient pointers is ATTN_EINVAL.
+ */
+size_t attn_hvp_workspace_bytes(int64_t B, int64_t H, int64_t N);
+
+attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
+                     const void* Q, const void* K, const void* V, const void* dO,
+                     const void* v_Q, const void* v_K, const void* v_V,
+                     int causal, float scale, int gproj,
+                     void* O, float* LSE, void* dQ, void* dK, void* dV,
+                     void* Hv_Q, void* Hv_K, void* Hv_V, void* Hv_dO,
+                     void* ws, size_t ws_bytes, void* stream);
+
 /* Text of a status code (static storage). */
 const char* attn_status_str(attn_status s);
 

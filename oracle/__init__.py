@@ -7,11 +7,11 @@ package.  It shares no code with the HIP library and never imports it; the HIP
 path never imports this package.
 
 Modules:
-  attention   dense definitions (fwd, bwd, bob, rows, last_columns, gproj_project)
+  attention   dense definitions (fwd, bwd, bob, hvp, rows, last_columns, gproj_project)
   online      the tiled online-softmax forward recurrence, as a model
   rounding    bf16 round-to-nearest-even and a rounding model of the bf16
               backward with and without GProj
 """
-from .attention import (probs, fwd, bwd, bob, rows, last_columns,  # noqa: F401
+from .attention import (probs, fwd, bwd, bob, hvp, rows, last_columns,  # noqa: F401
                         gproj_project, max_prob)
 from .online import online_fwd  # noqa: F401

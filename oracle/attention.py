@@ -33,7 +33,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["probs", "fwd", "bwd", "bob", "rows", "last_columns", "gproj_project",
+__all__ = ["probs", "fwd", "bwd", "bob", "hvp", "rows", "last_columns", "gproj_project",
            "max_prob"]
 
 
@@ -220,6 +220,20 @@ def bob(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, heads=None,
     O, LSE, D, alpha, beta, gQ, gK, gV, gdO (and dQ, dK, dV if with_bwd)."""
     return _run(Q, K, V, dO, gdQ, gdK, gdV, causal=causal, scale=scale,
                 want_bwd=with_bwd, want_bob=True, heads=heads, chunk=chunk)
+
+
+def hvp(Q, K, V, dO, vQ, vK, vV, causal=True, scale=None, heads=None, chunk=1024):
+    """Hessian of Phi(Q, K, V) = <dO, O(Q, K, V)>, dO held fixed, applied to
+    v = (vQ, vK, vV) (FlashBoB page, section "Why go backward through an
+    already computed gradient": the Hessian-vector products second-order
+    methods consume).  The gradient of Phi is (dQ, dK, dV) of ``bwd``, so H v
+    is the vector-Jacobian product of (Q, K, V) -> (dQ, dK, dV) with
+    cotangents v: the Q, K, V parts of ``bob`` with (gdQ, gdK, gdV) = v.  The
+    dO part (HvdO) is the mixed derivative of <v, grad Phi> in dO.  Returns a
+    dict with O, LSE, HvQ, HvK, HvV, HvdO."""
+    r = bob(Q, K, V, dO, vQ, vK, vV, causal=causal, scale=scale, heads=heads, chunk=chunk)
+    return {"O": r["O"], "LSE": r["LSE"], "HvQ": r["gQ"], "HvK": r["gK"], "HvV": r["gV"],
+            "HvdO": r["gdO"]}
 
 
 def rows(Q, K, V, dO=None, gdQ=None, gdK=None, gdV=None, row_idx=None,

@@ -81,3 +81,20 @@ def test_bwd_and_bob_reject_small_workspace(lib):
     st = lib.attn_bob(0, 1, 1, 8, 64, *p[:6], p[6], p[7], p[8], 1, 0.125, p[9], p[10], p[11],
                       FAKE * 20, FAKE * 30, need - 1, None)
     assert st == 4
+
+
+def hvp_call(lib, grad=(FAKE * 11, FAKE * 12, FAKE * 13), ws_bytes=None, **kw):
+    p = [FAKE * (i + 1) for i in range(9)]   # Q K V dO vQ vK vV O LSE
+    out = [FAKE * (20 + i) for i in range(4)]
+    need = fbd.hvp_workspace_bytes(1, 1, 8)
+    return lib.attn_hvp(kw.get("dt", 0), 1, 1, 8, kw.get("d", 64), *p[:7], 1, 0.125, 0, p[7],
+                        p[8], *grad, *out, FAKE * 40, need if ws_bytes is None else ws_bytes,
+                        None)
+
+
+def test_hvp_rejects_bad_arguments_before_launch(lib):
+    assert fbd.hvp_workspace_bytes(2, 3, 5) == fbd.bob_workspace_bytes(2, 3, 5)
+    assert hvp_call(lib, d=32) == 2
+    assert hvp_call(lib, grad=(FAKE * 11, None, FAKE * 13)) == 1     # partial gradient set
+    assert hvp_call(lib, ws_bytes=fbd.hvp_workspace_bytes(1, 1, 8) - 4) == 4
+    assert hvp_call(lib, grad=(FAKE * 11, FAKE * 12, FAKE)) == 1     # dV aliases Q

@@ -216,3 +216,47 @@ def test_long_context_bob_sampled():
                                  a["g_dv"], ncols_tail=256, chunk=32)
         for key in ("gK", "gV"):
             check(f"h{h} {key}", r[key][0, h][-256:], tl[key][0], 5e-2)
+
+
+# ------------------------------------- attn_hvp: one call, fwd + bwd + BoB
+@pytest.mark.parametrize("wid,causal", [(1, True), (None, False)])
+def test_hvp_matches_oracle(wid, causal):
+    import fwd_bwd_double_amd as fbd
+    w = W[wid] if wid else synthetic.Workload("hvp-bf16-nc", 1, 2, 300, 64, "bf16", 7777,
+                                              causal=False, qkv_std=0.5)
+    x, g, a = inputs(w)
+    say(f"[gpu] attn_hvp {w.name} B={w.B} H={w.H} N={w.N} dtype={w.dtype} causal={causal}")
+    r = fbd.attn_hvp(g["q"], g["k"], g["v"], g["do"], g["g_dq"], g["g_dk"], g["g_dv"],
+                     causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.hvp(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                     causal=causal)
+    grad = oracle.bwd(a["q"], a["k"], a["v"], a["do"], causal=causal)
+    t1, t2 = (1e-5, 1e-5) if w.dtype == "fp32" else (2e-2, 5e-2)
+    f64 = synthetic.to_f64
+    for k, rk in (("O", "O"), ("LSE", "LSE")):
+        check(k, f64(r[k]), ref[rk], t1)
+    for k in ("dQ", "dK", "dV"):
+        check(k, f64(r[k]), grad[k], t1)
+    for k, rk in (("Hv_q", "HvQ"), ("Hv_k", "HvK"), ("Hv_v", "HvV"), ("Hv_do", "HvdO")):
+        check(k, f64(r[k]), ref[rk], t2)
+
+
+def test_hvp_symmetry_on_gpu():
+    # <v1, H v2> = <v2, H v1>: the Hessian of <dO, O> is symmetric
+    import fwd_bwd_double_amd as fbd
+    w = W[1]
+    x, g, a = inputs(w)
+    rng = np.random.default_rng(4242)
+    v2 = [torch.from_numpy(rng.standard_normal((w.B, w.H, w.N, w.d))).float().cuda()
+          for _ in range(3)]
+    v1 = [g["g_dq"], g["g_dk"], g["g_dv"]]
+    say(f"[gpu] attn_hvp symmetry {w.name}")
+    h1 = fbd.attn_hvp(g["q"], g["k"], g["v"], g["do"], *v1, scale=w.scale, grad=False)
+    h2 = fbd.attn_hvp(g["q"], g["k"], g["v"], g["do"], *v2, scale=w.scale, grad=False)
+    torch.cuda.synchronize()
+    dot = lambda x, y: float((x.double() * y.double()).sum())
+    lhs = sum(dot(v, h2[k]) for v, k in zip(v1, ("Hv_q", "Hv_k", "Hv_v")))
+    rhs = sum(dot(v, h1[k]) for v, k in zip(v2, ("Hv_q", "Hv_k", "Hv_v")))
+    say(f"    <v1,Hv2> = {lhs:.9g}  <v2,Hv1> = {rhs:.9g}")
+    assert abs(lhs - rhs) <= 1e-5 * max(abs(lhs), abs(rhs))

@@ -140,6 +140,25 @@ def test_bob_hvp_symmetry():
     assert lhs == pytest.approx(rhs, rel=1e-11)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_hvp_is_derivative_of_the_gradient(causal):
+    # H v = d/de grad<dO, O>(x + e v) at e = 0, by central differences of the
+    # (separately pinned) backward: independent of the BoB closed forms
+    Q, K, V, dO, vQ, vK, vV = inputs(1, 2, 9, 6, 155)
+    r = oracle.hvp(Q, K, V, dO, vQ, vK, vV, causal=causal)
+    h = 1e-5
+    gp = oracle.bwd(Q + h * vQ, K + h * vK, V + h * vV, dO, causal=causal)
+    gm = oracle.bwd(Q - h * vQ, K - h * vK, V - h * vV, dO, causal=causal)
+    for name, key in (("dQ", "HvQ"), ("dK", "HvK"), ("dV", "HvV")):
+        num = (gp[name] - gm[name]) / (2 * h)
+        assert np.linalg.norm(num - r[key]) <= 1e-7 * np.linalg.norm(r[key]), key
+    # the dO part: derivative of <v, grad> in dO; grad is linear in dO
+    g1 = oracle.bwd(Q, K, V, dO + 1.0 * vQ, causal=causal)
+    g0 = oracle.bwd(Q, K, V, dO, causal=causal)
+    lhs = dot(vQ, g1["dQ"] - g0["dQ"]) + dot(vK, g1["dK"] - g0["dK"]) + dot(vV, g1["dV"] - g0["dV"])
+    assert lhs == pytest.approx(dot(vQ, r["HvdO"]), rel=1e-10)
+
+
 def test_bob_identities():
     Q, K, V, dO, A, Bk, C = inputs(2, 2, 23, 8, 170)
     r = oracle.bob(Q, K, V, dO, A, Bk, C, with_bwd=True)
