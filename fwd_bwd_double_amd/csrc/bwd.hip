@@ -81,39 +81,46 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
-      f32x16 sacc = zero16(), dpacc = zero16();
+      // S and dP are formed one after the other; P is packed (and its
+      // GProj product issued) before dP is formed, so few values are live
+      const int jt = jb / 16;
+      float p[16];
+      {
+        f32x16 sacc = zero16();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        mma(sacc, ld_row(Ks, jb, kb, lane), qf[kb]);
-        mma(dpacc, ld_row(Vs, jb, kb, lane), dof[kb]);
-      }
-      float p[16], ds[16];
+        for (int kb = 0; kb < 4; ++kb) mma(sacc, ld_row(Ks, jb, kb, lane), qf[kb]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - lse2);
-      if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
+        for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - lse2);
+        if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          p[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? 0.f : p[v];
+          for (int v = 0; v < 16; ++v) {
+            const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
+            p[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? 0.f : p[v];
+          }
         }
       }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ds[v] = p[v] * (dpacc[v] - Di);
-      const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
-      const int jt = jb / 16;
-      const Frag<T> a00 = ld_tr(Ks, 0, jt, lane), a01 = ld_tr(Ks, 0, jt + 1, lane);
-      const Frag<T> a10 = ld_tr(Ks, 32, jt, lane), a11 = ld_tr(Ks, 32, jt + 1, lane);
-      mma(dq0, a00, df0);
-      mma(dq0, a01, df1);
-      mma(dq1, a10, df0);
-      mma(dq1, a11, df1);
       if constexpr (GPROJ) {
-        r += frag_sum(df0) + frag_sum(df1);
-        const Frag<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
-        mma(pk0, a00, pf0);
-        mma(pk0, a01, pf1);
-        mma(pk1, a10, pf0);
-        mma(pk1, a11, pf1);
+        // PK += R(P) K
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const Frag<T> pf = pack8<T>(p + 8 * tt);
+          mma(pk0, ld_tr(Ks, 0, jt + tt, lane), pf);
+          mma(pk1, ld_tr(Ks, 32, jt + tt, lane), pf);
+        }
+      }
+      // dS = P o (dP - D):  dQ += R(dS) K,  r += sum of exactly those bf16 values
+      f32x16 ds = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(ds, ld_row(Vs, jb, kb, lane), dof[kb]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = p[8 * tt + k] * (ds[8 * tt + k] - Di);
+        const Frag<T> df = pack8<T>(e);
+        if constexpr (GPROJ) r += frag_sum(df);
+        mma(dq0, ld_tr(Ks, 0, jt + tt, lane), df);
+        mma(dq1, ld_tr(Ks, 32, jt + tt, lane), df);
       }
     }
   };
@@ -212,62 +219,69 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
       const int is = i0 + ib;
       // all waves compute all sub-blocks: rows before a key (causal) and rows
       // past N are masked below
-      f32x16 sacc = zero16(), dpacc = zero16();
+      // S and dP are formed one after the other and each is consumed at
+      // once (P -> dV, then dS -> dK), so few values are live together
+      const int it = ib / 16;
+      float p[16];
+      {
+        f32x16 sacc = zero16();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        mma(sacc, ld_row(Qs, ib, kb, lane), kf[kb]);
-        mma(dpacc, ld_row(dOs, ib, kb, lane), vf[kb]);
+        for (int kb = 0; kb < 4; ++kb) mma(sacc, ld_row(Qs, ib, kb, lane), kf[kb]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[ib + 8 * q + 4 * h]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            p[4 * q + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * q + u], sl2, l4[u]));
+        }
+        if ((CAUSAL && is <= kw) || is + 32 > N) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
+            p[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : p[v];
+          }
+        }
       }
-      float p[16], ds[16], rp[16];
+      // dV += R(P)^T dO
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const Frag<T> pf = pack8<T>(p + 8 * tt);
+        mma(dv0, ld_tr(dOs, 0, it + tt, lane), pf);
+        mma(dv1, ld_tr(dOs, 32, it + tt, lane), pf);
+      }
+      // dS = P o (dP - D):  dK += R(dS)^T Q  (+ GProj key correction
+      // - R(P)^T (r o Q) as Q^T R(-r o P), a separate fp32-accumulated
+      // product, so the projected dS is never re-rounded)
+      f32x16 ds = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(ds, ld_row(dOs, ib, kb, lane), vf[kb]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int rbase = ib + 8 * q + 4 * h;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[rbase]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[rbase]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[ib + 8 * q + 4 * h]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int v = 4 * q + u;
-          p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], sl2, l4[u]));
-          ds[v] = dpacc[v] - d4[u];
-        }
+        for (int u = 0; u < 4; ++u) ds[4 * q + u] = p[4 * q + u] * (ds[4 * q + u] - d4[u]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = ds[8 * tt + k];
+        const Frag<T> df = pack8<T>(e);
+        const Frag<T> qa = ld_tr(Qs, 0, it + tt, lane), qb = ld_tr(Qs, 32, it + tt, lane);
+        mma(dk0, qa, df);
+        mma(dk1, qb, df);
         if constexpr (GPROJ) {
-          const f32x4 r4 = *reinterpret_cast<const f32x4*>(&sR[rbase]);
+          float rp[8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) rp[4 * q + u] = -r4[u];
+          for (int q = 0; q < 2; ++q) {
+            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&sR[ib + 16 * tt + 8 * q + 4 * h]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rp[4 * q + u] = -r4[u] * p[8 * tt + 4 * q + u];
+          }
+          const Frag<T> rf = pack8<T>(rp);
+          mma(dk0, qa, rf);
+          mma(dk1, qb, rf);
         }
-      }
-      if ((CAUSAL && is <= kw) || is + 32 > N) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
-          p[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : p[v];
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ds[v] *= p[v];
-      const Frag<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
-      const Frag<T> df0 = pack8<T>(ds), df1 = pack8<T>(ds + 8);
-      const int it = ib / 16;
-      const Frag<T> q00 = ld_tr(Qs, 0, it, lane), q01 = ld_tr(Qs, 0, it + 1, lane);
-      const Frag<T> q10 = ld_tr(Qs, 32, it, lane), q11 = ld_tr(Qs, 32, it + 1, lane);
-      mma(dv0, ld_tr(dOs, 0, it, lane), pf0);
-      mma(dv0, ld_tr(dOs, 0, it + 1, lane), pf1);
-      mma(dv1, ld_tr(dOs, 32, it, lane), pf0);
-      mma(dv1, ld_tr(dOs, 32, it + 1, lane), pf1);
-      mma(dk0, q00, df0);
-      mma(dk0, q01, df1);
-      mma(dk1, q10, df0);
-      mma(dk1, q11, df1);
-      if constexpr (GPROJ) {
-        // key correction  - R(P)^T (r o Q)  as  Q^T R(-r o P): a separate
-        // fp32-accumulated product, so the projected dS is never re-rounded
-#pragma unroll
-        for (int v = 0; v < 16; ++v) rp[v] *= p[v];
-        const Frag<T> rf0 = pack8<T>(rp), rf1 = pack8<T>(rp + 8);
-        mma(dk0, q00, rf0);
-        mma(dk0, q01, rf1);
-        mma(dk1, q10, rf0);
-        mma(dk1, q11, rf1);
       }
     }
   };
