@@ -21,9 +21,10 @@
 // d-vectors per row
 //   XE = sum_j R(P (W (dP - D) + U)) K_j + R(dS) Bk_j,   Y = sum_j R(P) K_j,
 //   Z  = sum_j R(P dP) K_j,   FG = sum_j R(P W) V_j + R(P) C_j,
-// plus the row sums alpha_i and b_i = sum_j P (W dP + U), and after the last
-// key block applies the corrections once:
-//   beta_i = b_i - 2 alpha_i D_i,
+// plus the row sums alpha_i and x_i = sum_j P (W (dP - D) + U) (the fp32
+// values whose bf16 roundings feed XE), and after the last key block applies
+// the corrections once:
+//   beta_i = b_i - 2 alpha_i D_i = x_i - alpha_i D_i   (b_i = sum_j P (W dP + U)),
 //   gQ = scale (XE - alpha Z - beta Y),   gdO = FG - alpha O
 // (sum_j P_ij V_j = O_i).  It writes gQ, gdO and the row states D, alpha, beta.
 //
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
 
   f32x16 X0 = zero16(), X1 = zero16(), Y0 = zero16(), Y1 = zero16();
   f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
-  float alpha = 0.f, bsum = 0.f;
+  float alpha = 0.f, xsum = 0.f;
 
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend + BN - 1) / BN;
@@ -135,8 +136,8 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         const float dpd = dp[v] - Di;
         const float pw = pv * W;
         alpha += pw;
-        bsum += pv * (W * dp[v] + u[v]);
         xs[v] = pv * (W * dpd + u[v]);
+        xsum += xs[v];
         zs[v] = pv * dp[v];
         es[v] = pv * dpd;
         fs[v] = pw;
@@ -180,8 +181,9 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     if (t + 1 < ntiles) tile(t + 1, B1, B0);
   }
   alpha = half_sum(alpha);
-  bsum = half_sum(bsum);
-  const float beta = bsum - 2.f * alpha * Di;
+  // b = sum_j P (W dP + U) = sum_j x + alpha D, so beta = b - 2 alpha D = sum_j x - alpha D
+  xsum = half_sum(xsum);
+  const float beta = xsum - alpha * Di;
   float out[16], ov[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - beta * Y0[v]);
