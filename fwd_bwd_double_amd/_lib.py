@@ -66,6 +66,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_passes.restype = i32
     lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
     lib.attn_bob_passes.restype = i32
+    lib.attn_fwd_gqa.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, f32, vp, vp, vp]
+    lib.attn_fwd_gqa.restype = i32
+    lib.attn_bwd_gqa.argtypes = lib.attn_bwd.argtypes[:3] + [i64] + lib.attn_bwd.argtypes[3:]
+    lib.attn_bwd_gqa.restype = i32
+    lib.attn_bob_gqa.argtypes = lib.attn_bob.argtypes[:3] + [i64] + lib.attn_bob.argtypes[3:]
+    lib.attn_bob_gqa.restype = i32
     lib.attn_hvp_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_hvp_workspace_bytes.restype = sz
     lib.attn_hvp.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32,
@@ -109,6 +115,22 @@ def _raise(fn: str, st: int):
         raise AttnError(fn, st, load().attn_last_hip_error())
 
 
+def _kv_heads(q: torch.Tensor, k: torch.Tensor) -> int:
+    """Key/value heads of k: 1 <= Hkv <= H and H % Hkv == 0 (grouped-query
+    attention when Hkv < H)."""
+    if k.dim() != 4:
+        raise ValueError("k must be shaped (B, Hkv, N, d)")
+    H, Hkv = q.shape[1], k.shape[1]
+    if Hkv < 1 or Hkv > H or H % Hkv:
+        raise ValueError(f"k has {Hkv} heads; it must divide q's {H}")
+    return Hkv
+
+
+def _kv_shape(q: torch.Tensor, Hkv: int):
+    B, _, N, d = q.shape
+    return (B, Hkv, N, d)
+
+
 def _scale(q: torch.Tensor, scale: Optional[float]) -> float:
     return 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
 
@@ -128,19 +150,21 @@ def hvp_workspace_bytes(B: int, H: int, N: int) -> int:
 def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
              ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O, LSE = attention(q, k, v); q, k, v shaped (B, H, N, d), bf16 or fp32."""
+    """O, LSE = attention(q, k, v); q shaped (B, H, N, d), k and v (B, Hkv, N, d)
+    with H % Hkv == 0 (Hkv < H: grouped-query attention), bf16 or fp32."""
     lib = load()
-    for n, t in (("k", k), ("v", v)):
-        _check(n, t, q)
     _check("q", q, q)
+    Hkv = _kv_heads(q, k)
+    for n, t in (("k", k), ("v", v)):
+        _check(n, t, q, shape=_kv_shape(q, Hkv))
     B, H, N, d = q.shape
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
     _check("out", out, q)
     _check("lse", lse, q, torch.float32, (B, H, N))
-    st = lib.attn_fwd(_dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                      1 if causal else 0, _scale(q, scale), out.data_ptr(), lse.data_ptr(),
-                      _stream(q.device))
+    st = lib.attn_fwd_gqa(_dt(q), B, H, Hkv, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          1 if causal else 0, _scale(q, scale), out.data_ptr(), lse.data_ptr(),
+                          _stream(q.device))
     _raise("attn_fwd", st)
     return out, lse
 
@@ -152,23 +176,37 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
     the row states D, r and -LSE*log2(e), each B*H*N floats, afterwards.
     passes: 1 row pass, 2 column pass, 3 both."""
     lib = load()
-    for n, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+    Hkv = _kv_heads(q, k)
+    kvs = _kv_shape(q, Hkv)
+    for n, t in (("o", o), ("do", do)):
         _check(n, t, q)
+    for n, t in (("k", k), ("v", v)):
+        _check(n, t, q, shape=kvs)
     B, H, N, d = q.shape
     _check("lse", lse, q, torch.float32, (B, H, N))
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if outs is None else outs
-    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check(n, t, q)
+    if outs is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    else:
+        dq, dk, dv = outs
+    _check("dq", dq, q)
+    for n, t in (("dk", dk), ("dv", dv)):
+        _check(n, t, q, shape=kvs)
+    if Hkv != H and passes != 3:
+        raise ValueError("grouped-query backward runs both passes (passes=3)")
     need = lib.attn_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.attn_bwd_passes(passes, _dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                      lse.data_ptr(), do.data_ptr(), 1 if causal else 0, _scale(q, scale),
-                      1 if gproj else 0, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      workspace.data_ptr(), ws_bytes, _stream(q.device))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), 1 if causal else 0, _scale(q, scale), 1 if gproj else 0,
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes,
+            _stream(q.device))
+    if Hkv == H:
+        st = lib.attn_bwd_passes(passes, _dt(q), B, H, N, d, *args)
+    else:
+        st = lib.attn_bwd_gqa(_dt(q), B, H, Hkv, N, d, *args)
     _raise("attn_bwd", st)
     return dq, dk, dv
 
@@ -180,25 +218,39 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
     beta, -LSE*log2(e) and kappa = alpha*D + beta afterwards."""
     lib = load()
-    for n, t in (("k", k), ("v", v), ("o", o), ("do", do), ("g_dq", g_dq), ("g_dk", g_dk),
-                 ("g_dv", g_dv)):
+    Hkv = _kv_heads(q, k)
+    kvs = _kv_shape(q, Hkv)
+    for n, t in (("o", o), ("do", do), ("g_dq", g_dq)):
         _check(n, t, q)
+    for n, t in (("k", k), ("v", v), ("g_dk", g_dk), ("g_dv", g_dv)):
+        _check(n, t, q, shape=kvs)
     B, H, N, d = q.shape
     _check("lse", lse, q, torch.float32, (B, H, N))
-    gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4)) if outs is None else outs
-    for n, t in (("g_q", gq), ("g_k", gk), ("g_v", gv), ("g_do", gdo)):
+    if outs is None:
+        gq, gk, gv, gdo = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(k),
+                           torch.empty_like(q))
+    else:
+        gq, gk, gv, gdo = outs
+    for n, t in (("g_q", gq), ("g_do", gdo)):
         _check(n, t, q)
+    for n, t in (("g_k", gk), ("g_v", gv)):
+        _check(n, t, q, shape=kvs)
+    if Hkv != H and passes != 3:
+        raise ValueError("grouped-query BoB runs both passes (passes=3)")
     need = lib.attn_bob_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                      lse.data_ptr(), do.data_ptr(), g_dq.data_ptr(), g_dk.data_ptr(),
-                      g_dv.data_ptr(), 1 if causal else 0, _scale(q, scale), gq.data_ptr(),
-                      gk.data_ptr(), gv.data_ptr(), gdo.data_ptr(), workspace.data_ptr(),
-                      ws_bytes, _stream(q.device))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), g_dq.data_ptr(), g_dk.data_ptr(), g_dv.data_ptr(),
+            1 if causal else 0, _scale(q, scale), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+            gdo.data_ptr(), workspace.data_ptr(), ws_bytes, _stream(q.device))
+    if Hkv == H:
+        st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, *args)
+    else:
+        st = lib.attn_bob_gqa(_dt(q), B, H, Hkv, N, d, *args)
     _raise("attn_bob", st)
     return gq, gk, gv, gdo
 

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
     float* __restrict__ Bws, float* __restrict__ Lws, float* __restrict__ Kws, int N, int BH,
-    int nblk, float scale) {
+    int H, int grp, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   struct Buf {
@@ -59,12 +59,13 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
+  const size_t kvoff = (size_t)kv_head(wk.head, H, grp) * N * HD;
   const size_t soff = (size_t)wk.head * N;
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
-  const auto rk = make_rsrc(K + hoff, hbytes);
-  const auto rv = make_rsrc(V + hoff, hbytes);
-  const auto rb = make_rsrc(Bk + hoff, hbytes);
-  const auto rc = make_rsrc(C + hoff, hbytes);
+  const auto rk = make_rsrc(K + kvoff, hbytes);
+  const auto rv = make_rsrc(V + kvoff, hbytes);
+  const auto rb = make_rsrc(Bk + kvoff, hbytes);
+  const auto rc = make_rsrc(C + kvoff, hbytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q0 = wk.blk * BLK;
   const int qw = q0 + wave * WROWS;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const float* __restrict__ Lws, const T* __restrict__ dO, const T* __restrict__ A,
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
     const float* __restrict__ Aws, const float* __restrict__ Kws, T* __restrict__ gK,
-    T* __restrict__ gV, int N, int BH, float scale) {
+    T* __restrict__ gV, int N, int BH, int H, int grp, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, kappa of the tile's rows
@@ -225,17 +226,12 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
 
-  const Work wk = col_work(BH);
-  const size_t hoff = (size_t)wk.head * N * HD;
-  const size_t soff = (size_t)wk.head * N;
+  // workgroup = (key block, key/value head); the query heads sharing that
+  // key head stream past in turn, accumulating into the same gK, gV
+  const Work wk = col_work(BH / grp);
+  const size_t hoff = (size_t)wk.head * N * HD;   // key-side tensors
+  const int qh0 = first_q_head(wk.head, H, grp);
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
-  const auto rq = make_rsrc(Q + hoff, hbytes);
-  const auto rdo = make_rsrc(dO + hoff, hbytes);
-  const auto ra = make_rsrc(A + hoff, hbytes);
-  const auto rl = make_rsrc(Lws + soff, (uint32_t)N * 4u);
-  const auto rd = make_rsrc(Dws + soff, (uint32_t)N * 4u);
-  const auto ral = make_rsrc(Aws + soff, (uint32_t)N * 4u);
-  const auto rka = make_rsrc(Kws + soff, (uint32_t)N * 4u);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = wk.blk * BLK;
   const int kw = k0 + wave * WROWS;
@@ -252,23 +248,29 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
 
   const int istart = CAUSAL ? k0 : 0;
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
-  auto stage = [&](int i0, Buf& b) {
-    dma_tile<T, BM, NT / 64>(rq, i0, b.q, wave, lane);
-    dma_tile<T, BM, NT / 64>(rdo, i0, b.dO, wave, lane);
-    dma_tile<T, BM, NT / 64>(ra, i0, b.a, wave, lane);
+  const int nsteps = ntiles * grp;      // (query head, query tile) steps
+  // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
+  auto stage = [&](int u, Buf& b) {
+    const int qh = qh0 + u / ntiles;
+    const int i0 = istart + (u % ntiles) * BM;
+    const size_t qoff = (size_t)qh * N * HD, soff = (size_t)qh * N;
+    const uint32_t sbytes = (uint32_t)N * 4u;
+    dma_tile<T, BM, NT / 64>(make_rsrc(Q + qoff, hbytes), i0, b.q, wave, lane);
+    dma_tile<T, BM, NT / 64>(make_rsrc(dO + qoff, hbytes), i0, b.dO, wave, lane);
+    dma_tile<T, BM, NT / 64>(make_rsrc(A + qoff, hbytes), i0, b.a, wave, lane);
 #pragma unroll
     for (int k = 0; k < BM / 64; ++k) {
-      if (wave == 0) dma_rows_f32(rl, i0, b.nl, k, lane);
-      if (wave == 1) dma_rows_f32(rd, i0, b.D, k, lane);
-      if (wave == 2) dma_rows_f32(ral, i0, b.al, k, lane);
-      if (wave == 3) dma_rows_f32(rka, i0, b.ka, k, lane);
+      if (wave == 0) dma_rows_f32(make_rsrc(Lws + soff, sbytes), i0, b.nl, k, lane);
+      if (wave == 1) dma_rows_f32(make_rsrc(Dws + soff, sbytes), i0, b.D, k, lane);
+      if (wave == 2) dma_rows_f32(make_rsrc(Aws + soff, sbytes), i0, b.al, k, lane);
+      if (wave == 3) dma_rows_f32(make_rsrc(Kws + soff, sbytes), i0, b.ka, k, lane);
     }
   };
-  auto tile = [&](int t, const Buf& cb, Buf& nb) {
-    const int i0 = istart + t * BM;
+  auto tile = [&](int u, const Buf& cb, Buf& nb) {
+    const int i0 = istart + (u % ntiles) * BM;
     wait_dma();
-    __syncthreads();   // tile t is in cb; every wave is done with nb
-    if (t + 1 < ntiles) stage(i0 + BM, nb);
+    __syncthreads();   // step u is in cb; every wave is done with nb
+    if (u + 1 < nsteps) stage(u + 1, nb);
     const T* Qs = cb.q;
     const T* dOs = cb.dO;
     const T* As = cb.a;
@@ -370,10 +372,10 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
       }
     }
   };
-  if (ntiles > 0) stage(istart, B0);
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, B0, B1);
-    if (t + 1 < ntiles) tile(t + 1, B1, B0);
+  if (nsteps > 0) stage(0, B0);
+  for (int u = 0; u < nsteps; u += 2) {
+    tile(u, B0, B1);
+    if (u + 1 < nsteps) tile(u + 1, B1, B0);
   }
   float out[16];
 #pragma unroll
@@ -395,7 +397,7 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
                                float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
-                               int N, float scale, int passes, hipStream_t st) {
+                               int H, int grp, int N, float scale, int passes, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
@@ -403,25 +405,25 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
     hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
                        (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws,
-                       Lws, Kws, N, BH, nblk, scale);
+                       Lws, Kws, N, BH, H, grp, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
+  hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL>), dim3(nblk * (BH / grp)), dim3(NT), 0, st,
                      (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO,
                      (const T*)gdQ, (const T*)gdK, (const T*)gdV, (const float*)Dws,
-                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, scale);
+                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
-                      float* Aws, float* Bws, float* Lws, float* Kws, int BH, int N, int causal,
-                      float scale, int passes, hipStream_t st) {
+                      float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
+                      int N, int causal, float scale, int passes, hipStream_t st) {
 #define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, Lws, Kws, \
-                     BH, N, scale, passes, st
+                     BH, H, grp, N, scale, passes, st
   if (dt == 0)
     return causal ? launch_bob_t<bf16, true>(FBD_BOB_ARGS) : launch_bob_t<bf16, false>(FBD_BOB_ARGS);
   return causal ? launch_bob_t<float, true>(FBD_BOB_ARGS) : launch_bob_t<float, false>(FBD_BOB_ARGS);

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, float* __restrict__ Lws,
-    int N, int BH, int nblk, float scale) {
+    int N, int BH, int H, int grp, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   __shared__ __attribute__((aligned(16))) T K0[BN * HD];
@@ -42,10 +42,11 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
+  const size_t kvoff = (size_t)kv_head(wk.head, H, grp) * N * HD;
   const size_t soff = (size_t)wk.head * N;
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
-  const auto rk = make_rsrc(K + hoff, hbytes);
-  const auto rv = make_rsrc(V + hoff, hbytes);
+  const auto rk = make_rsrc(K + kvoff, hbytes);
+  const auto rv = make_rsrc(V + kvoff, hbytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q0 = wk.blk * BLK;
   const int qw = q0 + wave * WROWS;
@@ -158,8 +159,8 @@ template <class T, int BM, bool GPROJ, bool CAUSAL>
 __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const float* __restrict__ Dws,
-    const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
-    float scale) {
+    const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int H,
+    int grp, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q and dO tiles and the -LSE*log2(e), D (, r) of the tile's rows
@@ -171,15 +172,13 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
 
-  const Work wk = col_work(BH);
-  const size_t hoff = (size_t)wk.head * N * HD;
-  const size_t soff = (size_t)wk.head * N;
+  // workgroup = (key block, key/value head); the query heads sharing that
+  // key head stream past in turn and their contributions accumulate into the
+  // same dK, dV registers
+  const Work wk = col_work(BH / grp);
+  const size_t hoff = (size_t)wk.head * N * HD;   // key-side tensors
+  const int qh0 = first_q_head(wk.head, H, grp);
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
-  const auto rq = make_rsrc(Q + hoff, hbytes);
-  const auto rdo = make_rsrc(dO + hoff, hbytes);
-  const auto rl = make_rsrc(Lws + soff, (uint32_t)N * 4u);
-  const auto rd = make_rsrc(Dws + soff, (uint32_t)N * 4u);
-  const auto rr = make_rsrc(Rws + soff, (uint32_t)N * 4u);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = wk.blk * BLK;
   const int kw = k0 + wave * WROWS;
@@ -194,21 +193,27 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
 
   const int istart = CAUSAL ? k0 : 0;   // k0 is a multiple of BM
   const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
-  auto stage = [&](int i0, Buf& b) {
-    dma_tile<T, BM, NT / 64>(rq, i0, b.q, wave, lane);
-    dma_tile<T, BM, NT / 64>(rdo, i0, b.dO, wave, lane);
+  const int nsteps = ntiles * grp;      // (query head, query tile) steps
+  // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
+  auto stage = [&](int u, Buf& b) {
+    const int qh = qh0 + u / ntiles;
+    const int i0 = istart + (u % ntiles) * BM;
+    const size_t qoff = (size_t)qh * N * HD, soff = (size_t)qh * N;
+    dma_tile<T, BM, NT / 64>(make_rsrc(Q + qoff, hbytes), i0, b.q, wave, lane);
+    dma_tile<T, BM, NT / 64>(make_rsrc(dO + qoff, hbytes), i0, b.dO, wave, lane);
 #pragma unroll
     for (int k = 0; k < BM / 64; ++k) {
-      if (wave == 0) dma_rows_f32(rl, i0, b.nl, k, lane);
-      if (wave == 1) dma_rows_f32(rd, i0, b.D, k, lane);
-      if (GPROJ && wave == 2) dma_rows_f32(rr, i0, b.r, k, lane);
+      if (wave == 0) dma_rows_f32(make_rsrc(Lws + soff, (uint32_t)N * 4u), i0, b.nl, k, lane);
+      if (wave == 1) dma_rows_f32(make_rsrc(Dws + soff, (uint32_t)N * 4u), i0, b.D, k, lane);
+      if (GPROJ && wave == 2)
+        dma_rows_f32(make_rsrc(Rws + soff, (uint32_t)N * 4u), i0, b.r, k, lane);
     }
   };
-  auto tile = [&](int t, const Buf& cb, Buf& nb) {
-    const int i0 = istart + t * BM;
+  auto tile = [&](int u, const Buf& cb, Buf& nb) {
+    const int i0 = istart + (u % ntiles) * BM;
     wait_dma();
-    __syncthreads();   // tile t is in cb; every wave is done with nb
-    if (t + 1 < ntiles) stage(i0 + BM, nb);
+    __syncthreads();   // step u is in cb; every wave is done with nb
+    if (u + 1 < nsteps) stage(u + 1, nb);
     const T* Qs = cb.q;
     const T* dOs = cb.dO;
     const float* sL = cb.nl;
@@ -285,10 +290,10 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
       }
     }
   };
-  if (ntiles > 0) stage(istart, B0);
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, B0, B1);
-    if (t + 1 < ntiles) tile(t + 1, B1, B0);
+  if (nsteps > 0) stage(0, B0);
+  for (int u = 0; u < nsteps; u += 2) {
+    tile(u, B0, B1);
+    if (u + 1 < nsteps) tile(u + 1, B1, B0);
   }
   float out[16];
 #pragma unroll
@@ -308,22 +313,23 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
 template <class T, bool GPROJ, bool CAUSAL>
 static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
-                               float* Dws, float* Rws, float* Lws, int BH, int N, float scale,
-                               int passes, hipStream_t st) {
+                               float* Dws, float* Rws, float* Lws, int BH, int H, int grp,
+                               int N, float scale, int passes, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
     hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
-                       (T*)dQ, Dws, Rws, Lws, N, BH, nblk, scale);
+                       (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
-                     (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO, (const float*)Dws,
-                     (const float*)Rws, (T*)dK, (T*)dV, N, BH, scale);
+  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL>), dim3(nblk * (BH / grp)), dim3(NT),
+                     0, st, (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws,
+                     (const T*)dO, (const float*)Dws, (const float*)Rws, (T*)dK, (T*)dV, N, BH, H,
+                     grp, scale);
   return hipGetLastError();
 }
 
@@ -331,24 +337,24 @@ template <class T, bool GPROJ>
 static hipError_t launch_bwd_c(int causal, const void* Q, const void* K, const void* V,
                                const void* O, const float* LSE, const void* dO, void* dQ,
                                void* dK, void* dV, float* Dws, float* Rws, float* Lws, int BH,
-                               int N, float scale, int passes, hipStream_t st) {
+                               int H, int grp, int N, float scale, int passes, hipStream_t st) {
   if (causal)
-    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
-  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
+    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
+  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
 }
 
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
-                      float* Rws, float* Lws, int BH, int N, int causal, float scale, int gproj,
-                      int passes, hipStream_t st) {
+                      float* Rws, float* Lws, int BH, int H, int grp, int N, int causal,
+                      float scale, int gproj, int passes, hipStream_t st) {
   if (dt == 0) {
     if (gproj)
-      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
-    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
+      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
+    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
   }
   if (gproj)
-    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
-  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, N, scale, passes, st);
+    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
+  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
 }
 
 }  // namespace fbd

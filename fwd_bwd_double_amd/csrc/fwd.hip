@@ -41,7 +41,7 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,
-                                                     int nblk, float scale) {
+                                                     int H, int grp, int nblk, float scale) {
   // two buffers as separate objects, used in a loop unrolled by two, so the
   // compiler can tell the copy of the next tile never aliases the reads of
   // the current one (and places no wait between them)
@@ -52,9 +52,10 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
+  const size_t kvoff = (size_t)kv_head(wk.head, H, grp) * N * HD;
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
-  const auto rk = make_rsrc(K + hoff, hbytes);
-  const auto rv = make_rsrc(V + hoff, hbytes);
+  const auto rk = make_rsrc(K + kvoff, hbytes);
+  const auto rv = make_rsrc(V + kvoff, hbytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q0 = wk.blk * FWD_BLK;
   const int qw = q0 + wave * FWD_G * WROWS;
@@ -208,22 +209,23 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 
 template <class T, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               int BH, int N, float scale, hipStream_t st) {
+                               int BH, int H, int grp, int N, float scale, hipStream_t st) {
   constexpr int BN = sizeof(T) == 2 ? FBD_FWD_BN : 64;
   const int nblk = (N + FWD_BLK - 1) / FWD_BLK;
   hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
-                     (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, nblk, scale);
+                     (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, nblk,
+                     scale);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int BH, int N, int causal, float scale, hipStream_t st) {
+                      int BH, int H, int grp, int N, int causal, float scale, hipStream_t st) {
   if (dt == 0) {
-    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, N, scale, st);
-    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, N, scale, st);
+    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
+    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
   }
-  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, N, scale, st);
-  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, N, scale, st);
+  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
+  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
 }
 
 }  // namespace fbd

@@ -345,5 +345,15 @@ __device__ __forceinline__ Work col_work(int bh) {
   const int L = blockIdx.x;
   return Work{L % bh, L / bh};
 }
+// Key/value head used by query head `head` (of BH = batch * H): groups of grp
+// consecutive query heads share one key/value head.
+__device__ __forceinline__ int kv_head(int head, int H, int grp) {
+  return (head / H) * (H / grp) + (head % H) / grp;
+}
+// First query head of key/value head `kvh`.
+__device__ __forceinline__ int first_q_head(int kvh, int H, int grp) {
+  const int hkv = H / grp;
+  return (kvh / hkv) * H + (kvh % hkv) * grp;
+}
 
 }  // namespace fbd

@@ -34,7 +34,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["probs", "fwd", "bwd", "bob", "hvp", "rows", "last_columns", "gproj_project",
-           "max_prob"]
+           "max_prob", "expand_kv", "reduce_kv", "fwd_gqa", "bwd_gqa", "bob_gqa"]
 
 
 def _f64(x):
@@ -234,6 +234,54 @@ def hvp(Q, K, V, dO, vQ, vK, vV, causal=True, scale=None, heads=None, chunk=1024
     r = bob(Q, K, V, dO, vQ, vK, vV, causal=causal, scale=scale, heads=heads, chunk=chunk)
     return {"O": r["O"], "LSE": r["LSE"], "HvQ": r["gQ"], "HvK": r["gK"], "HvV": r["gV"],
             "HvdO": r["gdO"]}
+
+
+# ----------------------------------------------------- shared keys and values
+# Grouped-query attention (FlashBoB page, closing paragraph: shared keys and
+# values are named among the next extensions).  Query head h of a batch reads
+# key/value head h // g, g = H / Hkv; the model is multi-head attention on the
+# expanded K, V, and by the chain rule the gradient of a shared key-side
+# tensor is the sum of its copies' gradients.
+
+def expand_kv(X, group):
+    """(B, Hkv, N, d) -> (B, Hkv * group, N, d): head h is a copy of h // group."""
+    return np.repeat(_f64(X), group, axis=1)
+
+
+def reduce_kv(G, group):
+    """(B, H, N, d) per-query-head gradients -> (B, H / group, N, d) group sums."""
+    B, H, N, d = G.shape
+    return G.reshape(B, H // group, group, N, d).sum(axis=2)
+
+
+def _group(Q, K):
+    H, Hkv = np.shape(Q)[1], np.shape(K)[1]
+    assert H % Hkv == 0
+    return H // Hkv
+
+
+def fwd_gqa(Q, K, V, causal=True, scale=None):
+    g = _group(Q, K)
+    return fwd(Q, expand_kv(K, g), expand_kv(V, g), causal=causal, scale=scale)
+
+
+def bwd_gqa(Q, K, V, dO, causal=True, scale=None):
+    g = _group(Q, K)
+    r = bwd(Q, expand_kv(K, g), expand_kv(V, g), dO, causal=causal, scale=scale)
+    r["dK"], r["dV"] = reduce_kv(r["dK"], g), reduce_kv(r["dV"], g)
+    return r
+
+
+def bob_gqa(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, with_bwd=False):
+    """BoB of the grouped-query map: <gdK, dK> with dK summed over a group is
+    <expand(gdK), dK per query head>, so the cotangents expand like K and V
+    and the key-side outputs reduce like dK, dV."""
+    g = _group(Q, K)
+    r = bob(Q, expand_kv(K, g), expand_kv(V, g), dO, gdQ, expand_kv(gdK, g), expand_kv(gdV, g),
+            causal=causal, scale=scale, with_bwd=with_bwd)
+    for k in ("gK", "gV") + (("dK", "dV") if with_bwd else ()):
+        r[k] = reduce_kv(r[k], g)
+    return r
 
 
 def rows(Q, K, V, dO=None, gdQ=None, gdK=None, gdV=None, row_idx=None,

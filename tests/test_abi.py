@@ -98,3 +98,9 @@ def test_hvp_rejects_bad_arguments_before_launch(lib):
     assert hvp_call(lib, grad=(FAKE * 11, None, FAKE * 13)) == 1     # partial gradient set
     assert hvp_call(lib, ws_bytes=fbd.hvp_workspace_bytes(1, 1, 8) - 4) == 4
     assert hvp_call(lib, grad=(FAKE * 11, FAKE * 12, FAKE)) == 1     # dV aliases Q
+
+
+def test_grouped_query_rejects_bad_head_counts(lib):
+    p = [FAKE * (i + 1) for i in range(3)]
+    for H, Hkv in ((4, 3), (4, 0), (4, 8), (4, -1)):
+        assert lib.attn_fwd_gqa(0, 1, H, Hkv, 8, 64, *p, 1, 0.125, FAKE * 4, FAKE * 5, None) == 1

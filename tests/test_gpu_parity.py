@@ -260,3 +260,37 @@ def test_hvp_symmetry_on_gpu():
     rhs = sum(dot(v, h1[k]) for v, k in zip(v2, ("Hv_q", "Hv_k", "Hv_v")))
     say(f"    <v1,Hv2> = {lhs:.9g}  <v2,Hv1> = {rhs:.9g}")
     assert abs(lhs - rhs) <= 1e-5 * max(abs(lhs), abs(rhs))
+
+
+# --------------------- grouped-query / multi-query attention (shared K, V)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("H,Hkv,N", [(4, 2, 129), (4, 1, 300), (6, 3, 64)])
+def test_grouped_query(H, Hkv, N, causal, dtype):
+    import fwd_bwd_double_amd as fbd
+    w = synthetic.Workload(f"gqa-{dtype}", 2, H, N, 64, dtype, 8100 + N + H, causal=causal,
+                           qkv_std=1.0)
+    x, g, a = inputs(w)
+    # key-side tensors: the first Hkv heads of the seeded draws
+    for n in ("k", "v", "g_dk", "g_dv"):
+        g[n] = g[n][:, :Hkv].contiguous()
+        a[n] = a[n][:, :Hkv]
+    say(f"[gpu] gqa B=2 H={H} Hkv={Hkv} N={N} dtype={dtype} causal={causal}")
+    o, lse = fbd.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale)
+    t1, t2 = (1e-5, 1e-5) if dtype == "fp32" else (2e-2, 5e-2)
+    ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                         causal=causal, with_bwd=True)
+    f64 = synthetic.to_f64
+    for gproj in (False, True):
+        dq, dk, dv = fbd.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal,
+                                  scale=w.scale, gproj=gproj)
+        gq, gk, gv, gdo = fbd.attn_bob(g["q"], g["k"], g["v"], o, lse, g["do"], g["g_dq"],
+                                       g["g_dk"], g["g_dv"], causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        assert dk.shape == g["k"].shape and gk.shape == g["k"].shape
+        check("O", f64(o), ref["O"], t1)
+        check("LSE", f64(lse), ref["LSE"], t1)
+        for k, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            check(k, f64(t), ref[k], t1)
+        for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
+            check(k, f64(t), ref[k], t2)

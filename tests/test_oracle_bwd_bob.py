@@ -104,6 +104,35 @@ def test_bwd_and_bob_against_torch_double_backward(causal):
         assert np.linalg.norm(mine - ref) <= 1e-12 * max(1.0, np.linalg.norm(ref))
 
 
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (4, 1), (3, 3)])
+def test_grouped_query_against_torch_double_backward(H, Hkv):
+    # shared keys and values: torch's autograd differentiates through
+    # repeat_interleave (its own sum over each group), independently of the
+    # oracle's expand/reduce
+    g = H // Hkv
+    rng = np.random.default_rng(135)
+    Q, dO, A = (rng.standard_normal((1, H, 13, 8)) for _ in range(3))
+    K, V, Bk, C = (rng.standard_normal((1, Hkv, 13, 8)) for _ in range(4))
+    c = 1 / math.sqrt(8)
+    tq, tk, tv, tdo = (torch.tensor(x, requires_grad=True) for x in (Q, K, V, dO))
+    out = torch_attention(tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1),
+                          True, c)
+    gq, gk, gv = torch.autograd.grad(out, (tq, tk, tv), tdo, create_graph=True)
+    phi_ = (gq * torch.from_numpy(A)).sum() + (gk * torch.from_numpy(Bk)).sum() + \
+        (gv * torch.from_numpy(C)).sum()
+    hq, hk, hv, hdo = torch.autograd.grad(phi_, (tq, tk, tv, tdo))
+    o, lse = oracle.fwd_gqa(Q, K, V)
+    r = oracle.bob_gqa(Q, K, V, dO, A, Bk, C, with_bwd=True)
+    assert np.linalg.norm(o - out.detach().numpy()) <= 1e-12 * np.linalg.norm(o)
+    for mine, ref in ((r["dQ"], gq), (r["dK"], gk), (r["dV"], gv), (r["gQ"], hq),
+                      (r["gK"], hk), (r["gV"], hv), (r["gdO"], hdo)):
+        ref = ref.detach().numpy()
+        assert mine.shape == ref.shape
+        assert np.linalg.norm(mine - ref) <= 1e-12 * max(1.0, np.linalg.norm(ref))
+    b = oracle.bwd_gqa(Q, K, V, dO)
+    assert np.linalg.norm(b["dK"] - r["dK"]) <= 1e-13 * np.linalg.norm(b["dK"])
+
+
 # ---------------------------------------------------------------- BoB
 def phi(Q, K, V, dO, A, Bk, C, causal=True):
     g = oracle.bwd(Q, K, V, dO, causal=causal)
