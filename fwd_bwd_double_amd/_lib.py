@@ -66,12 +66,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_passes.restype = i32
     lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
     lib.attn_bob_passes.restype = i32
-    lib.attn_fwd_gqa.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, f32, vp, vp, vp]
-    lib.attn_fwd_gqa.restype = i32
-    lib.attn_bwd_gqa.argtypes = lib.attn_bwd.argtypes[:3] + [i64] + lib.attn_bwd.argtypes[3:]
-    lib.attn_bwd_gqa.restype = i32
-    lib.attn_bob_gqa.argtypes = lib.attn_bob.argtypes[:3] + [i64] + lib.attn_bob.argtypes[3:]
-    lib.attn_bob_gqa.restype = i32
+    # extended forms: Hkv after H, the window after causal
+    lib.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, f32, vp, vp,
+                                vp]
+    lib.attn_fwd_ex.restype = i32
+    a = lib.attn_bwd.argtypes
+    lib.attn_bwd_ex.argtypes = a[:3] + [i64] + a[3:12] + [i64] + a[12:]
+    lib.attn_bwd_ex.restype = i32
+    a = lib.attn_bob.argtypes
+    lib.attn_bob_ex.argtypes = a[:3] + [i64] + a[3:15] + [i64] + a[15:]
+    lib.attn_bob_ex.restype = i32
     lib.attn_hvp_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_hvp_workspace_bytes.restype = sz
     lib.attn_hvp.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32,
@@ -148,10 +152,11 @@ def hvp_workspace_bytes(B: int, H: int, N: int) -> int:
 
 
 def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
-             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
-             ) -> Tuple[torch.Tensor, torch.Tensor]:
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """O, LSE = attention(q, k, v); q shaped (B, H, N, d), k and v (B, Hkv, N, d)
-    with H % Hkv == 0 (Hkv < H: grouped-query attention), bf16 or fp32."""
+    with H % Hkv == 0 (Hkv < H: grouped-query attention), bf16 or fp32.
+    window > 0 (causal only): query i sees keys i - window < j <= i."""
     lib = load()
     _check("q", q, q)
     Hkv = _kv_heads(q, k)
@@ -162,16 +167,16 @@ def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
     lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
     _check("out", out, q)
     _check("lse", lse, q, torch.float32, (B, H, N))
-    st = lib.attn_fwd_gqa(_dt(q), B, H, Hkv, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                          1 if causal else 0, _scale(q, scale), out.data_ptr(), lse.data_ptr(),
-                          _stream(q.device))
+    st = lib.attn_fwd_ex(_dt(q), B, H, Hkv, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         1 if causal else 0, int(window), _scale(q, scale), out.data_ptr(),
+                         lse.data_ptr(), _stream(q.device))
     _raise("attn_fwd", st)
     return out, lse
 
 
 def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
              gproj: bool = False, workspace: Optional[torch.Tensor] = None, outs=None,
-             passes: int = 3) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             passes: int = 3, window: int = 0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV of <dO, O>.  `workspace` (fp32, >= bwd_workspace_bytes) holds
     the row states D, r and -LSE*log2(e), each B*H*N floats, afterwards.
     passes: 1 row pass, 2 column pass, 3 both."""
@@ -191,29 +196,32 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
     _check("dq", dq, q)
     for n, t in (("dk", dk), ("dv", dv)):
         _check(n, t, q, shape=kvs)
-    if Hkv != H and passes != 3:
-        raise ValueError("grouped-query backward runs both passes (passes=3)")
+    ext = Hkv != H or window != 0
+    if ext and passes != 3:
+        raise ValueError("grouped-query or windowed backward runs both passes (passes=3)")
     need = lib.attn_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            do.data_ptr(), 1 if causal else 0, _scale(q, scale), 1 if gproj else 0,
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes,
-            _stream(q.device))
-    if Hkv == H:
-        st = lib.attn_bwd_passes(passes, _dt(q), B, H, N, d, *args)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr())
+    rest = (_scale(q, scale), 1 if gproj else 0, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            workspace.data_ptr(), ws_bytes, _stream(q.device))
+    c = 1 if causal else 0
+    if ext:
+        st = lib.attn_bwd_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window), *rest)
     else:
-        st = lib.attn_bwd_gqa(_dt(q), B, H, Hkv, N, d, *args)
+        st = lib.attn_bwd_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bwd", st)
     return dq, dk, dv
 
 
 def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
              scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, outs=None,
-             passes: int = 3) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+             passes: int = 3, window: int = 0
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
     beta, -LSE*log2(e) and kappa = alpha*D + beta afterwards."""
@@ -235,22 +243,24 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
         _check(n, t, q)
     for n, t in (("g_k", gk), ("g_v", gv)):
         _check(n, t, q, shape=kvs)
-    if Hkv != H and passes != 3:
-        raise ValueError("grouped-query BoB runs both passes (passes=3)")
+    ext = Hkv != H or window != 0
+    if ext and passes != 3:
+        raise ValueError("grouped-query or windowed BoB runs both passes (passes=3)")
     need = lib.attn_bob_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            do.data_ptr(), g_dq.data_ptr(), g_dk.data_ptr(), g_dv.data_ptr(),
-            1 if causal else 0, _scale(q, scale), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
-            gdo.data_ptr(), workspace.data_ptr(), ws_bytes, _stream(q.device))
-    if Hkv == H:
-        st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, *args)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), g_dq.data_ptr(), g_dk.data_ptr(), g_dv.data_ptr())
+    rest = (_scale(q, scale), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(), gdo.data_ptr(),
+            workspace.data_ptr(), ws_bytes, _stream(q.device))
+    c = 1 if causal else 0
+    if ext:
+        st = lib.attn_bob_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window), *rest)
     else:
-        st = lib.attn_bob_gqa(_dt(q), B, H, Hkv, N, d, *args)
+        st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bob", st)
     return gq, gk, gv, gdo
 

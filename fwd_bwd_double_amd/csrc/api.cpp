@@ -51,6 +51,16 @@ attn_status check_heads(int64_t H, int64_t Hkv) {
   return ATTN_OK;
 }
 
+// Sliding window: 0 = none; w > 0 keeps keys i - w < j <= i and needs the
+// causal mask.  The kernels take a window of 2^30 (beyond any N) for none.
+constexpr int kNoWindow = 1 << 30;
+attn_status check_window(int causal, int64_t window, int* win) {
+  if (window < 0) return ATTN_EINVAL;
+  if (window > 0 && !causal) return ATTN_EUNSUPPORTED;
+  *win = (window == 0 || window >= kNoWindow) ? kNoWindow : (int)window;
+  return ATTN_OK;
+}
+
 struct Arg {
   const void* p;
   size_t bytes;
@@ -118,35 +128,39 @@ size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   return (size_t)5 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
-attn_status attn_fwd_gqa(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* Q, const void* K, const void* V, int causal, float scale,
-                         void* O, float* LSE, void* stream) {
+attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V, int causal, int64_t window,
+                        float scale, void* O, float* LSE, void* stream) {
   attn_status st = check_shape(dt, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
+  int win = 0;
+  if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
   const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
   const size_t tk = (size_t)B * Hkv * N * d * elem_size(dt);
   st = check_ptrs({{Q, t}, {K, tk}, {V, tk}}, {{O, t}, {LSE, s}});
   if (st != ATTN_OK) return st;
   return finish(fbd::launch_fwd((int)dt, Q, K, V, O, LSE, (int)(B * H), (int)H, (int)(H / Hkv),
-                                (int)N, causal ? 1 : 0, scale, (hipStream_t)stream));
+                                win, (int)N, causal ? 1 : 0, scale, (hipStream_t)stream));
 }
 
 attn_status attn_fwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
                      const void* K, const void* V, int causal, float scale, void* O, float* LSE,
                      void* stream) {
-  return attn_fwd_gqa(dt, B, H, H, N, d, Q, K, V, causal, scale, O, LSE, stream);
+  return attn_fwd_ex(dt, B, H, H, N, d, Q, K, V, causal, 0, scale, O, LSE, stream);
 }
 
 static attn_status bwd_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t Hkv,
                             int64_t N, int64_t d, const void* Q, const void* K, const void* V,
                             const void* O, const float* LSE, const void* dO, int causal,
-                            float scale, int gproj, void* dQ, void* dK, void* dV, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            int64_t window, float scale, int gproj, void* dQ, void* dK, void* dV,
+                            void* ws, size_t ws_bytes, void* stream) {
   if (passes < 1 || passes > 3) return ATTN_EINVAL;
   attn_status st = check_shape(dt, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
+  int win = 0;
+  if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
   const size_t need = attn_bwd_workspace_bytes(B, H, N);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
   const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
@@ -159,8 +173,8 @@ static attn_status bwd_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   float* Rws = Dws + bhn;
   float* Lws = Rws + bhn;
   return finish(fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws,
-                                (int)(B * H), (int)H, (int)(H / Hkv), (int)N, causal ? 1 : 0, scale,
-                                gproj ? 1 : 0, passes, (hipStream_t)stream));
+                                (int)(B * H), (int)H, (int)(H / Hkv), win, (int)N, causal ? 1 : 0,
+                                scale, gproj ? 1 : 0, passes, (hipStream_t)stream));
 }
 
 attn_status attn_bwd_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -168,16 +182,17 @@ attn_status attn_bwd_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             const float* LSE, const void* dO, int causal, float scale, int gproj,
                             void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                             void* stream) {
-  return bwd_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, causal, scale, gproj, dQ, dK,
-                  dV, ws, ws_bytes, stream);
+  return bwd_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, causal, 0, scale, gproj, dQ,
+                  dK, dV, ws, ws_bytes, stream);
 }
 
-attn_status attn_bwd_gqa(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* Q, const void* K, const void* V, const void* O,
-                         const float* LSE, const void* dO, int causal, float scale, int gproj,
-                         void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
-  return bwd_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, causal, scale, gproj, dQ, dK, dV,
-                  ws, ws_bytes, stream);
+attn_status attn_bwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V, const void* O,
+                        const float* LSE, const void* dO, int causal, int64_t window, float scale,
+                        int gproj, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return bwd_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, causal, window, scale, gproj, dQ,
+                  dK, dV, ws, ws_bytes, stream);
 }
 
 attn_status attn_bwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
@@ -191,13 +206,15 @@ attn_status attn_bwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
 static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t Hkv,
                             int64_t N, int64_t d, const void* Q, const void* K, const void* V,
                             const void* O, const float* LSE, const void* dO, const void* g_dQ,
-                            const void* g_dK, const void* g_dV, int causal, float scale, void* g_Q,
-                            void* g_K, void* g_V, void* g_dO, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            const void* g_dK, const void* g_dV, int causal, int64_t window,
+                            float scale, void* g_Q, void* g_K, void* g_V, void* g_dO, void* ws,
+                            size_t ws_bytes, void* stream) {
   if (passes < 1 || passes > 3) return ATTN_EINVAL;
   attn_status st = check_shape(dt, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
+  int win = 0;
+  if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
   const size_t need = attn_bob_workspace_bytes(B, H, N);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
   const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
@@ -214,7 +231,7 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   float* Kws = Lws + bhn;
   return finish(fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, g_Q, g_K, g_V,
                                 g_dO, Dws, Aws, Bws, Lws, Kws, (int)(B * H), (int)H,
-                                (int)(H / Hkv), (int)N, causal ? 1 : 0, scale, passes,
+                                (int)(H / Hkv), win, (int)N, causal ? 1 : 0, scale, passes,
                                 (hipStream_t)stream));
 }
 
@@ -223,17 +240,18 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             const float* LSE, const void* dO, const void* g_dQ, const void* g_dK,
                             const void* g_dV, int causal, float scale, void* g_Q, void* g_K,
                             void* g_V, void* g_dO, void* ws, size_t ws_bytes, void* stream) {
-  return bob_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, scale,
-                  g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
+  return bob_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, 0,
+                  scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
-attn_status attn_bob_gqa(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* Q, const void* K, const void* V, const void* O,
-                         const float* LSE, const void* dO, const void* g_dQ, const void* g_dK,
-                         const void* g_dV, int causal, float scale, void* g_Q, void* g_K,
-                         void* g_V, void* g_dO, void* ws, size_t ws_bytes, void* stream) {
-  return bob_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, scale,
-                  g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
+attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V, const void* O,
+                        const float* LSE, const void* dO, const void* g_dQ, const void* g_dK,
+                        const void* g_dV, int causal, int64_t window, float scale, void* g_Q,
+                        void* g_K, void* g_V, void* g_dO, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return bob_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, window,
+                  scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
 attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
@@ -275,15 +293,15 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
   const hipStream_t hs = (hipStream_t)stream;
   const size_t bhn = (size_t)B * H * N;
   float* w0 = static_cast<float*>(ws);
-  const int h = (int)H;
-  hipError_t e = fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, 1, n, c, scale, hs);
+  const int h = (int)H, nw = kNoWindow;
+  hipError_t e = fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, 1, nw, n, c, scale, hs);
   if (e == hipSuccess && ngrad == 3)
     e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, w0, w0 + bhn, w0 + 2 * bhn, bh,
-                        h, 1, n, c, scale, gproj ? 1 : 0, 3, hs);
+                        h, 1, nw, n, c, scale, gproj ? 1 : 0, 3, hs);
   if (e == hipSuccess)
     e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, w0,
-                        w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, h, 1, n, c, scale,
-                        3, hs);
+                        w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, h, 1, nw, n, c,
+                        scale, 3, hs);
   return finish(e);
 }
 

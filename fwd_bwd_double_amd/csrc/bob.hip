@@ -48,7 +48,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
     float* __restrict__ Bws, float* __restrict__ Lws, float* __restrict__ Kws, int N, int BH,
-    int H, int grp, int nblk, float scale) {
+    int H, int grp, int win, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   struct Buf {
@@ -89,8 +89,10 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
   float alpha = 0.f, xsum = 0.f;
 
+  // keys of the block's rows: causal j <= i, within the window j > i - win
+  const int jbeg = CAUSAL ? max(0, q0 - win + 1) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
-  const int ntiles = (jend + BN - 1) / BN;
+  const int ntiles = (jend - jbeg + BN - 1) / BN;
   auto stage = [&](int j0, Buf& bf) {
     dma_tile<T, BN, NT / 64>(rk, j0, bf.k, wave, lane);
     dma_tile<T, BN, NT / 64>(rv, j0, bf.v, wave, lane);
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     dma_tile<T, BN, NT / 64>(rc, j0, bf.c, wave, lane);
   };
   auto tile = [&](int t, const Buf& cb, Buf& nb) {
-    const int j0 = t * BN;
+    const int j0 = jbeg + t * BN;
     wait_dma();
     __syncthreads();   // tile t is in cb; every wave is done with nb
     if (t + 1 < ntiles) stage(j0 + BN, nb);
@@ -123,11 +125,11 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
       float xs[16], ps[16], zs[16], es[16], fs[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) ps[v] = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
-      if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
+      if (CAUSAL ? (js + 31 > qw || js <= qw + 31 - win) : (js + 32 > N)) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          ps[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? 0.f : ps[v];
+          ps[v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? 0.f : ps[v];
         }
       }
 #pragma unroll
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
       }
     }
   };
-  stage(0, B0);
+  stage(jbeg, B0);
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, B0, B1);
     if (t + 1 < ntiles) tile(t + 1, B1, B0);
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const float* __restrict__ Lws, const T* __restrict__ dO, const T* __restrict__ A,
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
     const float* __restrict__ Aws, const float* __restrict__ Kws, T* __restrict__ gK,
-    T* __restrict__ gV, int N, int BH, int H, int grp, float scale) {
+    T* __restrict__ gV, int N, int BH, int H, int grp, int win, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, kappa of the tile's rows
@@ -247,7 +249,9 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   f32x16 gk0 = zero16(), gk1 = zero16(), gv0 = zero16(), gv1 = zero16();
 
   const int istart = CAUSAL ? k0 : 0;
-  const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
+  // queries of the block's keys: causal i >= j, within the window i < j + win
+  const int iend = CAUSAL ? min(N, k0 + BLK - 1 + win) : N;
+  const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
   const int nsteps = ntiles * grp;      // (query head, query tile) steps
   // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
   auto stage = [&](int u, Buf& b) {
@@ -298,11 +302,11 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
           for (int r = 0; r < 4; ++r)
             ps[4 * q + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * q + r], sl2, l4[r]));
         }
-        if ((CAUSAL && is <= kw) || is + 32 > N) {
+        if ((CAUSAL && (is <= kw || is + 31 >= kw + win)) || is + 32 > N) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
-            ps[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : ps[v];
+            ps[v] = ((CAUSAL && (my_j > i || i >= my_j + win)) || i >= N) ? 0.f : ps[v];
           }
         }
       }
@@ -397,7 +401,8 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
                                float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
-                               int H, int grp, int N, float scale, int passes, hipStream_t st) {
+                               int H, int grp, int win, int N, float scale, int passes,
+                               hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
@@ -405,7 +410,7 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
     hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
                        (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws,
-                       Lws, Kws, N, BH, H, grp, nblk, scale);
+                       Lws, Kws, N, BH, H, grp, win, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -413,7 +418,8 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
   hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL>), dim3(nblk * (BH / grp)), dim3(NT), 0, st,
                      (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO,
                      (const T*)gdQ, (const T*)gdK, (const T*)gdV, (const float*)Dws,
-                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, scale);
+                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, win,
+                     scale);
   return hipGetLastError();
 }
 
@@ -421,9 +427,9 @@ hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
-                      int N, int causal, float scale, int passes, hipStream_t st) {
+                      int win, int N, int causal, float scale, int passes, hipStream_t st) {
 #define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, Lws, Kws, \
-                     BH, H, grp, N, scale, passes, st
+                     BH, H, grp, win, N, scale, passes, st
   if (dt == 0)
     return causal ? launch_bob_t<bf16, true>(FBD_BOB_ARGS) : launch_bob_t<bf16, false>(FBD_BOB_ARGS);
   return causal ? launch_bob_t<float, true>(FBD_BOB_ARGS) : launch_bob_t<float, false>(FBD_BOB_ARGS);

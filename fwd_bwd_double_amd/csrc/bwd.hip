@@ -32,7 +32,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, float* __restrict__ Lws,
-    int N, int BH, int H, int grp, int nblk, float scale) {
+    int N, int BH, int H, int grp, int win, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   __shared__ __attribute__((aligned(16))) T K0[BN * HD];
@@ -69,10 +69,12 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   f32x16 pk0 = zero16(), pk1 = zero16();
   float r = 0.f;
 
+  // keys of the block's rows: causal j <= i, within the window j > i - win
+  const int jbeg = CAUSAL ? max(0, q0 - win + 1) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
-  const int ntiles = (jend + BN - 1) / BN;
+  const int ntiles = (jend - jbeg + BN - 1) / BN;
   auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
-    const int j0 = t * BN;
+    const int j0 = jbeg + t * BN;
     wait_dma();
     __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
     if (t + 1 < ntiles) {
@@ -92,11 +94,11 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
         for (int kb = 0; kb < 4; ++kb) mma(sacc, ld_row(Ks, jb, kb, lane), qf[kb]);
 #pragma unroll
         for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - lse2);
-        if (CAUSAL ? (js + 31 > qw) : (js + 32 > N)) {
+        if (CAUSAL ? (js + 31 > qw || js <= qw + 31 - win) : (js + 32 > N)) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-            p[v] = (CAUSAL ? (j > my_i) : (j >= N)) ? 0.f : p[v];
+            p[v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? 0.f : p[v];
           }
         }
       }
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
       }
     }
   };
-  dma_tile<T, BN, NT / 64>(rk, 0, K0, wave, lane);
-  dma_tile<T, BN, NT / 64>(rv, 0, V0, wave, lane);
+  dma_tile<T, BN, NT / 64>(rk, jbeg, K0, wave, lane);
+  dma_tile<T, BN, NT / 64>(rv, jbeg, V0, wave, lane);
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, K0, V0, K1, V1);
     if (t + 1 < ntiles) tile(t + 1, K1, V1, K0, V0);
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int H,
-    int grp, float scale) {
+    int grp, int win, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q and dO tiles and the -LSE*log2(e), D (, r) of the tile's rows
@@ -192,7 +194,9 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
 
   const int istart = CAUSAL ? k0 : 0;   // k0 is a multiple of BM
-  const int ntiles = N > istart ? (N - istart + BM - 1) / BM : 0;
+  // queries of the block's keys: causal i >= j, within the window i < j + win
+  const int iend = CAUSAL ? min(N, k0 + BLK - 1 + win) : N;
+  const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
   const int nsteps = ntiles * grp;      // (query head, query tile) steps
   // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
   auto stage = [&](int u, Buf& b) {
@@ -239,11 +243,11 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
           for (int u = 0; u < 4; ++u)
             p[4 * q + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * q + u], sl2, l4[u]));
         }
-        if ((CAUSAL && is <= kw) || is + 32 > N) {
+        if ((CAUSAL && (is <= kw || is + 31 >= kw + win)) || is + 32 > N) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
-            p[v] = ((CAUSAL && my_j > i) || i >= N) ? 0.f : p[v];
+            p[v] = ((CAUSAL && (my_j > i || i >= my_j + win)) || i >= N) ? 0.f : p[v];
           }
         }
       }
@@ -314,14 +318,14 @@ template <class T, bool GPROJ, bool CAUSAL>
 static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
                                float* Dws, float* Rws, float* Lws, int BH, int H, int grp,
-                               int N, float scale, int passes, hipStream_t st) {
+                               int win, int N, float scale, int passes, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
     hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
-                       (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, nblk, scale);
+                       (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, win, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -329,7 +333,7 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
   hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL>), dim3(nblk * (BH / grp)), dim3(NT),
                      0, st, (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws,
                      (const T*)dO, (const float*)Dws, (const float*)Rws, (T*)dK, (T*)dV, N, BH, H,
-                     grp, scale);
+                     grp, win, scale);
   return hipGetLastError();
 }
 
@@ -337,24 +341,25 @@ template <class T, bool GPROJ>
 static hipError_t launch_bwd_c(int causal, const void* Q, const void* K, const void* V,
                                const void* O, const float* LSE, const void* dO, void* dQ,
                                void* dK, void* dV, float* Dws, float* Rws, float* Lws, int BH,
-                               int H, int grp, int N, float scale, int passes, hipStream_t st) {
+                               int H, int grp, int win, int N, float scale, int passes,
+                               hipStream_t st) {
   if (causal)
-    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
-  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
+    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
+  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
 }
 
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
-                      float* Rws, float* Lws, int BH, int H, int grp, int N, int causal,
-                      float scale, int gproj, int passes, hipStream_t st) {
+                      float* Rws, float* Lws, int BH, int H, int grp, int win, int N,
+                      int causal, float scale, int gproj, int passes, hipStream_t st) {
   if (dt == 0) {
     if (gproj)
-      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
-    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
+      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
+    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
   }
   if (gproj)
-    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
-  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, N, scale, passes, st);
+    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
+  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
 }
 
 }  // namespace fbd

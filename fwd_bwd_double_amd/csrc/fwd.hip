@@ -41,7 +41,8 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,
-                                                     int H, int grp, int nblk, float scale) {
+                                                     int H, int grp, int win, int nblk,
+                                                     float scale) {
   // two buffers as separate objects, used in a loop unrolled by two, so the
   // compiler can tell the copy of the next tile never aliases the reads of
   // the current one (and places no wait between them)
@@ -66,26 +67,33 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
   // output accumulator o.  The score products of a tile start from -m in the
   // MFMA accumulator (negm), so they arrive as x = S - m: the max is
   // subtracted without a VALU op.  The max, and with it the rescale of o and
-  // l, is updated once per key tile.
+  // l, is updated once per key tile.  `seen` marks rows that have met a
+  // visible key (until then m is a placeholder 0 and nothing is
+  // accumulated): with a sliding window a row's first visible key can lie
+  // beyond the block's first tile.
   Frag<T> qf[FWD_G][4];
   float m[FWD_G], l[FWD_G];
+  bool seen[FWD_G];
   f32x16 o[FWD_G][2], negm[FWD_G];
 #pragma unroll
   for (int g = 0; g < FWD_G; ++g) {
     ld_frags(Q + hoff, N, qw + g * WROWS, lane, qf[g]);
     m[g] = 0.f;
     l[g] = 0.f;
+    seen[g] = false;
     o[g][0] = zero16();
     o[g][1] = zero16();
     negm[g] = zero16();
   }
 
+  // keys of the block's rows: causal j <= i, within the window j > i - win
+  const int jbeg = CAUSAL ? max(0, q0 - win + 1) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
-  const int ntiles = (jend + BN - 1) / BN;
+  const int ntiles = (jend - jbeg + BN - 1) / BN;
   constexpr int NS = BN / 32;   // 32-key sub-blocks per tile
 
   auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
-    const int j0 = t * BN;
+    const int j0 = jbeg + t * BN;
     wait_dma();
     __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
     if (t + 1 < ntiles) {
@@ -121,11 +129,12 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
       for (int sb = 0; sb < NS; ++sb) {
         const int js = j0 + sb * 32;
-        if (CAUSAL ? (js + 31 > qg) : (js + 32 > N)) {
+        if (CAUSAL ? (js + 31 > qg || js <= qg + 31 - win) : (js + 32 > N)) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-            x[sb][g][v] = (CAUSAL ? (j > my_i) : (j >= N)) ? -INFINITY : x[sb][g][v];
+            x[sb][g][v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? -INFINITY
+                                                                             : x[sb][g][v];
           }
         }
       }
@@ -134,19 +143,20 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
       for (int sb = 0; sb < NS; ++sb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) xm = fmaxf(xm, x[sb][g][v]);
-      xm = half_max(xm);   // key 0 is visible to every row: finite on the first tile
-      base[g] = 0.f;
-      if (t == 0) {
-        m[g] = xm;
-        base[g] = xm;
-      } else if (__any(xm > 0.f)) {
-        base[g] = fmaxf(xm, 0.f);
-        const float alpha = __builtin_amdgcn_exp2f(-base[g] * sl2);
+      xm = half_max(xm);
+      // a row meeting its first visible key takes that tile's max as m (x is
+      // the raw score there); a row already seen subtracts the growth of its
+      // max and rescales; a row with no visible key yet keeps everything zero
+      const bool fresh = !seen[g] && xm > -INFINITY;
+      base[g] = seen[g] ? fmaxf(xm, 0.f) : (fresh ? xm : 0.f);
+      if (__any(seen[g] && xm > 0.f)) {
+        const float alpha = seen[g] ? __builtin_amdgcn_exp2f(-base[g] * sl2) : 1.f;
         l[g] *= alpha;
         o[g][0] *= alpha;
         o[g][1] *= alpha;
-        m[g] += base[g];
       }
+      m[g] += base[g];
+      seen[g] = seen[g] || fresh;
       sub[g] = __any(base[g] != 0.f);
     }
 #pragma unroll
@@ -183,8 +193,8 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
       negm[g] = zero16() - m[g];
     }
   };
-  dma_tile<T, BN, FWD_WAVES>(rk, 0, K0, wave, lane);
-  dma_tile<T, BN, FWD_WAVES>(rv, 0, V0, wave, lane);
+  dma_tile<T, BN, FWD_WAVES>(rk, jbeg, K0, wave, lane);
+  dma_tile<T, BN, FWD_WAVES>(rv, jbeg, V0, wave, lane);
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, K0, V0, K1, V1);
     if (t + 1 < ntiles) tile(t + 1, K1, V1, K0, V0);
@@ -209,23 +219,25 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 
 template <class T, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               int BH, int H, int grp, int N, float scale, hipStream_t st) {
+                               int BH, int H, int grp, int win, int N, float scale,
+                               hipStream_t st) {
   constexpr int BN = sizeof(T) == 2 ? FBD_FWD_BN : 64;
   const int nblk = (N + FWD_BLK - 1) / FWD_BLK;
   hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
-                     (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, nblk,
-                     scale);
+                     (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, win,
+                     nblk, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int BH, int H, int grp, int N, int causal, float scale, hipStream_t st) {
+                      int BH, int H, int grp, int win, int N, int causal, float scale,
+                      hipStream_t st) {
   if (dt == 0) {
-    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
-    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
+    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
+    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
   }
-  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
-  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, H, grp, N, scale, st);
+  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
+  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
 }
 
 }  // namespace fbd

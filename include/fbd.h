@@ -168,41 +168,50 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Grouped-query and multi-query attention: the same operations with K and V
- * (and their gradients and cotangents) shared by groups of query heads.  The
- * FlashBoB page (rit.work, flashbob-second-order-attention) names shared keys
- * and values among the extensions after plain multi-head attention, in its
- * closing paragraph on where the method applies.  Hkv key/value heads serve H
- * query heads (1 <= Hkv <= H, H % Hkv == 0): query head h of a batch uses key
- * head h / (H / Hkv).  Query-side tensors (Q, O, dO, dQ, g_dQ, g_Q, g_dO),
- * LSE and the workspace have H heads; key-side tensors (K, V, dK, dV, g_dK,
- * g_dV, g_K, g_V) are (B, Hkv, N, d).  The key-side gradients are the sums
- * over each group's query heads; the column passes stream every query head
- * of a group past the resident key block, so each key-side block is still
- * written once.  Hkv == H is multi-head attention, identical to attn_fwd /
- * attn_bwd / attn_bob; Hkv == 1 is multi-query attention.  An Hkv outside
- * that range is ATTN_EINVAL; other arguments and errors as for the
- * multi-head entry points (workspace sizes count the H query heads).
+ * Extended forms: shared keys and values, and a sliding window.  The FlashBoB
+ * page (rit.work, flashbob-second-order-attention), in its closing paragraph
+ * on where the method applies, names shared keys and values and flexible
+ * masks among the extensions after plain multi-head attention.
+ *
+ * Shared keys and values (grouped-query / multi-query attention): Hkv
+ * key/value heads serve H query heads (1 <= Hkv <= H, H % Hkv == 0); query
+ * head h of a batch uses key head h / (H / Hkv).  Query-side tensors (Q, O,
+ * dO, dQ, g_dQ, g_Q, g_dO), LSE and the workspace have H heads; key-side
+ * tensors (K, V, dK, dV, g_dK, g_dV, g_K, g_V) are (B, Hkv, N, d).  The
+ * key-side gradients are sums over each group's query heads: the column
+ * passes stream every query head of a group past the resident key block, so
+ * each key-side block is still written once.  Hkv == H is multi-head
+ * attention; Hkv == 1 is multi-query attention.
+ *
+ * Sliding window (window > 0, causal only): key j is visible to query i iff
+ * i - window < j <= i.  Tiles wholly outside the window are never loaded.
+ * window == 0 is plain causal (or full, with causal == 0) attention.
+ *
+ * With Hkv == H and window == 0 these equal attn_fwd / attn_bwd / attn_bob.
+ * Hkv outside the range above or window < 0 is ATTN_EINVAL; window > 0 with
+ * causal == 0 is ATTN_EUNSUPPORTED; other arguments and errors as for the
+ * multi-head entry points (workspace sizes count the H query heads).  The
+ * backward and BoB must get the same causal and window as the forward.
  */
-attn_status attn_fwd_gqa(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* Q, const void* K, const void* V,
-                         int causal, float scale,
-                         void* O, float* LSE, void* stream);
+attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V,
+                        int causal, int64_t window, float scale,
+                        void* O, float* LSE, void* stream);
 
-attn_status attn_bwd_gqa(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* Q, const void* K, const void* V, const void* O,
-                         const float* LSE, const void* dO,
-                         int causal, float scale, int gproj,
-                         void* dQ, void* dK, void* dV,
-                         void* ws, size_t ws_bytes, void* stream);
+attn_status attn_bwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V, const void* O,
+                        const float* LSE, const void* dO,
+                        int causal, int64_t window, float scale, int gproj,
+                        void* dQ, void* dK, void* dV,
+                        void* ws, size_t ws_bytes, void* stream);
 
-attn_status attn_bob_gqa(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* Q, const void* K, const void* V, const void* O,
-                         const float* LSE, const void* dO,
-                         const void* g_dQ, const void* g_dK, const void* g_dV,
-                         int causal, float scale,
-                         void* g_Q, void* g_K, void* g_V, void* g_dO,
-                         void* ws, size_t ws_bytes, void* stream);
+attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V, const void* O,
+                        const float* LSE, const void* dO,
+                        const void* g_dQ, const void* g_dK, const void* g_dV,
+                        int causal, int64_t window, float scale,
+                        void* g_Q, void* g_K, void* g_V, void* g_dO,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Hessian-vector product of one attention layer, the product that

@@ -83,21 +83,53 @@ def test_ragged_shapes(B, H, N, causal, dtype):
             check(k, r[k], ref[k], t1)
         for k in ("gQ", "gK", "gV", "gdO"):
             if N == 1 and k != "gdO":
-                # A single token has exact gQ = gK = gV = 0.  The row pass forms
-                # gQ as scale*(X - alpha Z - beta Y + E) from bf16-rounded
-                # operands, which cancel exactly only in exact arithmetic; the
-                # residual is bounded by the operand rounding (2^-8 relative)
-                # times scale*|K|*(|W dP| + |W D| + |U|).
-                c = w.scale
-                Wv = c * (np.sum(a["g_dq"] * a["k"], -1) + np.sum(a["q"] * a["g_dk"], -1))
-                dPv = np.sum(a["do"] * a["v"], -1)
-                Uv = np.sum(a["do"] * a["g_dv"], -1)
-                mag = np.abs(Wv * dPv) * 2 + np.abs(Uv)
-                bound = 2.0 ** -7 * c * np.linalg.norm(a["k"], axis=-1) * mag
-                eps = 2.0 ** -16 if dtype == "fp32" else 1.0   # fp32 vs bf16 ulp
-                assert np.all(np.linalg.norm(r[k], axis=-1) <= eps * bound), k
+                check_single_key_zero(k, r[k], a, w.scale, dtype)
                 continue
             check(k, r[k], ref[k], t2)
+
+
+def check_single_key_zero(name, got, a, c, dtype, kv=None):
+    """Rows that see exactly one key (N = 1, or a window of 1) have exact gQ =
+    gK = gV = 0.  The kernels reach zero by cancellation of rounded terms:
+      gQ, gK: the row pass forms gQ as scale*(X - alpha Z - beta Y + E) from
+        bf16-rounded operands; the residual is bounded by the operand rounding
+        (2^-8 relative in bf16; for fp32 the 64-term dot products, 2^-24 * 2^6,
+        combined a few times) times scale*|K|*(|W dP| + |W D| + |U|);
+      gV: H = P o (W - alpha) with alpha = W computed in the other pass, whose
+        W differs only in fp32 accumulation order: residual 2^-16 relative to
+        scale*sum|dQbar K| + scale*sum|Q dKbar|, times |dO|.
+    kv maps a query head to its key head (grouped-query inputs)."""
+    k, gdk, v, gdv = (a[n] if kv is None else a[n][:, kv] for n in ("k", "g_dk", "v", "g_dv"))
+    if name == "gV":
+        magw = c * (np.sum(np.abs(a["g_dq"] * k), -1) + np.sum(np.abs(a["q"] * gdk), -1))
+        bound = 2.0 ** -16 * magw * np.linalg.norm(a["do"], axis=-1)
+    else:
+        Wv = c * (np.sum(a["g_dq"] * k, -1) + np.sum(a["q"] * gdk, -1))
+        dPv = np.sum(a["do"] * v, -1)
+        Uv = np.sum(a["do"] * gdv, -1)
+        mag = np.abs(Wv * dPv) * 2 + np.abs(Uv)
+        eps = 2.0 ** -11 if dtype == "fp32" else 1.0
+        bound = eps * 2.0 ** -7 * c * np.linalg.norm(k, axis=-1) * mag
+    if got.shape[1] != bound.shape[1]:            # key-side output: sum over its group
+        g = bound.shape[1] // got.shape[1]
+        bound = bound.reshape(bound.shape[0], -1, g, bound.shape[2]).sum(axis=2)
+    e = np.linalg.norm(got, axis=-1)
+    say(f"    {name}: max |row| {e.max():.3e} (exact 0; bound {float(bound.max()):.3e})")
+    assert np.all(e <= bound + 1e-30), name
+
+
+def check_zero_grad(name, got, a, c, kv=None):
+    """With one visible key per row dS = dP - D vanishes exactly: D = dO.O and
+    O is that key's V, so only the fp32 accumulation order of the two dot
+    products differs; bound: 2^-16 scale |K| sum|dO V|."""
+    k, v = (a[n] if kv is None else a[n][:, kv] for n in ("k", "v"))
+    bound = 2.0 ** -16 * c * np.linalg.norm(k, axis=-1) * np.sum(np.abs(a["do"] * v), -1)
+    if got.shape[1] != bound.shape[1]:
+        g = bound.shape[1] // got.shape[1]
+        bound = bound.reshape(bound.shape[0], -1, g, bound.shape[2]).sum(axis=2)
+    e = np.linalg.norm(got, axis=-1)
+    say(f"    {name}: max |row| {e.max():.3e} (exact 0; bound {float(bound.max()):.3e})")
+    assert np.all(e <= bound + 1e-30), name
 
 
 def test_bitwise_deterministic():
@@ -294,3 +326,43 @@ def test_grouped_query(H, Hkv, N, causal, dtype):
             check(k, f64(t), ref[k], t1)
         for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
             check(k, f64(t), ref[k], t2)
+
+
+# ------------------------------------------------- causal sliding window
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("N,window,H,Hkv", [(300, 1, 2, 2), (300, 17, 2, 2), (1000, 64, 2, 2),
+                                            (1000, 129, 4, 2), (333, 100, 3, 1),
+                                            (2048, 256, 2, 2)])
+def test_sliding_window(N, window, H, Hkv, dtype):
+    import fwd_bwd_double_amd as fbd
+    w = synthetic.Workload(f"win-{dtype}", 1, H, N, 64, dtype, 9100 + N + window, causal=True,
+                           qkv_std=1.0)
+    x, g, a = inputs(w)
+    for n in ("k", "v", "g_dk", "g_dv"):
+        g[n] = g[n][:, :Hkv].contiguous()
+        a[n] = a[n][:, :Hkv]
+    say(f"[gpu] window={window} B=1 H={H} Hkv={Hkv} N={N} dtype={dtype}")
+    o, lse = fbd.attn_fwd(g["q"], g["k"], g["v"], scale=w.scale, window=window)
+    t1, t2 = (1e-5, 1e-5) if dtype == "fp32" else (2e-2, 5e-2)
+    ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                         with_bwd=True, window=window)
+    f64 = synthetic.to_f64
+    for gproj in (False, True):
+        dq, dk, dv = fbd.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale,
+                                  gproj=gproj, window=window)
+        gq, gk, gv, gdo = fbd.attn_bob(g["q"], g["k"], g["v"], o, lse, g["do"], g["g_dq"],
+                                       g["g_dk"], g["g_dv"], scale=w.scale, window=window)
+        torch.cuda.synchronize()
+        check("O", f64(o), ref["O"], t1)
+        check("LSE", f64(lse), ref["LSE"], t1)
+        kv = np.arange(H) // (H // Hkv)
+        for k, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            if window == 1 and k != "dV":
+                check_zero_grad(k, f64(t), a, w.scale, kv)
+            else:
+                check(k, f64(t), ref[k], t1)
+        for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
+            if window == 1 and k != "gdO":
+                check_single_key_zero(k, f64(t), a, w.scale, dtype, kv)
+            else:
+                check(k, f64(t), ref[k], t2)

@@ -133,6 +133,47 @@ def test_grouped_query_against_torch_double_backward(H, Hkv):
     assert np.linalg.norm(b["dK"] - r["dK"]) <= 1e-13 * np.linalg.norm(b["dK"])
 
 
+@pytest.mark.parametrize("window", [1, 3, 7])
+def test_sliding_window_against_torch_double_backward(window):
+    # a causal sliding window as an explicit boolean mask in torch (fp64
+    # autograd, double backward), independent of the oracle's _visible
+    Q, K, V, dO, A, Bk, C = inputs(1, 2, 15, 8, 137)
+    c = 1 / math.sqrt(8)
+    n = 15
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    hide = (j > i) | (j <= i - window)
+    tq, tk, tv, tdo = (torch.tensor(x, requires_grad=True) for x in (Q, K, V, dO))
+    s_ = (c * (tq @ tk.transpose(-1, -2))).masked_fill(hide, float("-inf"))
+    out = torch.softmax(s_, dim=-1) @ tv
+    gq, gk, gv = torch.autograd.grad(out, (tq, tk, tv), tdo, create_graph=True)
+    phi_ = (gq * torch.from_numpy(A)).sum() + (gk * torch.from_numpy(Bk)).sum() + \
+        (gv * torch.from_numpy(C)).sum()
+    hq, hk, hv, hdo = torch.autograd.grad(phi_, (tq, tk, tv, tdo))
+    r = oracle.bob(Q, K, V, dO, A, Bk, C, with_bwd=True, window=window)
+    o, _ = oracle.fwd(Q, K, V, window=window)
+    assert np.linalg.norm(o - out.detach().numpy()) <= 1e-12 * np.linalg.norm(o)
+    for mine, ref in ((r["dQ"], gq), (r["dK"], gk), (r["dV"], gv), (r["gQ"], hq),
+                      (r["gK"], hk), (r["gV"], hv), (r["gdO"], hdo)):
+        ref = ref.detach().numpy()
+        assert np.linalg.norm(mine - ref) <= 1e-12 * max(1.0, np.linalg.norm(ref))
+
+
+def test_window_of_one_closed_form_and_wide_window_is_causal():
+    Q, K, V, dO, A, Bk, C = inputs(1, 1, 9, 4, 138)
+    c = 0.5
+    r = oracle.bwd(Q, K, V, dO, scale=c, window=1)
+    # each row sees only its own key: O = V, LSE = c q.k, dS = 0, dV = dO
+    assert np.allclose(r["O"], V, atol=1e-15)
+    assert np.allclose(r["LSE"], c * np.einsum("bhnd,bhnd->bhn", Q, K), atol=1e-14)
+    assert np.abs(r["dQ"]).max() < 1e-14 and np.abs(r["dK"]).max() < 1e-14
+    assert np.allclose(r["dV"], dO, atol=1e-15)
+    full = oracle.bob(Q, K, V, dO, A, Bk, C, with_bwd=True)
+    wide = oracle.bob(Q, K, V, dO, A, Bk, C, with_bwd=True, window=9)
+    for k in full:
+        assert np.array_equal(full[k], wide[k]), k
+
+
 # ---------------------------------------------------------------- BoB
 def phi(Q, K, V, dO, A, Bk, C, causal=True):
     g = oracle.bwd(Q, K, V, dO, causal=causal)
