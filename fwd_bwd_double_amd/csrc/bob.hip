@@ -39,6 +39,8 @@
 #include "launch.hpp"
 #include "tile.hpp"
 
+#include <type_traits>
+
 namespace fbd {
 
 template <class T, int BN, bool CAUSAL>
@@ -108,6 +110,87 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* Vs = cb.v;
     const T* Bs = cb.b;
     const T* Cs = cb.c;
+#if FBD_BOB_ROW_SPLIT
+#pragma unroll
+    for (int jb = 0; jb < BN; jb += 32) {
+      const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
+      // one straight-line body per case, so the scheduler can interleave the
+      // whole sub-block's matrix and vector work
+      auto sub = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const Frag<T> kr = ld_row(Ks, jb, kb, lane);
+        mma(s, kr, qf[kb]);
+        mma(w, kr, af[kb]);
+        mma(w, ld_row(Bs, jb, kb, lane), qf[kb]);
+        const Frag<T> vr = ld_row(Vs, jb, kb, lane);
+        mma(dp, vr, dof[kb]);
+        mma(u, ld_row(Cs, jb, kb, lane), dof[kb]);
+      }
+      float xs[16], ps[16], zs[16], es[16], fs[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ps[v] = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
+      if constexpr (MASK) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
+          ps[v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? 0.f : ps[v];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = ps[v];
+        const float W = scale * w[v];
+        const float dpd = dp[v] - Di;
+        const float pw = pv * W;
+        alpha += pw;
+        xs[v] = pv * (W * dpd + u[v]);
+        xsum += xs[v];
+        zs[v] = pv * dp[v];
+        es[v] = pv * dpd;
+        fs[v] = pw;
+      }
+      const int jt = jb / 16;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const Frag<T> xf = pack8<T>(xs + 8 * tt), pf = pack8<T>(ps + 8 * tt);
+        const Frag<T> zf = pack8<T>(zs + 8 * tt), ef = pack8<T>(es + 8 * tt);
+        const Frag<T> ff = pack8<T>(fs + 8 * tt);
+        {
+          const Frag<T> a0 = ld_tr(Ks, 0, jt + tt, lane), a1 = ld_tr(Ks, 32, jt + tt, lane);
+          mma(X0, a0, xf);
+          mma(X1, a1, xf);
+          mma(Y0, a0, pf);
+          mma(Y1, a1, pf);
+          mma(Z0, a0, zf);
+          mma(Z1, a1, zf);
+        }
+        {
+          const Frag<T> a0 = ld_tr(Bs, 0, jt + tt, lane), a1 = ld_tr(Bs, 32, jt + tt, lane);
+          mma(X0, a0, ef);
+          mma(X1, a1, ef);
+        }
+        {
+          const Frag<T> a0 = ld_tr(Vs, 0, jt + tt, lane), a1 = ld_tr(Vs, 32, jt + tt, lane);
+          mma(F0, a0, ff);
+          mma(F1, a1, ff);
+        }
+        {
+          const Frag<T> a0 = ld_tr(Cs, 0, jt + tt, lane), a1 = ld_tr(Cs, 32, jt + tt, lane);
+          mma(F0, a0, pf);
+          mma(F1, a1, pf);
+        }
+      }
+      };
+      if (CAUSAL ? (js + 31 > qw || js <= qw + 31 - win) : (js + 32 > N))
+        sub(std::true_type());
+      else
+        sub(std::false_type());
+    }
+  };
+#else
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
@@ -178,6 +261,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
       }
     }
   };
+#endif
   stage(jbeg, B0);
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, B0, B1);

@@ -39,6 +39,9 @@
 #ifndef FBD_BOB_ROW_OCC
 #define FBD_BOB_ROW_OCC 1
 #endif
+#ifndef FBD_BOB_ROW_SPLIT
+#define FBD_BOB_ROW_SPLIT 1
+#endif
 #ifndef FBD_BOB_COL_OCC
 #define FBD_BOB_COL_OCC 2
 #endif
