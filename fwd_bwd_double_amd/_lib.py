@@ -67,14 +67,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
     lib.attn_bob_passes.restype = i32
     # extended forms: Hkv after H, the window after causal
-    lib.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, f32, vp, vp,
-                                vp]
+    lib.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, vp, f32, vp,
+                                vp, vp]
     lib.attn_fwd_ex.restype = i32
     a = lib.attn_bwd.argtypes
-    lib.attn_bwd_ex.argtypes = a[:3] + [i64] + a[3:12] + [i64] + a[12:]
+    lib.attn_bwd_ex.argtypes = a[:3] + [i64] + a[3:12] + [i64, vp] + a[12:]
     lib.attn_bwd_ex.restype = i32
     a = lib.attn_bob.argtypes
-    lib.attn_bob_ex.argtypes = a[:3] + [i64] + a[3:15] + [i64] + a[15:]
+    lib.attn_bob_ex.argtypes = a[:3] + [i64] + a[3:15] + [i64, vp] + a[15:]
     lib.attn_bob_ex.restype = i32
     lib.attn_hvp_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_hvp_workspace_bytes.restype = sz
@@ -135,6 +135,15 @@ def _kv_shape(q: torch.Tensor, Hkv: int):
     return (B, Hkv, N, d)
 
 
+def _docs(q: torch.Tensor, doc_start) -> Optional[int]:
+    """Device pointer of a (B, N) int32 doc_start tensor, or None."""
+    if doc_start is None:
+        return None
+    B, _, N, _ = q.shape
+    _check("doc_start", doc_start, q, torch.int32, (B, N))
+    return doc_start.data_ptr()
+
+
 def _scale(q: torch.Tensor, scale: Optional[float]) -> float:
     return 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
 
@@ -153,10 +162,13 @@ def hvp_workspace_bytes(B: int, H: int, N: int) -> int:
 
 def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+             window: int = 0, doc_start: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor]:
     """O, LSE = attention(q, k, v); q shaped (B, H, N, d), k and v (B, Hkv, N, d)
     with H % Hkv == 0 (Hkv < H: grouped-query attention), bf16 or fp32.
-    window > 0 (causal only): query i sees keys i - window < j <= i."""
+    window > 0 (causal only): query i sees keys i - window < j <= i.
+    doc_start (causal only): (B, N) int32 first position of each query's
+    document (packed sequences; non-decreasing, doc_start[b, i] <= i)."""
     lib = load()
     _check("q", q, q)
     Hkv = _kv_heads(q, k)
@@ -168,15 +180,16 @@ def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
     _check("out", out, q)
     _check("lse", lse, q, torch.float32, (B, H, N))
     st = lib.attn_fwd_ex(_dt(q), B, H, Hkv, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                         1 if causal else 0, int(window), _scale(q, scale), out.data_ptr(),
-                         lse.data_ptr(), _stream(q.device))
+                         1 if causal else 0, int(window), _docs(q, doc_start), _scale(q, scale),
+                         out.data_ptr(), lse.data_ptr(), _stream(q.device))
     _raise("attn_fwd", st)
     return out, lse
 
 
 def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
              gproj: bool = False, workspace: Optional[torch.Tensor] = None, outs=None,
-             passes: int = 3, window: int = 0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             passes: int = 3, window: int = 0, doc_start: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV of <dO, O>.  `workspace` (fp32, >= bwd_workspace_bytes) holds
     the row states D, r and -LSE*log2(e), each B*H*N floats, afterwards.
     passes: 1 row pass, 2 column pass, 3 both."""
@@ -196,9 +209,9 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
     _check("dq", dq, q)
     for n, t in (("dk", dk), ("dv", dv)):
         _check(n, t, q, shape=kvs)
-    ext = Hkv != H or window != 0
+    ext = Hkv != H or window != 0 or doc_start is not None
     if ext and passes != 3:
-        raise ValueError("grouped-query or windowed backward runs both passes (passes=3)")
+        raise ValueError("grouped-query or masked backward runs both passes (passes=3)")
     need = lib.attn_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
@@ -211,7 +224,8 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
             workspace.data_ptr(), ws_bytes, _stream(q.device))
     c = 1 if causal else 0
     if ext:
-        st = lib.attn_bwd_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window), *rest)
+        st = lib.attn_bwd_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window),
+                             _docs(q, doc_start), *rest)
     else:
         st = lib.attn_bwd_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bwd", st)
@@ -220,7 +234,7 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
 
 def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
              scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, outs=None,
-             passes: int = 3, window: int = 0
+             passes: int = 3, window: int = 0, doc_start: Optional[torch.Tensor] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
@@ -243,9 +257,9 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
         _check(n, t, q)
     for n, t in (("g_k", gk), ("g_v", gv)):
         _check(n, t, q, shape=kvs)
-    ext = Hkv != H or window != 0
+    ext = Hkv != H or window != 0 or doc_start is not None
     if ext and passes != 3:
-        raise ValueError("grouped-query or windowed BoB runs both passes (passes=3)")
+        raise ValueError("grouped-query or masked BoB runs both passes (passes=3)")
     need = lib.attn_bob_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
@@ -258,7 +272,8 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
             workspace.data_ptr(), ws_bytes, _stream(q.device))
     c = 1 if causal else 0
     if ext:
-        st = lib.attn_bob_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window), *rest)
+        st = lib.attn_bob_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window),
+                             _docs(q, doc_start), *rest)
     else:
         st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bob", st)

@@ -43,14 +43,14 @@
 
 namespace fbd {
 
-template <class T, int BN, bool CAUSAL>
+template <class T, int BN, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
     float* __restrict__ Bws, float* __restrict__ Lws, float* __restrict__ Kws, int N, int BH,
-    int H, int grp, int win, int nblk, float scale) {
+    int H, int grp, int win, const int* __restrict__ DS, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   struct Buf {
@@ -91,8 +91,14 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
   float alpha = 0.f, xsum = 0.f;
 
-  // keys of the block's rows: causal j <= i, within the window j > i - win
-  const int jbeg = CAUSAL ? max(0, q0 - win + 1) / BN * BN : 0;
+  // keys of the block's rows: causal j <= i, from each row's start (sliding
+  // window, document); the block's first row has the smallest start
+  // (documents only: the window alone is a fixed offset from each row)
+  const int* ds = DOCS ? DS + (size_t)(wk.head / H) * N : nullptr;
+  const int rs = DOCS ? row_start(ds, my_i, win, N) : 0;              // this lane's row
+  const int rs_w = DOCS ? __builtin_amdgcn_readlane(rs, 31) : 0;      // the wave's largest
+  const int rs0 = DOCS ? row_start(ds, q0, win, N) : q0 - win + 1;
+  const int jbeg = CAUSAL ? min(max(0, rs0), q0) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend - jbeg + BN - 1) / BN;
   auto stage = [&](int j0, Buf& bf) {
@@ -110,7 +116,6 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* Vs = cb.v;
     const T* Bs = cb.b;
     const T* Cs = cb.c;
-#if FBD_BOB_ROW_SPLIT
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          ps[v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? 0.f : ps[v];
+          ps[v] = (CAUSAL ? (j > my_i || (DOCS ? j < rs : j <= my_i - win)) : (j >= N)) ? 0.f : ps[v];
         }
       }
 #pragma unroll
@@ -184,84 +189,12 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         }
       }
       };
-      if (CAUSAL ? (js + 31 > qw || js <= qw + 31 - win) : (js + 32 > N))
+      if (CAUSAL ? (js + 31 > qw || (DOCS ? js < rs_w : js <= qw + 31 - win)) : (js + 32 > N))
         sub(std::true_type());
       else
         sub(std::false_type());
     }
   };
-#else
-#pragma unroll
-    for (int jb = 0; jb < BN; jb += 32) {
-      const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
-      f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const Frag<T> kr = ld_row(Ks, jb, kb, lane);
-        mma(s, kr, qf[kb]);
-        mma(w, kr, af[kb]);
-        mma(w, ld_row(Bs, jb, kb, lane), qf[kb]);
-        const Frag<T> vr = ld_row(Vs, jb, kb, lane);
-        mma(dp, vr, dof[kb]);
-        mma(u, ld_row(Cs, jb, kb, lane), dof[kb]);
-      }
-      float xs[16], ps[16], zs[16], es[16], fs[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ps[v] = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
-      if (CAUSAL ? (js + 31 > qw || js <= qw + 31 - win) : (js + 32 > N)) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          ps[v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? 0.f : ps[v];
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = ps[v];
-        const float W = scale * w[v];
-        const float dpd = dp[v] - Di;
-        const float pw = pv * W;
-        alpha += pw;
-        xs[v] = pv * (W * dpd + u[v]);
-        xsum += xs[v];
-        zs[v] = pv * dp[v];
-        es[v] = pv * dpd;
-        fs[v] = pw;
-      }
-      const int jt = jb / 16;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const Frag<T> xf = pack8<T>(xs + 8 * tt), pf = pack8<T>(ps + 8 * tt);
-        const Frag<T> zf = pack8<T>(zs + 8 * tt), ef = pack8<T>(es + 8 * tt);
-        const Frag<T> ff = pack8<T>(fs + 8 * tt);
-        {
-          const Frag<T> a0 = ld_tr(Ks, 0, jt + tt, lane), a1 = ld_tr(Ks, 32, jt + tt, lane);
-          mma(X0, a0, xf);
-          mma(X1, a1, xf);
-          mma(Y0, a0, pf);
-          mma(Y1, a1, pf);
-          mma(Z0, a0, zf);
-          mma(Z1, a1, zf);
-        }
-        {
-          const Frag<T> a0 = ld_tr(Bs, 0, jt + tt, lane), a1 = ld_tr(Bs, 32, jt + tt, lane);
-          mma(X0, a0, ef);
-          mma(X1, a1, ef);
-        }
-        {
-          const Frag<T> a0 = ld_tr(Vs, 0, jt + tt, lane), a1 = ld_tr(Vs, 32, jt + tt, lane);
-          mma(F0, a0, ff);
-          mma(F1, a1, ff);
-        }
-        {
-          const Frag<T> a0 = ld_tr(Cs, 0, jt + tt, lane), a1 = ld_tr(Cs, 32, jt + tt, lane);
-          mma(F0, a0, pf);
-          mma(F1, a1, pf);
-        }
-      }
-    }
-  };
-#endif
   stage(jbeg, B0);
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, B0, B1);
@@ -295,19 +228,21 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   }
 }
 
-template <class T, int BM, bool CAUSAL>
+template <class T, int BM, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const T* __restrict__ A,
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
     const float* __restrict__ Aws, const float* __restrict__ Kws, T* __restrict__ gK,
-    T* __restrict__ gV, int N, int BH, int H, int grp, int win, float scale) {
+    T* __restrict__ gV, int N, int BH, int H, int grp, int win, const int* __restrict__ DS,
+    float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, kappa of the tile's rows
   struct Buf {
     T q[BM * HD], dO[BM * HD], a[BM * HD];
     float nl[BM], D[BM], al[BM], ka[BM];
+    int ds[DOCS ? BM : 4];   // first visible key of each row (document masks)
   };
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
@@ -333,8 +268,13 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   f32x16 gk0 = zero16(), gk1 = zero16(), gv0 = zero16(), gv1 = zero16();
 
   const int istart = CAUSAL ? k0 : 0;
-  // queries of the block's keys: causal i >= j, within the window i < j + win
-  const int iend = CAUSAL ? min(N, k0 + BLK - 1 + win) : N;
+  // queries of the block's keys: causal i >= j, within the window i < j + win,
+  // and with documents up to the first row whose document starts past the
+  // block (rows of one batch: the group's query heads share it)
+  const int* ds = DOCS ? DS + (size_t)(qh0 / H) * N : nullptr;
+  const int kmax = k0 + BLK - 1;
+  int iend = CAUSAL ? min(N, kmax + win) : N;
+  if (CAUSAL && DOCS) iend = min(iend, first_above(ds, min(N, k0 + BLK), N, kmax, lane));
   const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
   const int nsteps = ntiles * grp;      // (query head, query tile) steps
   // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
@@ -352,6 +292,8 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
       if (wave == 1) dma_rows_f32(make_rsrc(Dws + soff, sbytes), i0, b.D, k, lane);
       if (wave == 2) dma_rows_f32(make_rsrc(Aws + soff, sbytes), i0, b.al, k, lane);
       if (wave == 3) dma_rows_f32(make_rsrc(Kws + soff, sbytes), i0, b.ka, k, lane);
+      if (DOCS && wave == 0)
+        dma_rows_f32(make_rsrc(ds, sbytes), i0, reinterpret_cast<float*>(b.ds), k, lane);
     }
   };
   auto tile = [&](int u, const Buf& cb, Buf& nb) {
@@ -366,6 +308,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const float* sD = cb.D;
     const float* sA = cb.al;
     const float* sK = cb.ka;
+    const int* sDS = cb.ds;
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
@@ -386,11 +329,13 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
           for (int r = 0; r < 4; ++r)
             ps[4 * q + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * q + r], sl2, l4[r]));
         }
-        if ((CAUSAL && (is <= kw || is + 31 >= kw + win)) || is + 32 > N) {
+        if ((CAUSAL && (is <= kw || is + 31 >= kw + win || (DOCS && sDS[ib + 31] > kw))) ||
+            is + 32 > N) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
-            ps[v] = ((CAUSAL && (my_j > i || i >= my_j + win)) || i >= N) ? 0.f : ps[v];
+            const bool doc = DOCS && sDS[ib + 8 * (v >> 2) + 4 * h + (v & 3)] > my_j;
+            ps[v] = ((CAUSAL && (my_j > i || i >= my_j + win || doc)) || i >= N) ? 0.f : ps[v];
           }
         }
       }
@@ -480,29 +425,31 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   st_cols(gV + hoff, N, kw, 32, lane, out);
 }
 
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, bool DOCS>
 static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
                                float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
-                               int H, int grp, int win, int N, float scale, int passes,
+                               int H, int grp, int win, const int* ds, int N, float scale,
+                               int passes,
                                hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
-    hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
+    hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
                        (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws,
-                       Lws, Kws, N, BH, H, grp, win, nblk, scale);
+                       Lws, Kws, N, BH, H, grp, win, ds, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL>), dim3(nblk * (BH / grp)), dim3(NT), 0, st,
+  hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL, DOCS>), dim3(nblk * (BH / grp)), dim3(NT), 0,
+                     st,
                      (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO,
                      (const T*)gdQ, (const T*)gdK, (const T*)gdV, (const float*)Dws,
-                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, win,
+                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, win, ds,
                      scale);
   return hipGetLastError();
 }
@@ -511,12 +458,18 @@ hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
-                      int win, int N, int causal, float scale, int passes, hipStream_t st) {
+                      int win, const int* ds, int N, int causal, float scale, int passes,
+                      hipStream_t st) {
 #define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, Lws, Kws, \
-                     BH, H, grp, win, N, scale, passes, st
-  if (dt == 0)
-    return causal ? launch_bob_t<bf16, true>(FBD_BOB_ARGS) : launch_bob_t<bf16, false>(FBD_BOB_ARGS);
-  return causal ? launch_bob_t<float, true>(FBD_BOB_ARGS) : launch_bob_t<float, false>(FBD_BOB_ARGS);
+                     BH, H, grp, win, ds, N, scale, passes, st
+  if (dt == 0) {
+    if (!causal) return launch_bob_t<bf16, false, false>(FBD_BOB_ARGS);
+    return ds ? launch_bob_t<bf16, true, true>(FBD_BOB_ARGS)
+              : launch_bob_t<bf16, true, false>(FBD_BOB_ARGS);
+  }
+  if (!causal) return launch_bob_t<float, false, false>(FBD_BOB_ARGS);
+  return ds ? launch_bob_t<float, true, true>(FBD_BOB_ARGS)
+            : launch_bob_t<float, true, false>(FBD_BOB_ARGS);
 #undef FBD_BOB_ARGS
 }
 

@@ -27,12 +27,12 @@
 
 namespace fbd {
 
-template <class T, int BN, bool GPROJ, bool CAUSAL>
+template <class T, int BN, bool GPROJ, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, float* __restrict__ Lws,
-    int N, int BH, int H, int grp, int win, int nblk, float scale) {
+    int N, int BH, int H, int grp, int win, const int* __restrict__ DS, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   __shared__ __attribute__((aligned(16))) T K0[BN * HD];
@@ -69,8 +69,14 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   f32x16 pk0 = zero16(), pk1 = zero16();
   float r = 0.f;
 
-  // keys of the block's rows: causal j <= i, within the window j > i - win
-  const int jbeg = CAUSAL ? max(0, q0 - win + 1) / BN * BN : 0;
+  // keys of the block's rows: causal j <= i, from each row's start (sliding
+  // window, document); the block's first row has the smallest start
+  // (documents only: the window alone is a fixed offset from each row)
+  const int* ds = DOCS ? DS + (size_t)(wk.head / H) * N : nullptr;
+  const int rs = DOCS ? row_start(ds, my_i, win, N) : 0;              // this lane's row
+  const int rs_w = DOCS ? __builtin_amdgcn_readlane(rs, 31) : 0;      // the wave's largest
+  const int rs0 = DOCS ? row_start(ds, q0, win, N) : q0 - win + 1;
+  const int jbeg = CAUSAL ? min(max(0, rs0), q0) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend - jbeg + BN - 1) / BN;
   auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
@@ -94,11 +100,11 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
         for (int kb = 0; kb < 4; ++kb) mma(sacc, ld_row(Ks, jb, kb, lane), qf[kb]);
 #pragma unroll
         for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(sacc[v] * sl2 - lse2);
-        if (CAUSAL ? (js + 31 > qw || js <= qw + 31 - win) : (js + 32 > N)) {
+        if (CAUSAL ? (js + 31 > qw || (DOCS ? js < rs_w : js <= qw + 31 - win)) : (js + 32 > N)) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-            p[v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? 0.f : p[v];
+            p[v] = (CAUSAL ? (j > my_i || (DOCS ? j < rs : j <= my_i - win)) : (j >= N)) ? 0.f : p[v];
           }
         }
       }
@@ -157,12 +163,12 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   }
 }
 
-template <class T, int BM, bool GPROJ, bool CAUSAL>
+template <class T, int BM, bool GPROJ, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int H,
-    int grp, int win, float scale) {
+    int grp, int win, const int* __restrict__ DS, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q and dO tiles and the -LSE*log2(e), D (, r) of the tile's rows
@@ -170,6 +176,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     T q[BM * HD];
     T dO[BM * HD];
     float nl[BM], D[BM], r[GPROJ ? BM : 4];   // -LSE*log2(e), D, r
+    int ds[DOCS ? BM : 4];                               // first visible key (document masks)
   };
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
@@ -194,8 +201,13 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
 
   const int istart = CAUSAL ? k0 : 0;   // k0 is a multiple of BM
-  // queries of the block's keys: causal i >= j, within the window i < j + win
-  const int iend = CAUSAL ? min(N, k0 + BLK - 1 + win) : N;
+  // queries of the block's keys: causal i >= j, within the window i < j + win,
+  // and with documents up to the first row whose document starts past the
+  // block (rows of one batch: the group's query heads share it)
+  const int* ds = DOCS ? DS + (size_t)(qh0 / H) * N : nullptr;
+  const int kmax = k0 + BLK - 1;
+  int iend = CAUSAL ? min(N, kmax + win) : N;
+  if (CAUSAL && DOCS) iend = min(iend, first_above(ds, min(N, k0 + BLK), N, kmax, lane));
   const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
   const int nsteps = ntiles * grp;      // (query head, query tile) steps
   // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
@@ -211,6 +223,8 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
       if (wave == 1) dma_rows_f32(make_rsrc(Dws + soff, (uint32_t)N * 4u), i0, b.D, k, lane);
       if (GPROJ && wave == 2)
         dma_rows_f32(make_rsrc(Rws + soff, (uint32_t)N * 4u), i0, b.r, k, lane);
+      if (DOCS && wave == 3)
+        dma_rows_f32(make_rsrc(ds, (uint32_t)N * 4u), i0, reinterpret_cast<float*>(b.ds), k, lane);
     }
   };
   auto tile = [&](int u, const Buf& cb, Buf& nb) {
@@ -223,6 +237,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const float* sL = cb.nl;
     const float* sD = cb.D;
     const float* sR = cb.r;
+    const int* sDS = cb.ds;
 #pragma unroll
     for (int ib = 0; ib < BM; ib += 32) {
       const int is = i0 + ib;
@@ -243,11 +258,13 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
           for (int u = 0; u < 4; ++u)
             p[4 * q + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * q + u], sl2, l4[u]));
         }
-        if ((CAUSAL && (is <= kw || is + 31 >= kw + win)) || is + 32 > N) {
+        if ((CAUSAL && (is <= kw || is + 31 >= kw + win || (DOCS && sDS[ib + 31] > kw))) ||
+            is + 32 > N) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int i = is + 8 * (v >> 2) + 4 * h + (v & 3);
-            p[v] = ((CAUSAL && (my_j > i || i >= my_j + win)) || i >= N) ? 0.f : p[v];
+            const bool doc = DOCS && sDS[ib + 8 * (v >> 2) + 4 * h + (v & 3)] > my_j;
+            p[v] = ((CAUSAL && (my_j > i || i >= my_j + win || doc)) || i >= N) ? 0.f : p[v];
           }
         }
       }
@@ -314,26 +331,27 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   st_cols(dV + hoff, N, kw, 32, lane, out);
 }
 
-template <class T, bool GPROJ, bool CAUSAL>
+template <class T, bool GPROJ, bool CAUSAL, bool DOCS>
 static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
                                float* Dws, float* Rws, float* Lws, int BH, int H, int grp,
-                               int win, int N, float scale, int passes, hipStream_t st) {
+                               int win, const int* ds, int N, float scale, int passes,
+                               hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
-    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL>), dim3(nblk * BH), dim3(NT), 0, st,
+    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL, DOCS>), dim3(nblk * BH), dim3(NT), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
-                       (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, win, nblk, scale);
+                       (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, win, ds, nblk, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL>), dim3(nblk * (BH / grp)), dim3(NT),
+  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL, DOCS>), dim3(nblk * (BH / grp)), dim3(NT),
                      0, st, (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws,
                      (const T*)dO, (const float*)Dws, (const float*)Rws, (T*)dK, (T*)dV, N, BH, H,
-                     grp, win, scale);
+                     grp, win, ds, scale);
   return hipGetLastError();
 }
 
@@ -341,25 +359,28 @@ template <class T, bool GPROJ>
 static hipError_t launch_bwd_c(int causal, const void* Q, const void* K, const void* V,
                                const void* O, const float* LSE, const void* dO, void* dQ,
                                void* dK, void* dV, float* Dws, float* Rws, float* Lws, int BH,
-                               int H, int grp, int win, int N, float scale, int passes,
+                               int H, int grp, int win, const int* ds, int N, float scale,
+                               int passes,
                                hipStream_t st) {
   if (causal)
-    return launch_bwd_t<T, GPROJ, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
-  return launch_bwd_t<T, GPROJ, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
+    return ds ? launch_bwd_t<T, GPROJ, true, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st)
+              : launch_bwd_t<T, GPROJ, true, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
+  return launch_bwd_t<T, GPROJ, false, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
 }
 
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
-                      float* Rws, float* Lws, int BH, int H, int grp, int win, int N,
+                      float* Rws, float* Lws, int BH, int H, int grp, int win, const int* ds,
+                      int N,
                       int causal, float scale, int gproj, int passes, hipStream_t st) {
   if (dt == 0) {
     if (gproj)
-      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
-    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
+      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
+    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
   }
   if (gproj)
-    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
-  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, N, scale, passes, st);
+    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
+  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
 }
 
 }  // namespace fbd

@@ -36,12 +36,13 @@ constexpr int FWD_NT = 64 * FWD_WAVES;
 constexpr int FWD_G = FBD_FWD_G;                      // 32-query groups per wave
 constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;    // query rows per workgroup
 
-template <class T, int BN, bool CAUSAL>
+template <class T, int BN, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,
-                                                     int H, int grp, int win, int nblk,
+                                                     int H, int grp, int win,
+                                                     const int* __restrict__ DS, int nblk,
                                                      float scale) {
   // two buffers as separate objects, used in a loop unrolled by two, so the
   // compiler can tell the copy of the next tile never aliases the reads of
@@ -86,8 +87,18 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
     negm[g] = zero16();
   }
 
-  // keys of the block's rows: causal j <= i, within the window j > i - win
-  const int jbeg = CAUSAL ? max(0, q0 - win + 1) / BN * BN : 0;
+  // keys of the block's rows: causal j <= i, from each row's start (sliding
+  // window, document); the block's first row has the smallest start
+  // (documents only: the window alone is a fixed offset from each row)
+  const int* ds = DOCS ? DS + (size_t)(wk.head / H) * N : nullptr;
+  int rs[FWD_G], rs_w[FWD_G];   // this lane's row start; the wave's largest
+#pragma unroll
+  for (int g = 0; g < FWD_G; ++g) {
+    rs[g] = DOCS ? row_start(ds, qw + g * WROWS + (lane & 31), win, N) : 0;
+    rs_w[g] = DOCS ? __builtin_amdgcn_readlane(rs[g], 31) : 0;
+  }
+  const int rs0 = DOCS ? row_start(ds, q0, win, N) : q0 - win + 1;
+  const int jbeg = CAUSAL ? min(max(0, rs0), q0) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
   const int ntiles = (jend - jbeg + BN - 1) / BN;
   constexpr int NS = BN / 32;   // 32-key sub-blocks per tile
@@ -129,12 +140,13 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
       for (int sb = 0; sb < NS; ++sb) {
         const int js = j0 + sb * 32;
-        if (CAUSAL ? (js + 31 > qg || js <= qg + 31 - win) : (js + 32 > N)) {
+        if (CAUSAL ? (js + 31 > qg || (DOCS ? js < rs_w[g] : js <= qg + 31 - win))
+                   : (js + 32 > N)) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-            x[sb][g][v] = (CAUSAL ? (j > my_i || j <= my_i - win) : (j >= N)) ? -INFINITY
-                                                                             : x[sb][g][v];
+            const bool early = DOCS ? j < rs[g] : j <= my_i - win;
+            x[sb][g][v] = (CAUSAL ? (j > my_i || early) : (j >= N)) ? -INFINITY : x[sb][g][v];
           }
         }
       }
@@ -219,25 +231,30 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
 
 template <class T, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               int BH, int H, int grp, int win, int N, float scale,
-                               hipStream_t st) {
+                               int BH, int H, int grp, int win, const int* ds, int N,
+                               float scale, hipStream_t st) {
   constexpr int BN = sizeof(T) == 2 ? FBD_FWD_BN : 64;
   const int nblk = (N + FWD_BLK - 1) / FWD_BLK;
-  hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
-                     (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, win,
-                     nblk, scale);
+  if (ds)
+    hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL, true>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, win, ds,
+                       nblk, scale);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL, false>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, win,
+                       ds, nblk, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int BH, int H, int grp, int win, int N, int causal, float scale,
-                      hipStream_t st) {
+                      int BH, int H, int grp, int win, const int* ds, int N, int causal,
+                      float scale, hipStream_t st) {
   if (dt == 0) {
-    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
-    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
+    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
+    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
   }
-  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
-  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, H, grp, win, N, scale, st);
+  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
+  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
 }
 
 }  // namespace fbd

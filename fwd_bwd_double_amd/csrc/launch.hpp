@@ -39,9 +39,6 @@
 #ifndef FBD_BOB_ROW_OCC
 #define FBD_BOB_ROW_OCC 1
 #endif
-#ifndef FBD_BOB_ROW_SPLIT
-#define FBD_BOB_ROW_SPLIT 1
-#endif
 #ifndef FBD_BOB_COL_OCC
 #define FBD_BOB_COL_OCC 2
 #endif
@@ -54,24 +51,27 @@ namespace fbd {
 // heads, key-side tensors (K, V, dK, dV, g_dK, g_dV, g_K, g_V) BH / grp; query
 // head h of a batch uses key head h / grp.  win: causal sliding window, key j
 // visible to query i iff i - win < j <= i (a value >= N is plain causal).
+// ds: nullptr, or (B, N) int32 first visible key of each query row (document
+// masks: key j visible to query i of batch b iff ds[b][i] <= j <= i).
 // Pointers are device pointers.
 // passes (backward and BoB): bit 0 = row pass, bit 1 = column pass.
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int BH, int H, int grp, int win, int N, int causal, float scale,
-                      hipStream_t st);
+                      int BH, int H, int grp, int win, const int* ds, int N, int causal,
+                      float scale, hipStream_t st);
 
 // Backward workspace: D, r, and -LSE*log2(e) per row (written by the row pass,
 // read by the column pass).
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
-                      float* Rws, float* Lws, int BH, int H, int grp, int win, int N,
-                      int causal, float scale, int gproj, int passes, hipStream_t st);
+                      float* Rws, float* Lws, int BH, int H, int grp, int win, const int* ds,
+                      int N, int causal, float scale, int gproj, int passes, hipStream_t st);
 
 // BoB workspace: D, alpha, beta, -LSE*log2(e) and kappa = alpha*D + beta per row.
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
-                      int win, int N, int causal, float scale, int passes, hipStream_t st);
+                      int win, const int* ds, int N, int causal, float scale, int passes,
+                      hipStream_t st);
 
 }  // namespace fbd

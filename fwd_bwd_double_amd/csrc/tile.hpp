@@ -334,6 +334,42 @@ __device__ __forceinline__ void ld_cols(const T* X, int n, int r0, int c0, int l
 // same position in every head.  Row passes go from the last row block (the
 // most key blocks under the causal mask) to the first; column passes from the
 // first key block (seen by the most queries) to the last.
+// Document masks: ds is one batch's row of first visible keys, non-decreasing
+// with ds[i] <= i (packed documents: each query sees only keys of its own
+// document).  Returns the first i in [lo, hi) with ds[i] > kmax, or hi, the
+// same in every lane: each round the 64 lanes probe 64 evenly spaced rows and
+// a ballot narrows the range 64-fold, so N = 2^18 takes three rounds.  Every
+// probe stays below hi (callers pass hi <= N) and the range shrinks every
+// round, so it ends for any contents of ds.
+__device__ __forceinline__ int first_above(const int* __restrict__ ds, int lo, int hi, int kmax,
+                                           int lane) {
+  int a = lo, b = hi;   // the answer lies in [a, b]
+  while (a < b) {
+    const int s = (b - a + 63) / 64;
+    const int p = a + lane * s;
+    const bool pred = p < b && ds[p] > kmax;
+    const unsigned long long m = __ballot(pred);
+    if (m == 0) {
+      const int last = a + s * min(63, (b - 1 - a) / s);
+      a = last + 1;
+    } else {
+      const int f = __builtin_ctzll(m);
+      b = a + f * s;
+      a = f == 0 ? b : a + (f - 1) * s + 1;
+    }
+  }
+  return a;
+}
+
+// First visible key of query row i under the causal mask: i - win + 1 for a
+// sliding window, raised to the row's document start when ds is given (row
+// index clamped into the head for padding rows past N).
+__device__ __forceinline__ int row_start(const int* __restrict__ ds, int i, int win, int N) {
+  int r = i - win + 1;
+  if (ds) r = max(r, ds[min(i, N - 1)]);
+  return r;
+}
+
 struct Work {
   int head, blk;
 };

@@ -187,29 +187,41 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
  * i - window < j <= i.  Tiles wholly outside the window are never loaded.
  * window == 0 is plain causal (or full, with causal == 0) attention.
  *
- * With Hkv == H and window == 0 these equal attn_fwd / attn_bwd / attn_bob.
- * Hkv outside the range above or window < 0 is ATTN_EINVAL; window > 0 with
- * causal == 0 is ATTN_EUNSUPPORTED; other arguments and errors as for the
- * multi-head entry points (workspace sizes count the H query heads).  The
- * backward and BoB must get the same causal and window as the forward.
+ * Document masks (doc_start != NULL, causal only): packed sequences of
+ * several documents per batch row.  doc_start is a device (B, N) int32 array
+ * (4-byte aligned, read-only) giving for each query position the position of
+ * its document's first token: key j is visible to query i of batch b iff
+ * doc_start[b][i] <= j <= i (and within the window, if any).  It must be
+ * non-decreasing along i with doc_start[b][i] <= i; other contents give
+ * unspecified values but stay within every buffer.  The kernels skip tiles
+ * outside the documents: a key block's column pass finds the last query row
+ * it reaches with a wave-parallel search of doc_start.
+ *
+ * With Hkv == H, window == 0 and no doc_start these equal attn_fwd / attn_bwd
+ * / attn_bob.  Hkv outside the range above, window < 0 or a doc_start that
+ * overlaps an output is ATTN_EINVAL; a misaligned doc_start is ATTN_EALIGN;
+ * window > 0 or doc_start with causal == 0 is ATTN_EUNSUPPORTED; other
+ * arguments and errors as for the multi-head entry points (workspace sizes
+ * count the H query heads).  The backward and BoB must get the same causal,
+ * window and doc_start as the forward.
  */
 attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V,
-                        int causal, int64_t window, float scale,
+                        int causal, int64_t window, const int32_t* doc_start, float scale,
                         void* O, float* LSE, void* stream);
 
 attn_status attn_bwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V, const void* O,
                         const float* LSE, const void* dO,
-                        int causal, int64_t window, float scale, int gproj,
-                        void* dQ, void* dK, void* dV,
+                        int causal, int64_t window, const int32_t* doc_start, float scale,
+                        int gproj, void* dQ, void* dK, void* dV,
                         void* ws, size_t ws_bytes, void* stream);
 
 attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V, const void* O,
                         const float* LSE, const void* dO,
                         const void* g_dQ, const void* g_dK, const void* g_dV,
-                        int causal, int64_t window, float scale,
+                        int causal, int64_t window, const int32_t* doc_start, float scale,
                         void* g_Q, void* g_K, void* g_V, void* g_dO,
                         void* ws, size_t ws_bytes, void* stream);
 

@@ -41,22 +41,26 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _visible(rows_idx: np.ndarray, ncols: int, causal: bool, window: int = 0) -> np.ndarray:
+def _visible(rows_idx: np.ndarray, ncols: int, causal: bool, window: int = 0,
+             starts=None) -> np.ndarray:
     """Boolean (len(rows_idx), ncols): True where query rows_idx[a] sees key j:
     j <= i when causal, and additionally j > i - window for a sliding window
-    (window > 0; a flexible mask the FlashBoB page names among its next
-    extensions, closing paragraph)."""
+    (window > 0) and j >= starts[i] for document masks (starts: this batch
+    row's first position of each query's document).  Both are flexible masks
+    the FlashBoB page names among its next extensions (closing paragraph)."""
     j = np.arange(ncols)[None, :]
     if causal:
         vis = j <= rows_idx[:, None]
         if window > 0:
             vis &= j > rows_idx[:, None] - window
+        if starts is not None:
+            vis &= j >= np.asarray(starts)[rows_idx][:, None]
         return vis
-    assert window == 0, "a sliding window needs the causal mask"
+    assert window == 0 and starts is None, "window and document masks need the causal mask"
     return np.ones((rows_idx.size, ncols), dtype=bool)
 
 
-def _row_softmax(q_rows, k, rows_idx, causal, scale, window=0):
+def _row_softmax(q_rows, k, rows_idx, causal, scale, window=0, starts=None):
     """P rows and LSE for the given query rows against keys k.
 
     m_i is the row max of the raw scores over visible keys; the exponent is
@@ -64,7 +68,7 @@ def _row_softmax(q_rows, k, rows_idx, causal, scale, window=0):
     largest entry is exactly exp(0) = 1 (GProj page, section "Why the error
     shows up at the end of training").  LSE_i = c m_i + ln l_i."""
     s = q_rows @ k.T
-    vis = _visible(rows_idx, k.shape[0], causal, window)
+    vis = _visible(rows_idx, k.shape[0], causal, window, starts)
     s_vis = np.where(vis, s, -np.inf)
     m = s_vis.max(axis=1, keepdims=True)
     e = np.exp(scale * (s_vis - m))        # masked keys: exp(-inf) = 0
@@ -106,7 +110,8 @@ def max_prob(Q, K, causal=True, scale=None, heads=None, row_idx=None, chunk=1024
     return out
 
 
-def _head(q, k, v, do, a, bk, cv, rows_idx, causal, c, want_bwd, want_bob, window=0):
+def _head(q, k, v, do, a, bk, cv, rows_idx, causal, c, want_bwd, want_bob, window=0,
+          starts=None):
     """All outputs of one head for the query rows ``rows_idx``.
 
     Row outputs (O, LSE, D, dQ, alpha, beta, gQ, gdO) are complete for those
@@ -117,7 +122,7 @@ def _head(q, k, v, do, a, bk, cv, rows_idx, causal, c, want_bwd, want_bob, windo
         ncols = int(rows_idx.max()) + 1
     kk, vv = k[:ncols], v[:ncols]
     qr = q[rows_idx]
-    p, lse = _row_softmax(qr, kk, rows_idx, causal, c, window)
+    p, lse = _row_softmax(qr, kk, rows_idx, causal, c, window, starts)
     o = p @ vv
     r = {"O": o, "LSE": lse}
     if not (want_bwd or want_bob):
@@ -135,7 +140,7 @@ def _head(q, k, v, do, a, bk, cv, rows_idx, causal, c, want_bwd, want_bob, windo
     if want_bob:
         ar = a[rows_idx]
         bkk, cc = bk[:ncols], cv[:ncols]
-        vis = _visible(rows_idx, ncols, causal, window)
+        vis = _visible(rows_idx, ncols, causal, window, starts)
         # Phi = <A, dQ> + <Bk, dK> + <C, dV> = <dS, W> + <P, U>
         W = np.where(vis, c * (ar @ kk.T + qr @ bkk.T), 0.0)
         U = np.where(vis, dor @ cc.T, 0.0)
@@ -160,7 +165,7 @@ _COL_KEYS = ("dK", "dV", "gK", "gV")
 
 
 def _run(Q, K, V, dO=None, A=None, Bk=None, C=None, causal=True, scale=None,
-         want_bwd=False, want_bob=False, chunk=1024, heads=None, window=0):
+         want_bwd=False, want_bob=False, chunk=1024, heads=None, window=0, docs=None):
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, H, N, d = Q.shape
     c = 1.0 / np.sqrt(d) if scale is None else float(scale)
@@ -188,7 +193,8 @@ def _run(Q, K, V, dO=None, A=None, Bk=None, C=None, causal=True, scale=None,
                 None if C is None else C[b, h])
         for r0 in range(0, N, chunk):
             idx = np.arange(r0, min(N, r0 + chunk))
-            r, ncols = _head(*args, idx, causal, c, want_bwd, want_bob, window)
+            r, ncols = _head(*args, idx, causal, c, want_bwd, want_bob, window,
+                             None if docs is None else np.asarray(docs)[b])
             for key, val in r.items():
                 if key in _ROW_KEYS:
                     out[key][b, h, idx] = val
@@ -197,22 +203,23 @@ def _run(Q, K, V, dO=None, A=None, Bk=None, C=None, causal=True, scale=None,
     return out
 
 
-def fwd(Q, K, V, causal=True, scale=None, heads=None, chunk=1024, window=0):
+def fwd(Q, K, V, causal=True, scale=None, heads=None, chunk=1024, window=0, docs=None):
     """O = softmax(c Q K^T + mask) V and LSE_i = c m_i + ln l_i per row."""
-    r = _run(Q, K, V, causal=causal, scale=scale, chunk=chunk, heads=heads, window=window)
+    r = _run(Q, K, V, causal=causal, scale=scale, chunk=chunk, heads=heads, window=window,
+             docs=docs)
     return r["O"], r["LSE"]
 
 
-def bwd(Q, K, V, dO, causal=True, scale=None, heads=None, chunk=1024, window=0):
+def bwd(Q, K, V, dO, causal=True, scale=None, heads=None, chunk=1024, window=0, docs=None):
     """Gradients of <dO, O(Q, K, V)>:  dP = dO V^T, D = rowsum(dO o O),
     dS = P o (dP - D), dQ = c dS K, dK = c dS^T Q, dV = P^T dO.
     Returns dict with O, LSE, D, dQ, dK, dV."""
     return _run(Q, K, V, dO, causal=causal, scale=scale, want_bwd=True,
-                heads=heads, chunk=chunk, window=window)
+                heads=heads, chunk=chunk, window=window, docs=docs)
 
 
 def bob(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, heads=None,
-        chunk=1024, with_bwd=False, window=0):
+        chunk=1024, with_bwd=False, window=0, docs=None):
     """Backward-over-backward: the gradient of
     Phi = <gdQ, dQ> + <gdK, dK> + <gdV, dV> with respect to (Q, K, V, dO),
     where (dQ, dK, dV) is the first backward of ``bwd``.  With A = gdQ,
@@ -226,7 +233,8 @@ def bob(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, heads=None,
     alpha and beta are the two per-row scalar states.  Returns a dict with
     O, LSE, D, alpha, beta, gQ, gK, gV, gdO (and dQ, dK, dV if with_bwd)."""
     return _run(Q, K, V, dO, gdQ, gdK, gdV, causal=causal, scale=scale,
-                want_bwd=with_bwd, want_bob=True, heads=heads, chunk=chunk, window=window)
+                want_bwd=with_bwd, want_bob=True, heads=heads, chunk=chunk, window=window,
+                docs=docs)
 
 
 def hvp(Q, K, V, dO, vQ, vK, vV, causal=True, scale=None, heads=None, chunk=1024):
@@ -267,25 +275,28 @@ def _group(Q, K):
     return H // Hkv
 
 
-def fwd_gqa(Q, K, V, causal=True, scale=None, window=0):
+def fwd_gqa(Q, K, V, causal=True, scale=None, window=0, docs=None):
     g = _group(Q, K)
-    return fwd(Q, expand_kv(K, g), expand_kv(V, g), causal=causal, scale=scale, window=window)
+    return fwd(Q, expand_kv(K, g), expand_kv(V, g), causal=causal, scale=scale, window=window,
+               docs=docs)
 
 
-def bwd_gqa(Q, K, V, dO, causal=True, scale=None, window=0):
+def bwd_gqa(Q, K, V, dO, causal=True, scale=None, window=0, docs=None):
     g = _group(Q, K)
-    r = bwd(Q, expand_kv(K, g), expand_kv(V, g), dO, causal=causal, scale=scale, window=window)
+    r = bwd(Q, expand_kv(K, g), expand_kv(V, g), dO, causal=causal, scale=scale, window=window,
+            docs=docs)
     r["dK"], r["dV"] = reduce_kv(r["dK"], g), reduce_kv(r["dV"], g)
     return r
 
 
-def bob_gqa(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, with_bwd=False, window=0):
+def bob_gqa(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, with_bwd=False, window=0,
+            docs=None):
     """BoB of the grouped-query map: <gdK, dK> with dK summed over a group is
     <expand(gdK), dK per query head>, so the cotangents expand like K and V
     and the key-side outputs reduce like dK, dV."""
     g = _group(Q, K)
     r = bob(Q, expand_kv(K, g), expand_kv(V, g), dO, gdQ, expand_kv(gdK, g), expand_kv(gdV, g),
-            causal=causal, scale=scale, with_bwd=with_bwd, window=window)
+            causal=causal, scale=scale, with_bwd=with_bwd, window=window, docs=docs)
     for k in ("gK", "gV") + (("dK", "dV") if with_bwd else ()):
         r[k] = reduce_kv(r[k], g)
     return r

@@ -366,3 +366,55 @@ def test_sliding_window(N, window, H, Hkv, dtype):
                 check_single_key_zero(k, f64(t), a, w.scale, dtype, kv)
             else:
                 check(k, f64(t), ref[k], t2)
+
+
+# -------------------------------------- document masks (packed sequences)
+def doc_starts(B, N, seed, mean_len):
+    """Seeded packed-document layout: (B, N) int first position of each row's
+    document, document lengths ~ geometric with the given mean (some of
+    length 1)."""
+    rng = np.random.default_rng(seed)
+    out = np.zeros((B, N), dtype=np.int64)
+    for b in range(B):
+        i = 0
+        while i < N:
+            n = int(min(N - i, rng.geometric(1.0 / mean_len)))
+            out[b, i:i + n] = i
+            i += n
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("N,mean_len,window,H,Hkv", [(300, 40, 0, 2, 2), (1000, 150, 0, 4, 2),
+                                                     (1000, 300, 64, 2, 1),
+                                                     (2048, 700, 0, 2, 2), (333, 5, 0, 3, 3)])
+def test_document_masks(N, mean_len, window, H, Hkv, dtype):
+    import fwd_bwd_double_amd as fbd
+    w = synthetic.Workload(f"doc-{dtype}", 2, H, N, 64, dtype, 9500 + N + mean_len, causal=True,
+                           qkv_std=1.0)
+    x, g, a = inputs(w)
+    for n in ("k", "v", "g_dk", "g_dv"):
+        g[n] = g[n][:, :Hkv].contiguous()
+        a[n] = a[n][:, :Hkv]
+    docs = doc_starts(2, N, 77 + N, mean_len)
+    ds = torch.from_numpy(docs.astype(np.int32)).cuda()
+    say(f"[gpu] docs mean_len={mean_len} window={window} B=2 H={H} Hkv={Hkv} N={N} "
+        f"dtype={dtype} ndocs={[len(set(r)) for r in docs]}")
+    o, lse = fbd.attn_fwd(g["q"], g["k"], g["v"], scale=w.scale, window=window, doc_start=ds)
+    t1, t2 = (1e-5, 1e-5) if dtype == "fp32" else (2e-2, 5e-2)
+    ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                         with_bwd=True, window=window, docs=docs)
+    f64 = synthetic.to_f64
+    for gproj in (False, True):
+        dq, dk, dv = fbd.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale,
+                                  gproj=gproj, window=window, doc_start=ds)
+        gq, gk, gv, gdo = fbd.attn_bob(g["q"], g["k"], g["v"], o, lse, g["do"], g["g_dq"],
+                                       g["g_dk"], g["g_dv"], scale=w.scale, window=window,
+                                       doc_start=ds)
+        torch.cuda.synchronize()
+        check("O", f64(o), ref["O"], t1)
+        check("LSE", f64(lse), ref["LSE"], t1)
+        for k, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            check(k, f64(t), ref[k], t1)
+        for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
+            check(k, f64(t), ref[k], t2)

@@ -159,6 +159,39 @@ def test_sliding_window_against_torch_double_backward(window):
         assert np.linalg.norm(mine - ref) <= 1e-12 * max(1.0, np.linalg.norm(ref))
 
 
+def test_document_mask_against_torch_and_independent_documents():
+    # packed documents: torch fp64 double backward with an explicit mask; and
+    # the packed result equals running each document on its own
+    Q, K, V, dO, A, Bk, C = inputs(1, 2, 16, 8, 139)
+    bounds = [0, 5, 6, 13, 16]                       # documents [0,5) [5,6) [6,13) [13,16)
+    starts = np.zeros(16, dtype=np.int64)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        starts[lo:hi] = lo
+    docs = starts[None, :]
+    c = 1 / math.sqrt(8)
+    i = torch.arange(16)[:, None]
+    j = torch.arange(16)[None, :]
+    hide = (j > i) | (j < torch.from_numpy(starts)[:, None])
+    tq, tk, tv, tdo = (torch.tensor(x, requires_grad=True) for x in (Q, K, V, dO))
+    s_ = (c * (tq @ tk.transpose(-1, -2))).masked_fill(hide, float("-inf"))
+    out = torch.softmax(s_, dim=-1) @ tv
+    gq, gk, gv = torch.autograd.grad(out, (tq, tk, tv), tdo, create_graph=True)
+    phi_ = (gq * torch.from_numpy(A)).sum() + (gk * torch.from_numpy(Bk)).sum() + \
+        (gv * torch.from_numpy(C)).sum()
+    hq, hk, hv, hdo = torch.autograd.grad(phi_, (tq, tk, tv, tdo))
+    r = oracle.bob(Q, K, V, dO, A, Bk, C, with_bwd=True, docs=docs)
+    for mine, ref in ((r["dQ"], gq), (r["dK"], gk), (r["dV"], gv), (r["gQ"], hq),
+                      (r["gK"], hk), (r["gV"], hv), (r["gdO"], hdo)):
+        ref = ref.detach().numpy()
+        assert np.linalg.norm(mine - ref) <= 1e-12 * max(1.0, np.linalg.norm(ref))
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        sl = slice(lo, hi)
+        own = oracle.bob(Q[..., sl, :], K[..., sl, :], V[..., sl, :], dO[..., sl, :],
+                         A[..., sl, :], Bk[..., sl, :], C[..., sl, :], with_bwd=True)
+        for k in ("O", "dQ", "dK", "dV", "gQ", "gK", "gV", "gdO"):
+            assert np.allclose(r[k][..., sl, :], own[k], rtol=1e-12, atol=1e-13), (k, lo)
+
+
 def test_window_of_one_closed_form_and_wide_window_is_causal():
     Q, K, V, dO, A, Bk, C = inputs(1, 1, 9, 4, 138)
     c = 0.5
