@@ -12,6 +12,8 @@ Modules:
   online      the tiled online-softmax forward recurrence, as a model
   rounding    bf16 round-to-nearest-even and a rounding model of the bf16
               backward with and without GProj
+  fp8         E4M3 codes, the Hadamard rotation, block quantisation and the
+              FP8 forward model (import as oracle.fp8)
 """
 from .attention import (probs, fwd, bwd, bob, hvp, rows, last_columns,  # noqa: F401
                         gproj_project, max_prob, expand_kv, reduce_kv, fwd_gqa, bwd_gqa,
