@@ -81,6 +81,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_hvp.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32,
                              vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_hvp.restype = i32
+    # FP8 forward
+    u64 = ctypes.c_uint64
+    lib.attn_fp8_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_fp8_workspace_bytes.restype = sz
+    lib.attn_fp8_workspace_layout.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
+    lib.attn_fp8_workspace_layout.restype = i32
+    lib.attn_fp8_quantize.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, u64, vp, sz,
+                                      vp]
+    lib.attn_fp8_quantize.restype = i32
+    lib.attn_fwd_fp8.argtypes = [i32, i64, i64, i64, i64, i64, vp, sz, i32, f32, vp, vp, vp]
+    lib.attn_fwd_fp8.restype = i32
     lib.attn_status_str.argtypes = [i32]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -314,3 +325,82 @@ def attn_hvp(q, k, v, do, v_q, v_k, v_v, causal: bool = True, scale: Optional[fl
     if grad:
         out.update(dQ=dq, dK=dk, dV=dv)
     return out
+
+
+FP8_PARTS = ("q", "k", "vt", "eq", "ek", "ev", "vmax")
+
+
+def fp8_workspace_bytes(B: int, H: int, Hkv: int, N: int) -> int:
+    return int(load().attn_fp8_workspace_bytes(B, H, Hkv, N))
+
+
+def fp8_parts(ws: torch.Tensor, B: int, H: int, Hkv: int, N: int) -> dict:
+    """Views of the parts of an FP8 workspace (uint8 tensor): codes q (B, H, N,
+    64), k (B, Hkv, N, 64), vt (B, Hkv, 64, NP) and int32 exponents eq (B, H,
+    nb), ek (B, Hkv, nb), ev (B, Hkv, 64), nb = ceil(N / 64), NP = 64 nb."""
+    lib = load()
+    offs = (ctypes.c_size_t * len(FP8_PARTS))()
+    _raise("attn_fp8_workspace_layout", lib.attn_fp8_workspace_layout(B, H, Hkv, N, offs))
+    nb = (N + 63) // 64
+    shapes = {"q": ((B, H, N, 64), torch.uint8), "k": ((B, Hkv, N, 64), torch.uint8),
+              "vt": ((B, Hkv, 64, nb * 64), torch.uint8), "eq": ((B, H, nb), torch.int32),
+              "ek": ((B, Hkv, nb), torch.int32), "ev": ((B, Hkv, 64), torch.int32)}
+    out = {}
+    for i, name in enumerate(FP8_PARTS[:-1]):
+        shape, dt = shapes[name]
+        n = math.prod(shape) * (4 if dt == torch.int32 else 1)
+        out[name] = ws[offs[i]:offs[i] + n].view(dt).view(shape)
+    return out
+
+
+def attn_fp8_quantize(q, k, v, signs: Optional[int] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """E4M3 codes and power-of-two exponents of q, k (rotated by diag(s) H / 8
+    when `signs`, a 64-bit sign mask, is given) and v, written into an FP8
+    workspace (uint8 tensor, returned; see fp8_parts for its contents)."""
+    lib = load()
+    _check("q", q, q)
+    Hkv = _kv_heads(q, k)
+    for n, t in (("k", k), ("v", v)):
+        _check(n, t, q, shape=_kv_shape(q, Hkv))
+    B, H, N, d = q.shape
+    need = fp8_workspace_bytes(B, H, Hkv, N)
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    if workspace.device != q.device or workspace.dtype != torch.uint8 or \
+            workspace.numel() < need or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 GPU tensor of >= {need} bytes")
+    rotate = signs is not None
+    mask = (int(signs) & (2 ** 64 - 1)) if rotate else 0
+    st = lib.attn_fp8_quantize(_dt(q), B, H, Hkv, N, d, q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), 1 if rotate else 0, mask, workspace.data_ptr(),
+                               workspace.numel(), _stream(q.device))
+    _raise("attn_fp8_quantize", st)
+    return workspace
+
+
+def attn_fwd_fp8_codes(workspace: torch.Tensor, B: int, H: int, Hkv: int, N: int,
+                       dtype=torch.bfloat16, causal: bool = True, scale: Optional[float] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O (dtype), LSE (fp32) of the forward on the codes of an FP8 workspace."""
+    lib = load()
+    dev = workspace.device
+    if dev.type != "cuda" or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    o = torch.empty((B, H, N, 64), device=dev, dtype=dtype)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    c = 0.125 if scale is None else float(scale)
+    st = lib.attn_fwd_fp8(_dt(o), B, H, Hkv, N, 64, workspace.data_ptr(), workspace.numel(),
+                          1 if causal else 0, c, o.data_ptr(), lse.data_ptr(), _stream(dev))
+    _raise("attn_fwd_fp8", st)
+    return o, lse
+
+
+def attn_fwd_fp8(q, k, v, causal: bool = True, scale: Optional[float] = None,
+                 signs: Optional[int] = None, workspace: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O, LSE of attention with both products in E4M3 (see attn_fp8_quantize
+    for `signs`); shapes and dtypes as attn_fwd, no window or document mask."""
+    ws = attn_fp8_quantize(q, k, v, signs, workspace)
+    B, H, N, _ = q.shape
+    return attn_fwd_fp8_codes(ws, B, H, k.shape[1], N, q.dtype, causal, _scale(q, scale))

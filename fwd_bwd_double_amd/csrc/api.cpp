@@ -331,4 +331,98 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
   return finish(e);
 }
 
+// ---------------------------------------------------------------------------
+// FP8 forward: quantisation pre-pass and forward on the codes.
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+struct F8Layout {
+  size_t off[ATTN_FP8_NPARTS];
+  size_t total;
+};
+
+F8Layout fp8_layout(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
+  const size_t nb = (size_t)(N + 63) / 64, np = nb * 64;
+  const size_t bh = (size_t)B * H, bhk = (size_t)B * Hkv;
+  const size_t bytes[ATTN_FP8_NPARTS] = {bh * N * 64, bhk * N * 64, bhk * 64 * np,
+                                         bh * nb * 4, bhk * nb * 4, bhk * 64 * 4, bhk * 64 * 4};
+  F8Layout L;
+  size_t off = 0;
+  for (int i = 0; i < ATTN_FP8_NPARTS; ++i) {
+    L.off[i] = off;
+    off = (off + bytes[i] + 255) & ~(size_t)255;
+  }
+  L.total = off;
+  return L;
+}
+
+// Shape checks of the FP8 entry points (the V code rows take N rounded up to
+// 64, still within 32-bit offsets).
+attn_status fp8_shape(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                      float scale) {
+  attn_status st = check_shape(dt, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  return check_heads(H, Hkv);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_fp8_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0) return 0;
+  return fp8_layout(B, H, Hkv, N).total;
+}
+
+attn_status attn_fp8_workspace_layout(int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                                      size_t* offsets) {
+  if (!offsets) return ATTN_EINVAL;
+  if (fp8_shape(ATTN_BF16, B, H, Hkv, N, 64, 1.f) != ATTN_OK) return ATTN_EINVAL;
+  const F8Layout L = fp8_layout(B, H, Hkv, N);
+  for (int i = 0; i < ATTN_FP8_NPARTS; ++i) offsets[i] = L.off[i];
+  return ATTN_OK;
+}
+
+attn_status attn_fp8_quantize(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                              int64_t d, const void* Q, const void* K, const void* V, int rotate,
+                              uint64_t signs, void* ws, size_t ws_bytes, void* stream) {
+  attn_status st = fp8_shape(dt, B, H, Hkv, N, d, 1.f);
+  if (st != ATTN_OK) return st;
+  const F8Layout L = fp8_layout(B, H, Hkv, N);
+  if (!ws || ws_bytes < L.total) return ATTN_EWORKSPACE;
+  const size_t t = (size_t)B * H * N * d * elem_size(dt);
+  const size_t tk = (size_t)B * Hkv * N * d * elem_size(dt);
+  st = check_ptrs({{Q, t}, {K, tk}, {V, tk}}, {{ws, L.total}});
+  if (st != ATTN_OK) return st;
+  char* w = static_cast<char*>(ws);
+  return finish(fbd::launch_fp8_quantize(
+      (int)dt, Q, K, V, (uint8_t*)(w + L.off[ATTN_FP8_Q]), (uint8_t*)(w + L.off[ATTN_FP8_K]),
+      (uint8_t*)(w + L.off[ATTN_FP8_VT]), (int*)(w + L.off[ATTN_FP8_EQ]),
+      (int*)(w + L.off[ATTN_FP8_EK]), (int*)(w + L.off[ATTN_FP8_EV]),
+      (uint32_t*)(w + L.off[ATTN_FP8_VMAX]), (int)(B * H), (int)(B * Hkv), (int)N,
+      rotate ? 1 : 0, signs, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_fp8(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                         const void* ws, size_t ws_bytes, int causal, float scale, void* O,
+                         float* LSE, void* stream) {
+  attn_status st = fp8_shape(dt, B, H, Hkv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  const F8Layout L = fp8_layout(B, H, Hkv, N);
+  if (!ws || ws_bytes < L.total) return ATTN_EWORKSPACE;
+  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
+  st = check_ptrs({{ws, L.total}}, {{O, t}, {LSE, s}});
+  if (st != ATTN_OK) return st;
+  const char* w = static_cast<const char*>(ws);
+  return finish(fbd::launch_fwd_fp8(
+      (int)dt, (const uint8_t*)(w + L.off[ATTN_FP8_Q]), (const uint8_t*)(w + L.off[ATTN_FP8_K]),
+      (const uint8_t*)(w + L.off[ATTN_FP8_VT]), (const int*)(w + L.off[ATTN_FP8_EQ]),
+      (const int*)(w + L.off[ATTN_FP8_EK]), (const int*)(w + L.off[ATTN_FP8_EV]), O, LSE,
+      (int)(B * H), (int)H, (int)(H / Hkv), (int)N, causal ? 1 : 0, scale,
+      (hipStream_t)stream));
+}
+
 }  // extern "C"

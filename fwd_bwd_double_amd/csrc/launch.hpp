@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 // Streamed tile sizes (rows of the streamed operand per LDS stage): keys per
 // tile for the row passes (BN), queries per tile for the column passes (BM).
@@ -73,5 +74,19 @@ hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
                       int win, const int* ds, int N, int causal, float scale, int passes,
                       hipStream_t st);
+
+// FP8 forward.  Quantisation pre-pass: E4M3 codes of Q and K (optionally
+// rotated by diag(signs) H / 8 when rotate != 0) with one power-of-two scale
+// exponent per 64 rows of a head, and of V transposed with one exponent per
+// column; VMAX is scratch for the column maxima (BHkv x 64).  The forward
+// reads only the codes and exponents.  Layouts are described in fp8.hip.
+hipError_t launch_fp8_quantize(int dt, const void* Q, const void* K, const void* V, uint8_t* Q8,
+                               uint8_t* K8, uint8_t* V8T, int* EQ, int* EK, int* EV,
+                               uint32_t* VMAX, int BH, int BHkv, int N, int rotate,
+                               uint64_t signs, hipStream_t st);
+hipError_t launch_fwd_fp8(int dt, const uint8_t* Q8, const uint8_t* K8, const uint8_t* V8T,
+                          const int* EQ, const int* EK, const int* EV, void* O, float* LSE,
+                          int BH, int H, int grp, int N, int causal, float scale,
+                          hipStream_t st);
 
 }  // namespace fbd

@@ -259,6 +259,68 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
                      void* Hv_Q, void* Hv_K, void* Hv_V, void* Hv_dO,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 forward with optional incoherent processing.
+ *
+ * The FlashAttention explainer page (marketmaker.cc,
+ * flash-attention-trading-models), section "FA3: the Hopper mechanics",
+ * item 3, describes FP8 attention.  Plain block quantisation is hurt by
+ * outliers, so the vectors are first multiplied by a random orthogonal matrix
+ * that spreads an outlier over all coordinates.  Here that matrix is
+ * R = diag(s) H / 8: H is the 64 x 64 Sylvester Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)) and s_i = -1 where bit i of `signs` is
+ * set.  Since (Q R)(K R)^T = Q K^T, only the rounding changes.
+ *
+ * Format: OCP E4M3 (4 exponent bits, bias 7, 3 mantissa bits, subnormals,
+ * largest finite value 448), rounded to nearest with ties to even.
+ * Scales are powers of two, 2^e with e = floor(log2 amax) - 7 (0 for an
+ * all-zero block), so each block's largest magnitude maps into [128, 256).
+ * Q and K (rotated when rotate != 0) get one exponent per 64 rows of a head;
+ * V (never rotated) gets one per column of a head.  Inputs must be finite,
+ * and the score scale 2^(eq + ek) of a query block and a key block must be
+ * a normal fp32 number.
+ *
+ * Two calls.  attn_fp8_quantize reads Q (B, H, N, 64) and K, V (B, Hkv, N,
+ * 64) of type dt and writes the codes and exponents into the workspace.
+ * attn_fwd_fp8 reads only the workspace and writes O (B, H, N, 64) of type dt
+ * and LSE (B, H, N) fp32, the same outputs as attn_fwd_ex, computed with both
+ * products on the E4M3 matrix cores.  The probabilities are rounded to E4M3
+ * as 256 P against the running row max; l sums the unrounded values.
+ * The workspace is device memory of attn_fp8_workspace_bytes(B, H, Hkv, N)
+ * bytes, 16-byte aligned.  Its parts start at the offsets that
+ * attn_fp8_workspace_layout writes, in the order of attn_fp8_part; each part
+ * is per head, heads in order:
+ *   Q, K   N x 64 uint8 codes, row-major;
+ *   VT     64 x NP uint8 codes (NP = N rounded up to 64): row d is column d
+ *          of V.  Within each group of 64 keys, stored 4-byte word w holds
+ *          keys 4s .. 4s+3 with s = 2 (w % 8) + w / 8.  Keys past N are zero;
+ *   EQ, EK int32 exponent per 64-row block (ceil(N / 64) per head);
+ *   EV     int32 exponent per column (64 per head);
+ *   VMAX   scratch of the pre-pass.
+ * Errors as elsewhere; ATTN_EWORKSPACE for a missing or short workspace.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  ATTN_FP8_Q = 0, ATTN_FP8_K = 1, ATTN_FP8_VT = 2, ATTN_FP8_EQ = 3, ATTN_FP8_EK = 4,
+  ATTN_FP8_EV = 5, ATTN_FP8_VMAX = 6, ATTN_FP8_NPARTS = 7
+} attn_fp8_part;
+
+/* Bytes of the FP8 workspace (0 for non-positive sizes). */
+size_t attn_fp8_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N);
+
+/* Byte offsets of the ATTN_FP8_NPARTS parts of the workspace, written to
+ * offsets[0 .. ATTN_FP8_NPARTS-1] (host array). */
+attn_status attn_fp8_workspace_layout(int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                                      size_t* offsets);
+
+attn_status attn_fp8_quantize(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                              int64_t d, const void* Q, const void* K, const void* V,
+                              int rotate, uint64_t signs, void* ws, size_t ws_bytes,
+                              void* stream);
+
+attn_status attn_fwd_fp8(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                         const void* ws, size_t ws_bytes, int causal, float scale, void* O,
+                         float* LSE, void* stream);
+
 /* Text of a status code (static storage). */
 const char* attn_status_str(attn_status s);
 

@@ -183,6 +183,10 @@ def fwd_fp8(Q, K, V, causal=True, scale=None, signs=None):
                of the absolute error of probabilities rounded in the
                subnormal range (a kernel that quantises 256 P relative to a
                running max adds at most 2^-18 U to O there);
+      A        max over visible keys j of sum_d |Q^_id| |K^_jd|: a sum of
+               the 64 products with relative precision eps errs by at most
+               eps A_i in S_ij, hence by c eps A_i in LSE_i and by a factor
+               of at most 2 c eps A_i in P;
       codes    {"q", "k", "v"} uint8 and {"eq", "ek", "ev"} exponents.
     """
     Q, K, V = (np.asarray(x) for x in (Q, K, V))
@@ -199,6 +203,7 @@ def fwd_fp8(Q, K, V, causal=True, scale=None, signs=None):
     O, LSE = _fwd_exact(qh, kh, vh, causal=causal, scale=c)
     W = np.empty_like(O)
     U = np.empty_like(O)
+    A = np.empty_like(LSE)
     idx = np.arange(N)
     for b in range(B):
         for h in range(H):
@@ -208,5 +213,7 @@ def fwd_fp8(Q, K, V, causal=True, scale=None, signs=None):
             W[b, h] = p @ np.abs(vh[b, h])
             U[b, h] = p.max(axis=1)[:, None] * (np.where(np.isfinite(s), 1.0, 0.0)
                                                @ np.abs(vh[b, h]))
-    return {"O": O, "LSE": LSE, "W": W, "U": U,
+            sa = np.abs(qh[b, h]) @ np.abs(kh[b, h]).T
+            A[b, h] = np.where(np.isfinite(s), sa, 0.0).max(axis=1)
+    return {"O": O, "LSE": LSE, "W": W, "U": U, "A": A, "scale": c,
             "codes": {"q": cq, "k": ck, "v": cv, "eq": eq, "ek": ek, "ev": ev}}

@@ -142,3 +142,27 @@ def make_inputs(w: Workload, which=("q", "k", "v", "do", "g_dq", "g_dk", "g_dv")
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact fp64 copy of a CPU or GPU tensor (bf16 and fp32 widen exactly)."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def fp8_inputs(seed: int, B: int, H: int, Hkv: int, N: int, dtype: str = "bf16",
+               std: float = 1.0, outlier_channels=(), outlier_mag: float = 1.0
+               ) -> Dict[str, torch.Tensor]:
+    """Q (B, H, N, 64), K and V (B, Hkv, N, 64) for the FP8 forward: std * N(0, 1)
+    from the q, k, v streams of ``seed``; the head-dimension channels listed in
+    ``outlier_channels`` of Q and K are multiplied by ``outlier_mag`` before the
+    cast (a few large channels, the outlier pattern rotation is meant for)."""
+    rs = _streams(seed)
+    out = {}
+    for name, heads in (("q", H), ("k", Hkv), ("v", Hkv)):
+        x = rs[name].standard_normal((B, heads, N, 64)) * std
+        if name != "v":
+            for ch in outlier_channels:
+                x[..., ch] *= outlier_mag
+        out[name] = _cast(x, dtype)
+    return out
+
+
+def sign_mask(seed: int) -> int:
+    """A random 64-bit sign mask (the rotation's random signs) from ``seed``."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    return int(rng.integers(0, 2 ** 63)) * 2 + int(rng.integers(0, 2))

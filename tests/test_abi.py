@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "fbd.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +28,9 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"attn_fwd", "attn_bwd", "attn_bob", "attn_bwd_workspace_bytes",
-            "attn_bob_workspace_bytes", "attn_status_str", "attn_last_hip_error"} <= set(names)
+            "attn_bob_workspace_bytes", "attn_status_str", "attn_last_hip_error",
+            "attn_fp8_quantize", "attn_fwd_fp8", "attn_fp8_workspace_bytes",
+            "attn_fp8_workspace_layout"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -111,3 +113,39 @@ def test_extended_forms_reject_bad_heads_and_windows(lib):
     assert call(4, 2, causal=0, ds=FAKE * 7) == 2  # so do document masks
     assert call(4, 2, ds=FAKE * 7 + 2) == 3        # doc_start must be 4-byte aligned
     assert call(4, 2, ds=FAKE * 4) == 1            # and must not overlap an output
+
+
+def test_fp8_workspace_layout(lib):
+    B, H, Hkv, N = 2, 4, 2, 130
+    offs = (ctypes.c_size_t * 7)()
+    assert lib.attn_fp8_workspace_layout(B, H, Hkv, N, offs) == 0
+    nb = 3
+    sizes = [B * H * N * 64, B * Hkv * N * 64, B * Hkv * 64 * nb * 64, B * H * nb * 4,
+             B * Hkv * nb * 4, B * Hkv * 64 * 4, B * Hkv * 64 * 4]
+    for i in range(7):
+        assert offs[i] % 256 == 0
+        end = offs[i] + sizes[i]
+        nxt = offs[i + 1] if i < 6 else fbd.fp8_workspace_bytes(B, H, Hkv, N)
+        assert end <= nxt
+    assert fbd.fp8_workspace_bytes(0, 1, 1, 8) == 0
+    assert lib.attn_fp8_workspace_layout(1, 4, 3, 8, offs) == 1   # Hkv must divide H
+    assert lib.attn_fp8_workspace_layout(1, 1, 1, 8, None) == 1
+
+
+def test_fp8_rejects_bad_arguments_before_launch(lib):
+    B, H, Hkv, N = 1, 2, 1, 64
+    need = fbd.fp8_workspace_bytes(B, H, Hkv, N)
+    q, k, v, ws, o, lse = (FAKE * (i + 1) for i in range(6))
+    ws = FAKE * 64   # far from the inputs: no overlap
+    assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 64, q, k, v, 1, 5, ws, need - 1, None) == 4
+    assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 64, q, k, v, 1, 5, None, need, None) == 4
+    assert lib.attn_fp8_quantize(0, B, H, 3, N, 64, q, k, v, 1, 5, ws, need, None) == 1
+    assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 32, q, k, v, 1, 5, ws, need, None) == 2
+    assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 64, 0, k, v, 1, 5, ws, need, None) == 1
+    assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 64, q + 8, k, v, 1, 5, ws, need, None) == 3
+    # the workspace overlapping an input
+    assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 64, q, k, v, 1, 5, k, need, None) == 1
+    assert lib.attn_fwd_fp8(0, B, H, Hkv, N, 64, ws, need - 1, 1, 0.125, o, lse, None) == 4
+    assert lib.attn_fwd_fp8(0, B, H, Hkv, N, 64, ws, need, 1, 0.0, o, lse, None) == 1
+    assert lib.attn_fwd_fp8(0, B, H, Hkv, N, 64, ws, need, 1, 0.125, ws, lse, None) == 1
+    assert lib.attn_fwd_fp8(7, B, H, Hkv, N, 64, ws, need, 1, 0.125, o, lse, None) == 2
