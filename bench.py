@@ -17,7 +17,8 @@ sample of the same workload on this host.
 
 `--sweep` instead times each operation separately over sequence lengths
 1k .. 256k (H=12, d=64, B = max(1, 16384/N), causal, GProj on) and the other
-workload shapes, printing one JSON line per case.
+workload shapes, printing one JSON line per case; it includes the FP8 forward
+(quantisation pre-pass and the forward on the codes, against the fp8 peak).
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
 HBM_PEAK_GBS = 8000.0
 METRIC = "attn fwd/bwd/BoB TFLOP/s & % bf16 MFMA peak, GPT-2S head shape, N≤262k"
 
@@ -206,6 +208,9 @@ def sweep():
         gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4))
         ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
         ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
+        ws8 = torch.empty(fbd.fp8_workspace_bytes(B, H, H, N), device=dev, dtype=torch.uint8)
+        o8 = torch.empty_like(q)
+        signs = 0x9E3779B97F4A7C15
         sc = 1.0 / 8.0
         ops = {
             "fwd": lambda: fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse),
@@ -213,6 +218,10 @@ def sweep():
                                         workspace=ws_b, outs=(dq, dk, dv)),
             "bob": lambda: fbd.attn_bob(q, k, v, o, lse, do, a, bk, c, causal=True, scale=sc,
                                         workspace=ws_bb, outs=(gq, gk, gv, gdo)),
+            # FP8 forward: the quantisation pre-pass (rotated) and the forward on the codes
+            "fp8_quant": lambda: fbd.attn_fp8_quantize(q, k, v, signs, ws8),
+            "fp8_fwd": lambda: fbd.attn_fwd_fp8_codes(ws8, B, H, H, N, torch.bfloat16, True, sc,
+                                                      out=o8, lse=lse),
         }
         pairs = B * H * N * (N + 1) / 2
         exec_units = {"fwd": UNITS["fwd"], "bwd": UNITS["bwd_row"] + UNITS["bwd_col"],
@@ -229,18 +238,27 @@ def sweep():
             ev[reps].record()
             torch.cuda.synchronize()
             ms = float(np.median([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]))
+            if op == "fp8_quant":
+                # reads Q, K, V (bf16) and V again for its column maxima, writes the codes
+                nbytes = B * H * N * d * (2 * 4 + 3)
+                res[op] = {"ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9}
+                continue
+            peak = PEAK_FP8_TFLOPS if op == "fp8_fwd" else PEAK_BF16_TFLOPS
+            u = exec_units["fwd" if op == "fp8_fwd" else op]
             res[op] = {"ms": ms,
-                       "conv_tflops": CONV[op] * d * pairs / (ms * 1e-3) / 1e12,
-                       "executed_frac_mfma_peak":
-                           exec_units[op] * 2 * d * pairs / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+                       "conv_tflops": CONV["fwd" if op == "fp8_fwd" else op] * d * pairs
+                       / (ms * 1e-3) / 1e12,
+                       "executed_frac_mfma_peak": u * 2 * d * pairs / (ms * 1e-3) / 1e12 / peak}
         line = {"case": name, "B": B, "H": H, "N": N, "d": d, "causal": True, "gproj": True,
                 "dtype": "bf16", "data": "synthetic", "ops": res,
                 "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9}
         print(json.dumps(line), flush=True)
         print(f"[sweep] {name:14s} " + "  ".join(
-            f"{op} {r['ms']:9.3f} ms {r['conv_tflops']:7.1f} TF {100 * r['executed_frac_mfma_peak']:5.1f}%"
+            f"{op} {r['ms']:9.3f} ms " + (f"{r['gbs']:7.0f} GB/s" if "gbs" in r else
+                                          f"{r['conv_tflops']:7.1f} TF "
+                                          f"{100 * r['executed_frac_mfma_peak']:5.1f}%")
             for op, r in res.items()), file=sys.stderr, flush=True)
-        del q, k, v, do, a, bk, c, o, lse, dq, dk, dv, gq, gk, gv, gdo, ws_b, ws_bb
+        del q, k, v, do, a, bk, c, o, lse, dq, dk, dv, gq, gk, gv, gdo, ws_b, ws_bb, ws8, o8
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
 

@@ -380,15 +380,18 @@ def attn_fp8_quantize(q, k, v, signs: Optional[int] = None,
 
 
 def attn_fwd_fp8_codes(workspace: torch.Tensor, B: int, H: int, Hkv: int, N: int,
-                       dtype=torch.bfloat16, causal: bool = True, scale: Optional[float] = None
+                       dtype=torch.bfloat16, causal: bool = True, scale: Optional[float] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
                        ) -> Tuple[torch.Tensor, torch.Tensor]:
     """O (dtype), LSE (fp32) of the forward on the codes of an FP8 workspace."""
     lib = load()
     dev = workspace.device
     if dev.type != "cuda" or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 GPU tensor")
-    o = torch.empty((B, H, N, 64), device=dev, dtype=dtype)
-    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    o = torch.empty((B, H, N, 64), device=dev, dtype=dtype) if out is None else out
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32) if lse is None else lse
+    _check("out", o, o, dtype, (B, H, N, 64))
+    _check("lse", lse, o, torch.float32, (B, H, N))
     c = 0.125 if scale is None else float(scale)
     st = lib.attn_fwd_fp8(_dt(o), B, H, Hkv, N, 64, workspace.data_ptr(), workspace.numel(),
                           1 if causal else 0, c, o.data_ptr(), lse.data_ptr(), _stream(dev))
