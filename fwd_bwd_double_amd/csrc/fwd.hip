@@ -37,7 +37,7 @@ constexpr int FWD_G = FBD_FWD_G;                      // 32-query groups per wav
 constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;    // query rows per workgroup
 
 template <class T, int BN, bool CAUSAL, bool DOCS>
-__global__ __launch_bounds__(FWD_NT) void fwd_kernel(const T* __restrict__ Q,
+__global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,

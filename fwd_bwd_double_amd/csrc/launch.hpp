@@ -17,6 +17,13 @@
 #ifndef FBD_FWD_G
 #define FBD_FWD_G 1
 #endif
+// forward: minimum waves per SIMD the register budget must allow.  At 4 the
+// bf16 kernel fits 128 registers without spilling (the compiler alone picks
+// 138 and 3 waves); the fp32 kernel is held to 2 workgroups per CU by its
+// 64 KB of LDS tiles either way.
+#ifndef FBD_FWD_OCC
+#define FBD_FWD_OCC 4
+#endif
 #ifndef FBD_BWD_BN
 #define FBD_BWD_BN 64
 #endif
