@@ -10,7 +10,7 @@
 // (Q R)(K R)^T = Q K^T.  R is applied to the rows of Q and K only.
 //
 // Two stages:
-//  * a quantisation pre-pass writes E4M3 codes and power-of-two scales 2^e,
+//  * a quantisation pre-pass (three launches) writes E4M3 codes and power-of-two scales 2^e,
 //    with e = floor(log2 amax) - 7.  Q and K get one scale per 64 rows of a
 //    head; V gets one per column of a head, because P V accumulates each
 //    output column over all keys and so needs only one multiply at the end.
@@ -68,15 +68,24 @@ __device__ __forceinline__ float wave_max(float x) {
 // Pre-pass.
 // ---------------------------------------------------------------------------
 
-// Q or K: one wave per 64-row block of one head, one row per lane.
+// Q and K in one launch: one wave per 64-row block of one head, one row per
+// lane; blocks [0, nqb) are Q's, the rest K's.  Workgroup 0 also clears the
+// nvmax column maxima that the V kernels accumulate next on the stream.
 template <class T>
-__global__ __launch_bounds__(64) void fp8_quant_rows_kernel(const T* __restrict__ X,
-                                                            uint8_t* __restrict__ X8,
-                                                            int* __restrict__ E, int N, int nb,
-                                                            int rotate, uint32_t s_lo,
-                                                            uint32_t s_hi) {
-  const int head = blockIdx.x / nb, blk = blockIdx.x % nb;
+__global__ __launch_bounds__(64) void fp8_quant_rows_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, uint8_t* __restrict__ Q8,
+    uint8_t* __restrict__ K8, int* __restrict__ EQ, int* __restrict__ EK,
+    uint32_t* __restrict__ VMAX, int nvmax, int N, int nb, int nqb, int rotate, uint32_t s_lo,
+    uint32_t s_hi) {
+  const bool isq = (int)blockIdx.x < nqb;
+  const int bid = isq ? blockIdx.x : blockIdx.x - nqb;
+  const T* X = isq ? Q : K;
+  uint8_t* X8 = isq ? Q8 : K8;
+  int* E = isq ? EQ : EK;
+  const int head = bid / nb, blk = bid % nb;
   const int lane = threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int i = lane; i < nvmax; i += 64) VMAX[i] = 0u;
   const int row = blk * 64 + lane;
   const bool ok = row < N;
   float x[64];
@@ -139,76 +148,85 @@ __global__ __launch_bounds__(64) void fp8_quant_rows_kernel(const T* __restrict_
   }
 }
 
-__global__ void fp8_zero_kernel(uint32_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-// Column maxima of V: one workgroup per 256 rows of one head, folded into
-// VMAX (zeroed first) with an atomic max on the bit patterns (non-negative
-// floats order like their bits).
+// Column maxima of V: one workgroup per 256 rows of one head, 16-byte loads
+// (a wave reads whole rows), folded into VMAX with an atomic max on the bit
+// patterns (non-negative floats order like their bits).
 template <class T>
 __global__ __launch_bounds__(256) void fp8_vmax_kernel(const T* __restrict__ V,
                                                        uint32_t* __restrict__ VMAX, int N,
                                                        int nch) {
-  __shared__ float red[256];
+  constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte load
+  constexpr int LPR = HD / EPL;               // lanes per row
+  constexpr int RPI = 256 / LPR;              // rows per workgroup iteration
+  __shared__ float red[4][HD];
   const int head = blockIdx.x / nch, ch = blockIdx.x % nch;
-  const int d = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const T* p = V + (size_t)head * N * HD;
-  float am = 0.f;
-  const int r0 = ch * 256;
-  for (int i = 0; i < 64; ++i) {
-    const int r = r0 + rg + 4 * i;
-    if (r < N) am = fmaxf(am, fabsf((float)p[(size_t)r * HD + d]));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cg = tid % LPR, r0 = tid / LPR;
+  const T* p = V + (size_t)head * N * HD + cg * EPL;
+  float m[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) m[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 256 / RPI; ++i) {
+    const int r = ch * 256 + r0 + i * RPI;
+    if (r < N) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p + (size_t)r * HD);
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) m[e] = fmaxf(m[e], fabsf((float)b[e]));
+      } else {
+        const f32x4 f = __builtin_bit_cast(f32x4, u);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) m[e] = fmaxf(m[e], fabsf(f[e]));
+      }
+    }
   }
-  red[threadIdx.x] = am;
+#pragma unroll
+  for (int off = LPR; off < 64; off *= 2)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) m[e] = fmaxf(m[e], __shfl_xor(m[e], off, 64));
+  if (lane < LPR)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) red[wave][cg * EPL + e] = m[e];
   __syncthreads();
-  if (threadIdx.x < 64) {
-    am = fmaxf(fmaxf(red[d], red[64 + d]), fmaxf(red[128 + d], red[192 + d]));
-    atomicMax(&VMAX[(size_t)head * HD + d], __float_as_uint(am));
+  if (tid < HD) {
+    const float am = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    atomicMax(&VMAX[(size_t)head * HD + tid], __float_as_uint(am));
   }
 }
 
-// V codes, transposed: one workgroup per 64-key tile of one head.
+// V codes, transposed: one workgroup per 64-key tile of one head; thread ->
+// column d = tid % 64 and keys 16 kg .. 16 kg + 15 of the tile (kg = tid / 64),
+// so each load instruction of a wave reads one whole row.  The thread's four
+// 4-key words s = 4 kg .. 4 kg + 3 go to stored words 2 kg, 8 + 2 kg, 2 kg + 1,
+// 9 + 2 kg (stored word w holds source word 2 (w % 8) + w / 8).
 template <class T>
 __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const T* __restrict__ V,
                                                           const uint32_t* __restrict__ VMAX,
                                                           uint8_t* __restrict__ V8T,
                                                           int* __restrict__ EV, int N, int NP,
                                                           int ntile) {
-  __shared__ __attribute__((aligned(16))) uint8_t tr[64][68];   // [d][key]
   const int head = blockIdx.x / ntile, t = blockIdx.x % ntile;
-  const int tid = threadIdx.x;
-  {
-    const int r = tid >> 2, c0 = 16 * (tid & 3);
-    const int key = t * 64 + r;
-    const T* p = V + ((size_t)head * N + key) * HD + c0;
+  const int d = threadIdx.x & 63, kg = threadIdx.x >> 6;
+  const int e = blk_exp(__uint_as_float(VMAX[(size_t)head * HD + d]));
+  if (t == 0 && kg == 0) EV[(size_t)head * HD + d] = e;
+  const int k0 = t * 64 + kg * 16;
+  const T* p = V + (size_t)head * N * HD + d;
+  int w[4];
 #pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      int e[4];
-      float x[4];
+  for (int s = 0; s < 4; ++s) {
+    float x[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        e[k] = blk_exp(__uint_as_float(VMAX[(size_t)head * HD + c0 + i + k]));
-        x[k] = key < N ? __builtin_amdgcn_ldexpf((float)p[i + k], -e[k]) : 0.f;
-      }
-      const int w = f8x4(x[0], x[1], x[2], x[3]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) tr[c0 + i + k][r] = (uint8_t)(w >> (8 * k));
-      if (t == 0 && r == 0)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) EV[(size_t)head * HD + c0 + i + k] = e[k];
+    for (int b = 0; b < 4; ++b) {
+      const int key = k0 + 4 * s + b;
+      x[b] = key < N ? __builtin_amdgcn_ldexpf((float)p[(size_t)key * HD], -e) : 0.f;
     }
+    w[s] = f8x4(x[0], x[1], x[2], x[3]);
   }
-  __syncthreads();
-  const int d = tid >> 2, w0 = 4 * (tid & 3);
-  i32x4 out;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int w = w0 + k, s = 2 * (w % 8) + w / 8;
-    out[k] = *reinterpret_cast<const int*>(&tr[d][4 * s]);
-  }
-  *reinterpret_cast<i32x4*>(V8T + ((size_t)head * HD + d) * NP + t * 64 + 4 * w0) = out;
+  uint8_t* row = V8T + ((size_t)head * HD + d) * NP + t * 64;
+  *reinterpret_cast<int2*>(row + 8 * kg) = make_int2(w[0], w[2]);
+  *reinterpret_cast<int2*>(row + 32 + 8 * kg) = make_int2(w[1], w[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -253,7 +271,7 @@ __device__ __forceinline__ f32x16 splat16(float x) {
 constexpr int F8_BLK = 128;   // query rows per workgroup: 4 waves x 32
 
 template <class T, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_fp8_kernel(
+__global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
     const uint8_t* __restrict__ V8T, const int* __restrict__ EQ, const int* __restrict__ EK,
     const int* __restrict__ EV, T* __restrict__ O, float* __restrict__ LSE, int N, int NP,
@@ -397,12 +415,9 @@ hipError_t launch_fp8_quantize(int dt, const void* Q, const void* K, const void*
   const uint32_t lo = (uint32_t)signs, hi = (uint32_t)(signs >> 32);
   auto run = [&](auto tag) -> hipError_t {
     using T = decltype(tag);
-    hipLaunchKernelGGL(fp8_zero_kernel, dim3((BHkv * HD + 255) / 256), dim3(256), 0, st, VMAX,
-                       BHkv * HD);
-    hipLaunchKernelGGL(fp8_quant_rows_kernel<T>, dim3(BH * nb), dim3(64), 0, st, (const T*)Q,
-                       Q8, EQ, N, nb, rotate, lo, hi);
-    hipLaunchKernelGGL(fp8_quant_rows_kernel<T>, dim3(BHkv * nb), dim3(64), 0, st, (const T*)K,
-                       K8, EK, N, nb, rotate, lo, hi);
+    hipLaunchKernelGGL(fp8_quant_rows_kernel<T>, dim3((BH + BHkv) * nb), dim3(64), 0, st,
+                       (const T*)Q, (const T*)K, Q8, K8, EQ, EK, VMAX, BHkv * HD, N, nb, BH * nb,
+                       rotate, lo, hi);
     hipLaunchKernelGGL(fp8_vmax_kernel<T>, dim3(BHkv * nch), dim3(256), 0, st, (const T*)V, VMAX,
                        N, nch);
     hipLaunchKernelGGL(fp8_quant_v_kernel<T>, dim3(BHkv * nb), dim3(256), 0, st, (const T*)V,

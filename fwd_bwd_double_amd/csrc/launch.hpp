@@ -24,6 +24,11 @@
 #ifndef FBD_FWD_OCC
 #define FBD_FWD_OCC 4
 #endif
+// FP8 forward: minimum waves per SIMD (1: the compiler's choice, 132
+// registers and 3 waves; 4 waves measured no faster)
+#ifndef FBD_FP8_OCC
+#define FBD_FP8_OCC 1
+#endif
 #ifndef FBD_BWD_BN
 #define FBD_BWD_BN 64
 #endif
