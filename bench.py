@@ -15,6 +15,9 @@ sample of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 
+`--fp8` times the FP8 forward (rotated quantisation pre-pass + E4M3 forward)
+on the same workload instead of the step, one JSON line.
+
 `--sweep` instead times each operation separately over sequence lengths
 1k .. 256k (H=12, d=64, B = max(1, 16384/N), causal, GProj on) and the other
 workload shapes, printing one JSON line per case; it includes the FP8 forward
@@ -54,6 +57,9 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="time fwd, bwd and BoB separately over N = 1k .. 256k and the other "
                         "workload shapes (one JSON line per case) instead of the step")
+    p.add_argument("--fp8", action="store_true",
+                   help="time the FP8 forward (rotated quantisation pre-pass + E4M3 forward) on "
+                        "the step's workload instead of the step (one JSON line)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a plain copy "
                         "kernel of known size, to calibrate memory counters)")
@@ -64,6 +70,8 @@ def main():
     args = parse()
     if args.sweep and args.gpus == 1:
         return sweep()
+    if args.fp8 and args.gpus == 1:
+        return fp8_bench(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(heads would shard across GPUs with no exchange); run with --gpus 1",
@@ -171,6 +179,72 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "per_kernel": per_kernel, "per_op": per_op,
         "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def fp8_bench(args):
+    """The FP8 forward on the step's workload (B4 H12 N4096, causal, bf16 Q, K,
+    V from its seeded generator, rotation signs from its seed): W untimed then
+    K timed repetitions of the rotated quantisation pre-pass followed by the
+    E4M3 forward, each launch bracketed by HIP events on the launch stream.
+    `value` is the forward's model TFLOP/s (4d per unmasked pair) over the
+    whole (pre-pass + forward); `per_op` gives each part, the forward against
+    the 5 PFLOP/s fp8 peak and the pre-pass in GB/s of its algorithmic bytes
+    (11 per element: Q, K, V read, V read again for its column maxima, codes
+    written)."""
+    import numpy as np
+    import torch
+
+    import fwd_bwd_double_amd as fbd
+    import synthetic
+
+    w = synthetic.WORKLOADS[4]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = synthetic.make_inputs(w, ("q", "k", "v"))
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    signs = synthetic.sign_mask(w.seed)
+    ws = torch.empty(fbd.fp8_workspace_bytes(B, H, H, N), device=dev, dtype=torch.uint8)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+
+    def once(ev):
+        ev[0].record()
+        fbd.attn_fp8_quantize(q, k, v, signs, ws)
+        ev[1].record()
+        fbd.attn_fwd_fp8_codes(ws, B, H, H, N, torch.bfloat16, True, w.scale, out=o, lse=lse)
+        ev[2].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.warmup + args.steps)]
+    for i in range(args.warmup):
+        once(evs[i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        once(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    timed = evs[args.warmup:]
+    qms = float(np.mean([e[0].elapsed_time(e[1]) for e in timed]))
+    fms = float(np.mean([e[1].elapsed_time(e[2]) for e in timed]))
+    pairs = B * H * N * (N + 1) / 2
+    conv = CONV["fwd"] * d * pairs
+    line = {
+        "metric": "fp8 attention forward TFLOP/s (rotated E4M3 pre-pass + forward)",
+        "value": conv / wall / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3", "data": "synthetic",
+        "config": {"workload": w.name + " forward", "B": B, "H": H, "N": N, "d": d,
+                   "causal": True, "rotation": True},
+        "per_op": {
+            "quantize": {"ms": qms, "gbs": B * H * N * d * 11 / (qms * 1e-3) / 1e9},
+            "fwd_fp8": {"ms": fms, "conv_tflops": conv / (fms * 1e-3) / 1e12,
+                        "executed_frac_fp8_peak":
+                            UNITS["fwd"] * 2 * d * pairs / (fms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
+        },
     }
     print(json.dumps(line), flush=True)
 
