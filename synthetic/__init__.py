@@ -166,3 +166,11 @@ def sign_mask(seed: int) -> int:
     """A random 64-bit sign mask (the rotation's random signs) from ``seed``."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     return int(rng.integers(0, 2 ** 63)) * 2 + int(rng.integers(0, 2))
+
+
+def rademacher(seed: int, shape, dtype: str = "fp32") -> torch.Tensor:
+    """Independent random signs (+1 / -1) of the given shape from ``seed``: the
+    probes of a Hutchinson estimate of a Hessian diagonal."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    x = np.where(rng.integers(0, 2, size=shape) == 1, 1.0, -1.0)
+    return _cast(x, dtype)

@@ -371,3 +371,32 @@ def test_gproj_model_large_key_regime():
     assert plain > 0.05
     assert proj < 0.01
     assert proj < plain / 10
+
+
+def test_hutchinson_average_over_all_sign_vectors_is_the_hessian_diagonal():
+    """Hutchinson's estimate diag(H) ~ mean of z o (H z) over random sign
+    vectors z (the estimate second-order methods such as Sophia-H build on the
+    FlashBoB page's Hessian-vector products) is exact when the mean runs over
+    all 2^n sign vectors: E[z_i z_j] = [i = j].  Checked on a problem small
+    enough to enumerate them (n = 3 N d = 6) against the diagonal from the
+    Hessian's columns H e_j."""
+    import itertools
+    rng = np.random.default_rng(99)
+    N, d = 2, 1
+    Q, K, V, dO = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    n = 3 * N * d
+
+    def hv(vec):
+        vq, vk, vv = (vec[i * N * d:(i + 1) * N * d].reshape(1, 1, N, d) for i in range(3))
+        r = oracle.hvp(Q, K, V, dO, vq, vk, vv, causal=False)
+        return np.concatenate([r["HvQ"].ravel(), r["HvK"].ravel(), r["HvV"].ravel()])
+
+    Hm = np.stack([hv(e) for e in np.eye(n)], axis=1)
+    np.testing.assert_allclose(Hm, Hm.T, atol=1e-12)       # a Hessian is symmetric
+    est = np.zeros(n)
+    for signs in itertools.product((-1.0, 1.0), repeat=n):
+        z = np.array(signs)
+        est += z * hv(z)
+    est /= 2 ** n
+    np.testing.assert_allclose(est, np.diag(Hm), rtol=0, atol=1e-12)
+    assert np.abs(np.diag(Hm)).max() > 1e-3                # not trivially zero
