@@ -42,12 +42,15 @@ def _f64(x):
 
 
 def _visible(rows_idx: np.ndarray, ncols: int, causal: bool, window: int = 0,
-             starts=None) -> np.ndarray:
+             starts=None, blocks=None) -> np.ndarray:
     """Boolean (len(rows_idx), ncols): True where query rows_idx[a] sees key j:
     j <= i when causal, and additionally j > i - window for a sliding window
     (window > 0) and j >= starts[i] for document masks (starts: this batch
-    row's first position of each query's document).  Both are flexible masks
-    the FlashBoB page names among its next extensions (closing paragraph)."""
+    row's first position of each query's document); blocks (this batch row's
+    (nb, nb) block-sparse mask over 128 x 128 blocks) further hides key j
+    from query i where blocks[i // 128, j // 128] == 0.  These are the
+    flexible masks the FlashBoB page names among its next extensions (closing
+    paragraph)."""
     j = np.arange(ncols)[None, :]
     if causal:
         vis = j <= rows_idx[:, None]
@@ -55,26 +58,34 @@ def _visible(rows_idx: np.ndarray, ncols: int, causal: bool, window: int = 0,
             vis &= j > rows_idx[:, None] - window
         if starts is not None:
             vis &= j >= np.asarray(starts)[rows_idx][:, None]
-        return vis
-    assert window == 0 and starts is None, "window and document masks need the causal mask"
-    return np.ones((rows_idx.size, ncols), dtype=bool)
+    else:
+        assert window == 0 and starts is None, "window and document masks need the causal mask"
+        vis = np.ones((rows_idx.size, ncols), dtype=bool)
+    if blocks is not None:
+        bl = np.asarray(blocks) != 0
+        vis &= bl[rows_idx // 128][:, np.arange(ncols) // 128]
+    return vis
 
 
-def _row_softmax(q_rows, k, rows_idx, causal, scale, window=0, starts=None):
+def _row_softmax(q_rows, k, rows_idx, causal, scale, window=0, starts=None, blocks=None):
     """P rows and LSE for the given query rows against keys k.
 
     m_i is the row max of the raw scores over visible keys; the exponent is
     taken as c * (S - m), i.e. the max is subtracted before scaling, so the
     largest entry is exactly exp(0) = 1 (GProj page, section "Why the error
-    shows up at the end of training").  LSE_i = c m_i + ln l_i."""
+    shows up at the end of training").  LSE_i = c m_i + ln l_i.  A row with
+    no visible key (possible only under a block-sparse mask) is the empty
+    softmax: P = 0 and LSE = -inf (the log of an empty sum)."""
     s = q_rows @ k.T
-    vis = _visible(rows_idx, k.shape[0], causal, window, starts)
+    vis = _visible(rows_idx, k.shape[0], causal, window, starts, blocks)
+    empty = ~vis.any(axis=1)
     s_vis = np.where(vis, s, -np.inf)
-    m = s_vis.max(axis=1, keepdims=True)
+    m = np.where(empty[:, None], 0.0, s_vis.max(axis=1, keepdims=True))
     e = np.exp(scale * (s_vis - m))        # masked keys: exp(-inf) = 0
     l = e.sum(axis=1, keepdims=True)
-    p = e / l
-    lse = scale * m[:, 0] + np.log(l[:, 0])
+    p = e / np.where(empty[:, None], 1.0, l)
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, scale * m[:, 0] + np.log(l[:, 0]))
     return p, lse
 
 
@@ -111,7 +122,7 @@ def max_prob(Q, K, causal=True, scale=None, heads=None, row_idx=None, chunk=1024
 
 
 def _head(q, k, v, do, a, bk, cv, rows_idx, causal, c, want_bwd, want_bob, window=0,
-          starts=None):
+          starts=None, blocks=None):
     """All outputs of one head for the query rows ``rows_idx``.
 
     Row outputs (O, LSE, D, dQ, alpha, beta, gQ, gdO) are complete for those
@@ -122,7 +133,7 @@ def _head(q, k, v, do, a, bk, cv, rows_idx, causal, c, want_bwd, want_bob, windo
         ncols = int(rows_idx.max()) + 1
     kk, vv = k[:ncols], v[:ncols]
     qr = q[rows_idx]
-    p, lse = _row_softmax(qr, kk, rows_idx, causal, c, window, starts)
+    p, lse = _row_softmax(qr, kk, rows_idx, causal, c, window, starts, blocks)
     o = p @ vv
     r = {"O": o, "LSE": lse}
     if not (want_bwd or want_bob):
@@ -140,7 +151,7 @@ def _head(q, k, v, do, a, bk, cv, rows_idx, causal, c, want_bwd, want_bob, windo
     if want_bob:
         ar = a[rows_idx]
         bkk, cc = bk[:ncols], cv[:ncols]
-        vis = _visible(rows_idx, ncols, causal, window, starts)
+        vis = _visible(rows_idx, ncols, causal, window, starts, blocks)
         # Phi = <A, dQ> + <Bk, dK> + <C, dV> = <dS, W> + <P, U>
         W = np.where(vis, c * (ar @ kk.T + qr @ bkk.T), 0.0)
         U = np.where(vis, dor @ cc.T, 0.0)
@@ -165,7 +176,8 @@ _COL_KEYS = ("dK", "dV", "gK", "gV")
 
 
 def _run(Q, K, V, dO=None, A=None, Bk=None, C=None, causal=True, scale=None,
-         want_bwd=False, want_bob=False, chunk=1024, heads=None, window=0, docs=None):
+         want_bwd=False, want_bob=False, chunk=1024, heads=None, window=0, docs=None,
+         block_mask=None):
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, H, N, d = Q.shape
     c = 1.0 / np.sqrt(d) if scale is None else float(scale)
@@ -194,7 +206,8 @@ def _run(Q, K, V, dO=None, A=None, Bk=None, C=None, causal=True, scale=None,
         for r0 in range(0, N, chunk):
             idx = np.arange(r0, min(N, r0 + chunk))
             r, ncols = _head(*args, idx, causal, c, want_bwd, want_bob, window,
-                             None if docs is None else np.asarray(docs)[b])
+                             None if docs is None else np.asarray(docs)[b],
+                             None if block_mask is None else np.asarray(block_mask)[b])
             for key, val in r.items():
                 if key in _ROW_KEYS:
                     out[key][b, h, idx] = val
@@ -203,23 +216,25 @@ def _run(Q, K, V, dO=None, A=None, Bk=None, C=None, causal=True, scale=None,
     return out
 
 
-def fwd(Q, K, V, causal=True, scale=None, heads=None, chunk=1024, window=0, docs=None):
+def fwd(Q, K, V, causal=True, scale=None, heads=None, chunk=1024, window=0, docs=None,
+        block_mask=None):
     """O = softmax(c Q K^T + mask) V and LSE_i = c m_i + ln l_i per row."""
     r = _run(Q, K, V, causal=causal, scale=scale, chunk=chunk, heads=heads, window=window,
-             docs=docs)
+             docs=docs, block_mask=block_mask)
     return r["O"], r["LSE"]
 
 
-def bwd(Q, K, V, dO, causal=True, scale=None, heads=None, chunk=1024, window=0, docs=None):
+def bwd(Q, K, V, dO, causal=True, scale=None, heads=None, chunk=1024, window=0, docs=None,
+        block_mask=None):
     """Gradients of <dO, O(Q, K, V)>:  dP = dO V^T, D = rowsum(dO o O),
     dS = P o (dP - D), dQ = c dS K, dK = c dS^T Q, dV = P^T dO.
     Returns dict with O, LSE, D, dQ, dK, dV."""
     return _run(Q, K, V, dO, causal=causal, scale=scale, want_bwd=True,
-                heads=heads, chunk=chunk, window=window, docs=docs)
+                heads=heads, chunk=chunk, window=window, docs=docs, block_mask=block_mask)
 
 
 def bob(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, heads=None,
-        chunk=1024, with_bwd=False, window=0, docs=None):
+        chunk=1024, with_bwd=False, window=0, docs=None, block_mask=None):
     """Backward-over-backward: the gradient of
     Phi = <gdQ, dQ> + <gdK, dK> + <gdV, dV> with respect to (Q, K, V, dO),
     where (dQ, dK, dV) is the first backward of ``bwd``.  With A = gdQ,
@@ -234,7 +249,7 @@ def bob(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, heads=None,
     O, LSE, D, alpha, beta, gQ, gK, gV, gdO (and dQ, dK, dV if with_bwd)."""
     return _run(Q, K, V, dO, gdQ, gdK, gdV, causal=causal, scale=scale,
                 want_bwd=with_bwd, want_bob=True, heads=heads, chunk=chunk, window=window,
-                docs=docs)
+                docs=docs, block_mask=block_mask)
 
 
 def hvp(Q, K, V, dO, vQ, vK, vV, causal=True, scale=None, heads=None, chunk=1024):
@@ -275,28 +290,29 @@ def _group(Q, K):
     return H // Hkv
 
 
-def fwd_gqa(Q, K, V, causal=True, scale=None, window=0, docs=None):
+def fwd_gqa(Q, K, V, causal=True, scale=None, window=0, docs=None, block_mask=None):
     g = _group(Q, K)
     return fwd(Q, expand_kv(K, g), expand_kv(V, g), causal=causal, scale=scale, window=window,
-               docs=docs)
+               docs=docs, block_mask=block_mask)
 
 
-def bwd_gqa(Q, K, V, dO, causal=True, scale=None, window=0, docs=None):
+def bwd_gqa(Q, K, V, dO, causal=True, scale=None, window=0, docs=None, block_mask=None):
     g = _group(Q, K)
     r = bwd(Q, expand_kv(K, g), expand_kv(V, g), dO, causal=causal, scale=scale, window=window,
-            docs=docs)
+            docs=docs, block_mask=block_mask)
     r["dK"], r["dV"] = reduce_kv(r["dK"], g), reduce_kv(r["dV"], g)
     return r
 
 
 def bob_gqa(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, with_bwd=False, window=0,
-            docs=None):
+            docs=None, block_mask=None):
     """BoB of the grouped-query map: <gdK, dK> with dK summed over a group is
     <expand(gdK), dK per query head>, so the cotangents expand like K and V
     and the key-side outputs reduce like dK, dV."""
     g = _group(Q, K)
     r = bob(Q, expand_kv(K, g), expand_kv(V, g), dO, gdQ, expand_kv(gdK, g), expand_kv(gdV, g),
-            causal=causal, scale=scale, with_bwd=with_bwd, window=window, docs=docs)
+            causal=causal, scale=scale, with_bwd=with_bwd, window=window, docs=docs,
+            block_mask=block_mask)
     for k in ("gK", "gV") + (("dK", "dV") if with_bwd else ()):
         r[k] = reduce_kv(r[k], g)
     return r

@@ -192,6 +192,76 @@ def test_document_mask_against_torch_and_independent_documents():
             assert np.allclose(r[k][..., sl, :], own[k], rtol=1e-12, atol=1e-13), (k, lo)
 
 
+def _torch_masked_double_backward(Q, K, V, dO, A, Bk, C, hide, c):
+    """fp64 torch autograd: outputs and BoB of softmax attention with an
+    explicit boolean mask (True hides), query rows Q may be a subset."""
+    tq, tk, tv, tdo = (torch.tensor(x, requires_grad=True) for x in (Q, K, V, dO))
+    s_ = (c * (tq @ tk.transpose(-1, -2))).masked_fill(torch.from_numpy(hide), float("-inf"))
+    out = torch.softmax(s_, dim=-1) @ tv
+    gq, gk, gv = torch.autograd.grad(out, (tq, tk, tv), tdo, create_graph=True)
+    phi_ = (gq * torch.from_numpy(A)).sum() + (gk * torch.from_numpy(Bk)).sum() + \
+        (gv * torch.from_numpy(C)).sum()
+    hq, hk, hv, hdo = torch.autograd.grad(phi_, (tq, tk, tv, tdo))
+    return {k: t.detach().numpy() for k, t in (("O", out), ("dQ", gq), ("dK", gk), ("dV", gv),
+                                               ("gQ", hq), ("gK", hk), ("gV", hv),
+                                               ("gdO", hdo))}
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_sparse_mask_against_torch_double_backward(causal):
+    # a (B, nb, nb) mask over 128 x 128 blocks (N = 300: blocks of 128, 128
+    # and 44 rows), expanded to an explicit element mask for torch; every row
+    # keeps a visible key (diagonal blocks kept when causal)
+    N, d = 300, 8
+    Q, K, V, dO, A, Bk, C = inputs(1, 2, N, d, 141)
+    c = 1 / math.sqrt(d)
+    bm = np.array([[[1, 0, 1], [0, 1, 0], [1, 1, 1]]], dtype=np.uint8)
+    if not causal:
+        bm[0, 1, 2] = 1
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    hide = bm[0][i // 128, j // 128] == 0
+    if causal:
+        hide |= j > i
+    ref = _torch_masked_double_backward(Q, K, V, dO, A, Bk, C, hide, c)
+    r = oracle.bob(Q, K, V, dO, A, Bk, C, causal=causal, with_bwd=True, block_mask=bm)
+    o, _ = oracle.fwd(Q, K, V, causal=causal, block_mask=bm)
+    assert np.linalg.norm(o - ref["O"]) <= 1e-12 * np.linalg.norm(o)
+    for k in ("dQ", "dK", "dV", "gQ", "gK", "gV", "gdO"):
+        assert np.linalg.norm(r[k] - ref[k]) <= 1e-12 * max(1.0, np.linalg.norm(ref[k])), k
+    # a mask of ones is no mask, bit for bit
+    ones = np.ones((1, 3, 3), dtype=np.uint8)
+    full = oracle.bob(Q, K, V, dO, A, Bk, C, causal=causal, with_bwd=True)
+    same = oracle.bob(Q, K, V, dO, A, Bk, C, causal=causal, with_bwd=True, block_mask=ones)
+    for k in full:
+        assert np.array_equal(full[k], same[k]), k
+
+
+def test_block_sparse_empty_rows():
+    # query block 0 keeps no key block: its rows are empty softmax rows (O = 0,
+    # LSE = -inf, zero row gradients) and contribute nothing to the key side;
+    # the other rows and the key-side outputs equal torch on the remaining
+    # query rows against all keys
+    N, d = 300, 8
+    Q, K, V, dO, A, Bk, C = inputs(1, 1, N, d, 142)
+    c = 1 / math.sqrt(d)
+    bm = np.array([[[0, 0, 0], [1, 0, 1], [0, 1, 1]]], dtype=np.uint8)
+    r = oracle.bob(Q, K, V, dO, A, Bk, C, causal=False, with_bwd=True, block_mask=bm)
+    assert np.all(r["O"][..., :128, :] == 0) and np.all(np.isneginf(r["LSE"][..., :128]))
+    for k in ("dQ", "gQ", "gdO"):
+        assert np.all(r[k][..., :128, :] == 0), k
+    i = np.arange(128, N)[:, None]
+    j = np.arange(N)[None, :]
+    hide = bm[0][i // 128, j // 128] == 0
+    sub = slice(128, N)
+    ref = _torch_masked_double_backward(Q[..., sub, :], K, V, dO[..., sub, :], A[..., sub, :],
+                                        Bk, C, hide, c)
+    for k in ("O", "dQ", "gQ", "gdO"):
+        assert np.linalg.norm(r[k][..., sub, :] - ref[k]) <= 1e-12 * np.linalg.norm(ref[k]), k
+    for k in ("dK", "dV", "gK", "gV"):
+        assert np.linalg.norm(r[k] - ref[k]) <= 1e-12 * np.linalg.norm(ref[k]), k
+
+
 def test_window_of_one_closed_form_and_wide_window_is_causal():
     Q, K, V, dO, A, Bk, C = inputs(1, 1, 9, 4, 138)
     c = 0.5
