@@ -263,11 +263,14 @@ def sweep():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cases = [("gpt2s-layer", 8, 12, 1024), ("large-key", 1, 12, 16384)]
-    cases += [(f"sweep-N{n}", max(1, 16384 // n), 12, n)
+    cases = [("gpt2s-layer", 8, 12, 1024, 0.0), ("large-key", 1, 12, 16384, 0.0)]
+    cases += [(f"sweep-N{n}", max(1, 16384 // n), 12, n, 0.0)
               for n in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
+    # block-sparse: each 128 x 128 block below the diagonal kept with
+    # probability 1/2 (seeded), diagonal blocks kept
+    cases += [("bsparse-N16384", 1, 12, 16384, 0.5)]
     d = 64
-    for name, B, H, N in cases:
+    for name, B, H, N, density in cases:
         gen = torch.Generator(device=dev)
         gen.manual_seed(1000 + N)
 
@@ -282,22 +285,33 @@ def sweep():
         gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4))
         ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
         ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
+        bm, pairs = None, B * H * N * (N + 1) / 2
+        if density:
+            nb = (N + 127) // 128
+            rng = np.random.default_rng(2024)
+            keep = (rng.random((B, nb, nb)) < density) | np.eye(nb, dtype=bool)[None]
+            bm = torch.from_numpy(keep.astype(np.uint8)).to(dev)
+            pairs = H * float((np.tril(keep.astype(np.float64), -1)).sum() * 128 * 128 +
+                              keep[:, np.arange(nb), np.arange(nb)].sum() * 128 * 129 / 2)
         ws8 = torch.empty(fbd.fp8_workspace_bytes(B, H, H, N), device=dev, dtype=torch.uint8)
         o8 = torch.empty_like(q)
         signs = 0x9E3779B97F4A7C15
         sc = 1.0 / 8.0
         ops = {
-            "fwd": lambda: fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse),
+            "fwd": lambda: fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse,
+                                        block_mask=bm),
             "bwd": lambda: fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=sc, gproj=True,
-                                        workspace=ws_b, outs=(dq, dk, dv)),
+                                        workspace=ws_b, outs=(dq, dk, dv), block_mask=bm),
             "bob": lambda: fbd.attn_bob(q, k, v, o, lse, do, a, bk, c, causal=True, scale=sc,
-                                        workspace=ws_bb, outs=(gq, gk, gv, gdo)),
+                                        workspace=ws_bb, outs=(gq, gk, gv, gdo), block_mask=bm),
             # FP8 forward: the quantisation pre-pass (rotated) and the forward on the codes
             "fp8_quant": lambda: fbd.attn_fp8_quantize(q, k, v, signs, ws8),
             "fp8_fwd": lambda: fbd.attn_fwd_fp8_codes(ws8, B, H, H, N, torch.bfloat16, True, sc,
                                                       out=o8, lse=lse),
         }
-        pairs = B * H * N * (N + 1) / 2
+        if density:   # the FP8 forward takes no block mask
+            ops.pop("fp8_quant")
+            ops.pop("fp8_fwd")
         exec_units = {"fwd": UNITS["fwd"], "bwd": UNITS["bwd_row"] + UNITS["bwd_col"],
                       "bob": UNITS["bob_row"] + UNITS["bob_col"]}
         reps = 3 if N >= 65536 else 10
@@ -324,6 +338,7 @@ def sweep():
                        / (ms * 1e-3) / 1e12,
                        "executed_frac_mfma_peak": u * 2 * d * pairs / (ms * 1e-3) / 1e12 / peak}
         line = {"case": name, "B": B, "H": H, "N": N, "d": d, "causal": True, "gproj": True,
+                "block_density": density, "pairs": pairs,
                 "dtype": "bf16", "data": "synthetic", "ops": res,
                 "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9}
         print(json.dumps(line), flush=True)
@@ -341,7 +356,7 @@ def sweep():
 # these files are unchanged since the counters were taken.
 KERNEL_SOURCES = {
     "fwd": ["fwd.hip"], "bwd_row": ["bwd.hip"], "bwd_col": ["bwd.hip"],
-    "bob_row": ["bob.hip"], "bob_col": ["bob.hip"],
+    "bob_row": ["bob_kernels.hpp", "bob.hip"], "bob_col": ["bob_kernels.hpp", "bob.hip"],
 }
 COMMON_SOURCES = ["tile.hpp", "launch.hpp", "../build.py"]
 

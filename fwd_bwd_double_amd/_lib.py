@@ -66,15 +66,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_passes.restype = i32
     lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
     lib.attn_bob_passes.restype = i32
-    # extended forms: Hkv after H, the window after causal
-    lib.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, vp, f32, vp,
-                                vp, vp]
+    # extended forms: Hkv after H; the window, doc_start and block_mask after causal
+    lib.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, vp, vp, f32,
+                                vp, vp, vp]
     lib.attn_fwd_ex.restype = i32
     a = lib.attn_bwd.argtypes
-    lib.attn_bwd_ex.argtypes = a[:3] + [i64] + a[3:12] + [i64, vp] + a[12:]
+    lib.attn_bwd_ex.argtypes = a[:3] + [i64] + a[3:12] + [i64, vp, vp] + a[12:]
     lib.attn_bwd_ex.restype = i32
     a = lib.attn_bob.argtypes
-    lib.attn_bob_ex.argtypes = a[:3] + [i64] + a[3:15] + [i64, vp] + a[15:]
+    lib.attn_bob_ex.argtypes = a[:3] + [i64] + a[3:15] + [i64, vp, vp] + a[15:]
     lib.attn_bob_ex.restype = i32
     lib.attn_hvp_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_hvp_workspace_bytes.restype = sz
@@ -146,6 +146,17 @@ def _kv_shape(q: torch.Tensor, Hkv: int):
     return (B, Hkv, N, d)
 
 
+def _bmask(q: torch.Tensor, block_mask) -> Optional[int]:
+    """Device pointer of a (B, nb, nb) uint8 block mask (nb = ceil(N / 128)),
+    or None."""
+    if block_mask is None:
+        return None
+    B, _, N, _ = q.shape
+    nb = (N + 127) // 128
+    _check("block_mask", block_mask, q, torch.uint8, (B, nb, nb))
+    return block_mask.data_ptr()
+
+
 def _docs(q: torch.Tensor, doc_start) -> Optional[int]:
     """Device pointer of a (B, N) int32 doc_start tensor, or None."""
     if doc_start is None:
@@ -173,13 +184,15 @@ def hvp_workspace_bytes(B: int, H: int, N: int) -> int:
 
 def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             window: int = 0, doc_start: Optional[torch.Tensor] = None
-             ) -> Tuple[torch.Tensor, torch.Tensor]:
+             window: int = 0, doc_start: Optional[torch.Tensor] = None,
+             block_mask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """O, LSE = attention(q, k, v); q shaped (B, H, N, d), k and v (B, Hkv, N, d)
     with H % Hkv == 0 (Hkv < H: grouped-query attention), bf16 or fp32.
     window > 0 (causal only): query i sees keys i - window < j <= i.
     doc_start (causal only): (B, N) int32 first position of each query's
-    document (packed sequences; non-decreasing, doc_start[b, i] <= i)."""
+    document (packed sequences; non-decreasing, doc_start[b, i] <= i).
+    block_mask: (B, nb, nb) uint8, nb = ceil(N / 128); a zero hides the
+    128 x 128 block (query block, key block) on top of the other masks."""
     lib = load()
     _check("q", q, q)
     Hkv = _kv_heads(q, k)
@@ -191,7 +204,8 @@ def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
     _check("out", out, q)
     _check("lse", lse, q, torch.float32, (B, H, N))
     st = lib.attn_fwd_ex(_dt(q), B, H, Hkv, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                         1 if causal else 0, int(window), _docs(q, doc_start), _scale(q, scale),
+                         1 if causal else 0, int(window), _docs(q, doc_start),
+                         _bmask(q, block_mask), _scale(q, scale),
                          out.data_ptr(), lse.data_ptr(), _stream(q.device))
     _raise("attn_fwd", st)
     return out, lse
@@ -199,7 +213,8 @@ def attn_fwd(q, k, v, causal: bool = True, scale: Optional[float] = None,
 
 def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
              gproj: bool = False, workspace: Optional[torch.Tensor] = None, outs=None,
-             passes: int = 3, window: int = 0, doc_start: Optional[torch.Tensor] = None
+             passes: int = 3, window: int = 0, doc_start: Optional[torch.Tensor] = None,
+             block_mask: Optional[torch.Tensor] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV of <dO, O>.  `workspace` (fp32, >= bwd_workspace_bytes) holds
     the row states D, r and -LSE*log2(e), each B*H*N floats, afterwards.
@@ -220,7 +235,7 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
     _check("dq", dq, q)
     for n, t in (("dk", dk), ("dv", dv)):
         _check(n, t, q, shape=kvs)
-    ext = Hkv != H or window != 0 or doc_start is not None
+    ext = Hkv != H or window != 0 or doc_start is not None or block_mask is not None
     if ext and passes != 3:
         raise ValueError("grouped-query or masked backward runs both passes (passes=3)")
     need = lib.attn_bwd_workspace_bytes(B, H, N)
@@ -236,7 +251,7 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
     c = 1 if causal else 0
     if ext:
         st = lib.attn_bwd_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window),
-                             _docs(q, doc_start), *rest)
+                             _docs(q, doc_start), _bmask(q, block_mask), *rest)
     else:
         st = lib.attn_bwd_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bwd", st)
@@ -245,7 +260,8 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
 
 def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
              scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, outs=None,
-             passes: int = 3, window: int = 0, doc_start: Optional[torch.Tensor] = None
+             passes: int = 3, window: int = 0, doc_start: Optional[torch.Tensor] = None,
+             block_mask: Optional[torch.Tensor] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
@@ -268,7 +284,7 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
         _check(n, t, q)
     for n, t in (("g_k", gk), ("g_v", gv)):
         _check(n, t, q, shape=kvs)
-    ext = Hkv != H or window != 0 or doc_start is not None
+    ext = Hkv != H or window != 0 or doc_start is not None or block_mask is not None
     if ext and passes != 3:
         raise ValueError("grouped-query or masked BoB runs both passes (passes=3)")
     need = lib.attn_bob_workspace_bytes(B, H, N)
@@ -284,7 +300,7 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
     c = 1 if causal else 0
     if ext:
         st = lib.attn_bob_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window),
-                             _docs(q, doc_start), *rest)
+                             _docs(q, doc_start), _bmask(q, block_mask), *rest)
     else:
         st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bob", st)

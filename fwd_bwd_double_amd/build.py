@@ -18,9 +18,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfbd.so")
-SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bob.hip", "fp8.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bob.hip", "bob_f32.hip", "fp8.hip"]
 # MFMA results are kept in the architectural VGPRs, so the element-wise work
-# between products needs no accumulator-register moves.
+# between products needs no accumulator-register moves (not for bob_f32.hip:
+# the compiler fails on the fp32 BoB row kernel with it).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 PER_SOURCE = {"fwd.hip": VGPR_FORM, "bwd.hip": VGPR_FORM, "bob.hip": VGPR_FORM,
               "fp8.hip": VGPR_FORM}

@@ -81,6 +81,20 @@ attn_status check_docs(const int32_t* ds, int causal, int64_t B, int64_t N,
   return ATTN_OK;
 }
 
+// Block-sparse mask: a (B, ceil(N/128), ceil(N/128)) byte input, disjoint
+// from every output (any alignment; causal or not).
+attn_status check_block_mask(const uint8_t* bm, int64_t B, int64_t N,
+                             const std::vector<Arg>& outs) {
+  if (!bm) return ATTN_OK;
+  const int64_t nb = (N + 127) / 128;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(bm), hi = lo + (size_t)(B * nb * nb);
+  for (const Arg& a : outs) {
+    const uintptr_t olo = reinterpret_cast<uintptr_t>(a.p), ohi = olo + a.bytes;
+    if (olo < hi && lo < ohi) return ATTN_EINVAL;
+  }
+  return ATTN_OK;
+}
+
 // Null, alignment and overlap checks.  `ins` are read-only, `outs` written.
 attn_status check_ptrs(const std::vector<Arg>& ins, const std::vector<Arg>& outs) {
   for (const Arg& a : ins) {
@@ -145,8 +159,8 @@ size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N) {
 
 attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V, int causal, int64_t window,
-                        const int32_t* doc_start, float scale, void* O, float* LSE,
-                        void* stream) {
+                        const int32_t* doc_start, const uint8_t* block_mask, float scale,
+                        void* O, float* LSE, void* stream) {
   attn_status st = check_shape(dt, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
@@ -157,23 +171,25 @@ attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
   st = check_ptrs({{Q, t}, {K, tk}, {V, tk}}, {{O, t}, {LSE, s}});
   if (st != ATTN_OK) return st;
   if ((st = check_docs(doc_start, causal, B, N, {{O, t}, {LSE, s}})) != ATTN_OK) return st;
+  if ((st = check_block_mask(block_mask, B, N, {{O, t}, {LSE, s}})) != ATTN_OK) return st;
   return finish(fbd::launch_fwd((int)dt, Q, K, V, O, LSE, (int)(B * H), (int)H, (int)(H / Hkv),
-                                win, doc_start, (int)N, causal ? 1 : 0, scale,
+                                win, doc_start, block_mask, (int)N, causal ? 1 : 0, scale,
                                 (hipStream_t)stream));
 }
 
 attn_status attn_fwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
                      const void* K, const void* V, int causal, float scale, void* O, float* LSE,
                      void* stream) {
-  return attn_fwd_ex(dt, B, H, H, N, d, Q, K, V, causal, 0, nullptr, scale, O, LSE, stream);
+  return attn_fwd_ex(dt, B, H, H, N, d, Q, K, V, causal, 0, nullptr, nullptr, scale, O, LSE,
+                     stream);
 }
 
 static attn_status bwd_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t Hkv,
                             int64_t N, int64_t d, const void* Q, const void* K, const void* V,
                             const void* O, const float* LSE, const void* dO, int causal,
-                            int64_t window, const int32_t* doc_start, float scale, int gproj,
-                            void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            int64_t window, const int32_t* doc_start,
+                            const uint8_t* block_mask, float scale, int gproj, void* dQ,
+                            void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
   if (passes < 1 || passes > 3) return ATTN_EINVAL;
   attn_status st = check_shape(dt, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
@@ -189,13 +205,15 @@ static attn_status bwd_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   if (st != ATTN_OK) return st;
   st = check_docs(doc_start, causal, B, N, {{dQ, t}, {dK, tk}, {dV, tk}, {ws, need}});
   if (st != ATTN_OK) return st;
+  st = check_block_mask(block_mask, B, N, {{dQ, t}, {dK, tk}, {dV, tk}, {ws, need}});
+  if (st != ATTN_OK) return st;
   const size_t bhn = (size_t)B * H * N;
   float* Dws = static_cast<float*>(ws);
   float* Rws = Dws + bhn;
   float* Lws = Rws + bhn;
   return finish(fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws,
-                                (int)(B * H), (int)H, (int)(H / Hkv), win, doc_start, (int)N,
-                                causal ? 1 : 0, scale, gproj ? 1 : 0, passes,
+                                (int)(B * H), (int)H, (int)(H / Hkv), win, doc_start, block_mask,
+                                (int)N, causal ? 1 : 0, scale, gproj ? 1 : 0, passes,
                                 (hipStream_t)stream));
 }
 
@@ -204,17 +222,18 @@ attn_status attn_bwd_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             const float* LSE, const void* dO, int causal, float scale, int gproj,
                             void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                             void* stream) {
-  return bwd_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, causal, 0, nullptr, scale,
-                  gproj, dQ, dK, dV, ws, ws_bytes, stream);
+  return bwd_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, causal, 0, nullptr, nullptr,
+                  scale, gproj, dQ, dK, dV, ws, ws_bytes, stream);
 }
 
 attn_status attn_bwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V, const void* O,
                         const float* LSE, const void* dO, int causal, int64_t window,
-                        const int32_t* doc_start, float scale, int gproj, void* dQ, void* dK,
-                        void* dV, void* ws, size_t ws_bytes, void* stream) {
-  return bwd_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, causal, window, doc_start, scale,
-                  gproj, dQ, dK, dV, ws, ws_bytes, stream);
+                        const int32_t* doc_start, const uint8_t* block_mask, float scale,
+                        int gproj, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return bwd_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, causal, window, doc_start,
+                  block_mask, scale, gproj, dQ, dK, dV, ws, ws_bytes, stream);
 }
 
 attn_status attn_bwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
@@ -229,8 +248,9 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             int64_t N, int64_t d, const void* Q, const void* K, const void* V,
                             const void* O, const float* LSE, const void* dO, const void* g_dQ,
                             const void* g_dK, const void* g_dV, int causal, int64_t window,
-                            const int32_t* doc_start, float scale, void* g_Q, void* g_K,
-                            void* g_V, void* g_dO, void* ws, size_t ws_bytes, void* stream) {
+                            const int32_t* doc_start, const uint8_t* block_mask, float scale,
+                            void* g_Q, void* g_K, void* g_V, void* g_dO, void* ws,
+                            size_t ws_bytes, void* stream) {
   if (passes < 1 || passes > 3) return ATTN_EINVAL;
   attn_status st = check_shape(dt, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
@@ -248,6 +268,9 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   st = check_docs(doc_start, causal, B, N,
                   {{g_Q, t}, {g_K, tk}, {g_V, tk}, {g_dO, t}, {ws, need}});
   if (st != ATTN_OK) return st;
+  st = check_block_mask(block_mask, B, N,
+                        {{g_Q, t}, {g_K, tk}, {g_V, tk}, {g_dO, t}, {ws, need}});
+  if (st != ATTN_OK) return st;
   const size_t bhn = (size_t)B * H * N;
   float* Dws = static_cast<float*>(ws);
   float* Aws = Dws + bhn;
@@ -256,8 +279,8 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   float* Kws = Lws + bhn;
   return finish(fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, g_Q, g_K, g_V,
                                 g_dO, Dws, Aws, Bws, Lws, Kws, (int)(B * H), (int)H,
-                                (int)(H / Hkv), win, doc_start, (int)N, causal ? 1 : 0, scale,
-                                passes, (hipStream_t)stream));
+                                (int)(H / Hkv), win, doc_start, block_mask, (int)N,
+                                causal ? 1 : 0, scale, passes, (hipStream_t)stream));
 }
 
 attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -266,17 +289,18 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             const void* g_dV, int causal, float scale, void* g_Q, void* g_K,
                             void* g_V, void* g_dO, void* ws, size_t ws_bytes, void* stream) {
   return bob_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, 0,
-                  nullptr, scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
+                  nullptr, nullptr, scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
 attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V, const void* O,
                         const float* LSE, const void* dO, const void* g_dQ, const void* g_dK,
                         const void* g_dV, int causal, int64_t window,
-                        const int32_t* doc_start, float scale, void* g_Q, void* g_K, void* g_V,
-                        void* g_dO, void* ws, size_t ws_bytes, void* stream) {
+                        const int32_t* doc_start, const uint8_t* block_mask, float scale,
+                        void* g_Q, void* g_K, void* g_V, void* g_dO, void* ws, size_t ws_bytes,
+                        void* stream) {
   return bob_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, window,
-                  doc_start, scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
+                  doc_start, block_mask, scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
 attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
@@ -319,15 +343,15 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
   const size_t bhn = (size_t)B * H * N;
   float* w0 = static_cast<float*>(ws);
   const int h = (int)H, nw = kNoWindow;
-  hipError_t e = fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, 1, nw, nullptr, n, c, scale,
-                                 hs);
+  hipError_t e =
+      fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, 1, nw, nullptr, nullptr, n, c, scale, hs);
   if (e == hipSuccess && ngrad == 3)
     e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, w0, w0 + bhn, w0 + 2 * bhn, bh,
-                        h, 1, nw, nullptr, n, c, scale, gproj ? 1 : 0, 3, hs);
+                        h, 1, nw, nullptr, nullptr, n, c, scale, gproj ? 1 : 0, 3, hs);
   if (e == hipSuccess)
     e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, w0,
                         w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, h, 1, nw, nullptr,
-                        n, c, scale, 3, hs);
+                        nullptr, n, c, scale, 3, hs);
   return finish(e);
 }
 

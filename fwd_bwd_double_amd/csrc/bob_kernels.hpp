@@ -1,3 +1,4 @@
+#pragma once
 // Backward-over-backward: the vector-Jacobian product of the first backward
 // map (Q, K, V, dO) -> (dQ, dK, dV) with cotangents (A, Bk, C) =
 // (g_dQ, g_dK, g_dV), computed in two passes as on the FlashBoB page
@@ -43,14 +44,15 @@
 
 namespace fbd {
 
-template <class T, int BN, bool CAUSAL, bool DOCS>
+template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK>
 __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
     float* __restrict__ Bws, float* __restrict__ Lws, float* __restrict__ Kws, int N, int BH,
-    int H, int grp, int win, const int* __restrict__ DS, int nblk, float scale) {
+    int H, int grp, int win, const int* __restrict__ DS, const uint8_t* __restrict__ BMK,
+    int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   struct Buf {
@@ -101,17 +103,25 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   const int jbeg = CAUSAL ? min(max(0, rs0), q0) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend - jbeg + BN - 1) / BN;
+  // block-sparse mask: the workgroup's row of 128 x 128 blocks
+  const int nbm = (N + 127) >> 7;
+  // (a compile-time variant, so the unmasked kernel keeps its registers)
+  const uint8_t* bmr = BMASK ? BMK + ((size_t)(wk.head / H) * nbm + (q0 >> 7)) * nbm : nullptr;
+  auto kept = [&](int t) { return !BMASK || bmr[(jbeg + t * BN) >> 7] != 0; };
   auto stage = [&](int j0, Buf& bf) {
     dma_tile<T, BN, NT / 64>(rk, j0, bf.k, wave, lane);
     dma_tile<T, BN, NT / 64>(rv, j0, bf.v, wave, lane);
     dma_tile<T, BN, NT / 64>(rb, j0, bf.b, wave, lane);
     dma_tile<T, BN, NT / 64>(rc, j0, bf.c, wave, lane);
   };
+  // the loop visits every tile index so that it keeps its counted form; a
+  // tile of a dropped block is neither loaded nor computed
   auto tile = [&](int t, const Buf& cb, Buf& nb) {
     const int j0 = jbeg + t * BN;
     wait_dma();
     __syncthreads();   // tile t is in cb; every wave is done with nb
-    if (t + 1 < ntiles) stage(j0 + BN, nb);
+    if (t + 1 < ntiles && kept(t + 1)) stage(j0 + BN, nb);
+    if (!kept(t)) return;
     const T* Ks = cb.k;
     const T* Vs = cb.v;
     const T* Bs = cb.b;
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         sub(std::false_type());
     }
   };
-  stage(jbeg, B0);
+  if (!BMASK || (ntiles > 0 && kept(0))) stage(jbeg, B0);
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, B0, B1);
     if (t + 1 < ntiles) tile(t + 1, B1, B0);
@@ -228,14 +238,14 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   }
 }
 
-template <class T, int BM, bool CAUSAL, bool DOCS>
+template <class T, int BM, bool CAUSAL, bool DOCS, bool BMASK>
 __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const T* __restrict__ A,
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
     const float* __restrict__ Aws, const float* __restrict__ Kws, T* __restrict__ gK,
     T* __restrict__ gV, int N, int BH, int H, int grp, int win, const int* __restrict__ DS,
-    float scale) {
+    const uint8_t* __restrict__ BMK, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, kappa of the tile's rows
@@ -277,6 +287,14 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   if (CAUSAL && DOCS) iend = min(iend, first_above(ds, min(N, k0 + BLK), N, kmax, lane));
   const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
   const int nsteps = ntiles * grp;      // (query head, query tile) steps
+  // block-sparse mask (a compile-time variant): the workgroup's column of
+  // 128 x 128 blocks; every step index is visited, and a step whose query
+  // tile lies in a dropped block is neither loaded nor computed
+  const int nbm = (N + 127) >> 7;
+  const uint8_t* bmc = BMASK ? BMK + (size_t)(qh0 / H) * nbm * nbm + (k0 >> 7) : nullptr;
+  auto kept = [&](int u) {
+    return !BMASK || bmc[(size_t)((istart + (u % ntiles) * BM) >> 7) * nbm] != 0;
+  };
   // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
   auto stage = [&](int u, Buf& b) {
     const int qh = qh0 + u / ntiles;
@@ -300,7 +318,8 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const int i0 = istart + (u % ntiles) * BM;
     wait_dma();
     __syncthreads();   // step u is in cb; every wave is done with nb
-    if (u + 1 < nsteps) stage(u + 1, nb);
+    if (u + 1 < nsteps && kept(u + 1)) stage(u + 1, nb);
+    if (!kept(u)) return;
     const T* Qs = cb.q;
     const T* dOs = cb.dO;
     const T* As = cb.a;
@@ -405,7 +424,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
       }
     }
   };
-  if (nsteps > 0) stage(0, B0);
+  if (nsteps > 0 && kept(0)) stage(0, B0);
   for (int u = 0; u < nsteps; u += 2) {
     tile(u, B0, B1);
     if (u + 1 < nsteps) tile(u + 1, B1, B0);
@@ -430,47 +449,40 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
                                float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
-                               int H, int grp, int win, const int* ds, int N, float scale,
+                               int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
+                               float scale,
                                int passes,
                                hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
-    hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS>), dim3(nblk * BH), dim3(NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
-                       (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws,
-                       Lws, Kws, N, BH, H, grp, win, ds, nblk, scale);
+    if (bm)
+      hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS, true>), dim3(nblk * BH), dim3(NT),
+                         0, st, (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE,
+                         (const T*)dO, (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ,
+                         (T*)gdO, Dws, Aws, Bws, Lws, Kws, N, BH, H, grp, win, ds, bm, nblk,
+                         scale);
+    else
+      hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS, false>), dim3(nblk * BH), dim3(NT),
+                         0, st, (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE,
+                         (const T*)dO, (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ,
+                         (T*)gdO, Dws, Aws, Bws, Lws, Kws, N, BH, H, grp, win, ds, bm, nblk,
+                         scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL, DOCS>), dim3(nblk * (BH / grp)), dim3(NT), 0,
-                     st,
-                     (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO,
-                     (const T*)gdQ, (const T*)gdK, (const T*)gdV, (const float*)Dws,
-                     (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, win, ds,
-                     scale);
+  auto col = [&](auto bmask) {
+    hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL, DOCS, decltype(bmask)::value>),
+                       dim3(nblk * (BH / grp)), dim3(NT), 0, st, (const T*)Q, (const T*)K,
+                       (const T*)V, (const float*)Lws, (const T*)dO, (const T*)gdQ,
+                       (const T*)gdK, (const T*)gdV, (const float*)Dws, (const float*)Aws,
+                       (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, win, ds, bm, scale);
+  };
+  if (bm) col(std::true_type{});
+  else col(std::false_type{});
   return hipGetLastError();
-}
-
-hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
-                      const float* LSE, const void* dO, const void* gdQ, const void* gdK,
-                      const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
-                      float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
-                      int win, const int* ds, int N, int causal, float scale, int passes,
-                      hipStream_t st) {
-#define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, Lws, Kws, \
-                     BH, H, grp, win, ds, N, scale, passes, st
-  if (dt == 0) {
-    if (!causal) return launch_bob_t<bf16, false, false>(FBD_BOB_ARGS);
-    return ds ? launch_bob_t<bf16, true, true>(FBD_BOB_ARGS)
-              : launch_bob_t<bf16, true, false>(FBD_BOB_ARGS);
-  }
-  if (!causal) return launch_bob_t<float, false, false>(FBD_BOB_ARGS);
-  return ds ? launch_bob_t<float, true, true>(FBD_BOB_ARGS)
-            : launch_bob_t<float, true, false>(FBD_BOB_ARGS);
-#undef FBD_BOB_ARGS
 }
 
 }  // namespace fbd

@@ -22,17 +22,20 @@
 // operands contracted over the sequence index are read with the transposing
 // LDS read, so every tile is stored once, row-major.
 // Each output block is written once by one workgroup; there are no atomics.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "tile.hpp"
 
 namespace fbd {
 
-template <class T, int BN, bool GPROJ, bool CAUSAL, bool DOCS>
+template <class T, int BN, bool GPROJ, bool CAUSAL, bool DOCS, bool BMASK>
 __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, float* __restrict__ Lws,
-    int N, int BH, int H, int grp, int win, const int* __restrict__ DS, int nblk, float scale) {
+    int N, int BH, int H, int grp, int win, const int* __restrict__ DS,
+    const uint8_t* __restrict__ BMK, int nblk, float scale) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   __shared__ __attribute__((aligned(16))) T K0[BN * HD];
@@ -79,14 +82,21 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   const int jbeg = CAUSAL ? min(max(0, rs0), q0) / BN * BN : 0;
   const int jend = CAUSAL ? min(N, q0 + BLK) : N;
   const int ntiles = (jend - jbeg + BN - 1) / BN;
+  // block-sparse mask (a compile-time variant): the workgroup's row of
+  // 128 x 128 blocks; the loop visits every tile index, and a tile of a
+  // dropped block is neither loaded nor computed
+  const int nbm = (N + 127) >> 7;
+  const uint8_t* bmr = BMASK ? BMK + ((size_t)(wk.head / H) * nbm + (q0 >> 7)) * nbm : nullptr;
+  auto kept = [&](int t) { return !BMASK || bmr[(jbeg + t * BN) >> 7] != 0; };
   auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
     const int j0 = jbeg + t * BN;
     wait_dma();
     __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
-    if (t + 1 < ntiles) {
+    if (t + 1 < ntiles && kept(t + 1)) {
       dma_tile<T, BN, NT / 64>(rk, j0 + BN, Kn, wave, lane);
       dma_tile<T, BN, NT / 64>(rv, j0 + BN, Vn, wave, lane);
     }
+    if (!kept(t)) return;
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 32) {
       const int js = j0 + jb;   // all waves compute all sub-blocks; dead keys masked
@@ -133,8 +143,10 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
       }
     }
   };
-  dma_tile<T, BN, NT / 64>(rk, jbeg, K0, wave, lane);
-  dma_tile<T, BN, NT / 64>(rv, jbeg, V0, wave, lane);
+  if (!BMASK || (ntiles > 0 && kept(0))) {
+    dma_tile<T, BN, NT / 64>(rk, jbeg, K0, wave, lane);
+    dma_tile<T, BN, NT / 64>(rv, jbeg, V0, wave, lane);
+  }
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, K0, V0, K1, V1);
     if (t + 1 < ntiles) tile(t + 1, K1, V1, K0, V0);
@@ -163,12 +175,12 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   }
 }
 
-template <class T, int BM, bool GPROJ, bool CAUSAL, bool DOCS>
+template <class T, int BM, bool GPROJ, bool CAUSAL, bool DOCS, bool BMASK>
 __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int H,
-    int grp, int win, const int* __restrict__ DS, float scale) {
+    int grp, int win, const int* __restrict__ DS, const uint8_t* __restrict__ BMK, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q and dO tiles and the -LSE*log2(e), D (, r) of the tile's rows
@@ -210,6 +222,14 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   if (CAUSAL && DOCS) iend = min(iend, first_above(ds, min(N, k0 + BLK), N, kmax, lane));
   const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
   const int nsteps = ntiles * grp;      // (query head, query tile) steps
+  // block-sparse mask (a compile-time variant): the workgroup's column of
+  // 128 x 128 blocks; every step index is visited, and a step whose query
+  // tile lies in a dropped block is neither loaded nor computed
+  const int nbm = (N + 127) >> 7;
+  const uint8_t* bmc = BMASK ? BMK + (size_t)(qh0 / H) * nbm * nbm + (k0 >> 7) : nullptr;
+  auto kept = [&](int u) {
+    return !BMASK || bmc[(size_t)((istart + (u % ntiles) * BM) >> 7) * nbm] != 0;
+  };
   // stage step u: query tile u % ntiles of query head qh0 + u / ntiles
   auto stage = [&](int u, Buf& b) {
     const int qh = qh0 + u / ntiles;
@@ -231,7 +251,8 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const int i0 = istart + (u % ntiles) * BM;
     wait_dma();
     __syncthreads();   // step u is in cb; every wave is done with nb
-    if (u + 1 < nsteps) stage(u + 1, nb);
+    if (u + 1 < nsteps && kept(u + 1)) stage(u + 1, nb);
+    if (!kept(u)) return;
     const T* Qs = cb.q;
     const T* dOs = cb.dO;
     const float* sL = cb.nl;
@@ -311,7 +332,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
       }
     }
   };
-  if (nsteps > 0) stage(0, B0);
+  if (nsteps > 0 && kept(0)) stage(0, B0);
   for (int u = 0; u < nsteps; u += 2) {
     tile(u, B0, B1);
     if (u + 1 < nsteps) tile(u + 1, B1, B0);
@@ -335,23 +356,33 @@ template <class T, bool GPROJ, bool CAUSAL, bool DOCS>
 static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
                                float* Dws, float* Rws, float* Lws, int BH, int H, int grp,
-                               int win, const int* ds, int N, float scale, int passes,
+                               int win, const int* ds, const uint8_t* bm, int N, float scale, int passes,
                                hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
+  // the block mask selects a compile-time kernel variant
+  auto row = [&](auto bmask) {
+    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL, DOCS, decltype(bmask)::value>),
+                       dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                       (const T*)O, LSE, (const T*)dO, (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, win,
+                       ds, bm, nblk, scale);
+  };
+  auto col = [&](auto bmask) {
+    hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL, DOCS, decltype(bmask)::value>),
+                       dim3(nblk * (BH / grp)), dim3(NT), 0, st, (const T*)Q, (const T*)K,
+                       (const T*)V, (const float*)Lws, (const T*)dO, (const float*)Dws,
+                       (const float*)Rws, (T*)dK, (T*)dV, N, BH, H, grp, win, ds, bm, scale);
+  };
   if (passes & 1) {
-    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL, DOCS>), dim3(nblk * BH), dim3(NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE, (const T*)dO,
-                       (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, win, ds, nblk, scale);
+    if (bm) row(std::true_type{});
+    else row(std::false_type{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL, DOCS>), dim3(nblk * (BH / grp)), dim3(NT),
-                     0, st, (const T*)Q, (const T*)K, (const T*)V, (const float*)Lws,
-                     (const T*)dO, (const float*)Dws, (const float*)Rws, (T*)dK, (T*)dV, N, BH, H,
-                     grp, win, ds, scale);
+  if (bm) col(std::true_type{});
+  else col(std::false_type{});
   return hipGetLastError();
 }
 
@@ -359,28 +390,28 @@ template <class T, bool GPROJ>
 static hipError_t launch_bwd_c(int causal, const void* Q, const void* K, const void* V,
                                const void* O, const float* LSE, const void* dO, void* dQ,
                                void* dK, void* dV, float* Dws, float* Rws, float* Lws, int BH,
-                               int H, int grp, int win, const int* ds, int N, float scale,
+                               int H, int grp, int win, const int* ds, const uint8_t* bm, int N, float scale,
                                int passes,
                                hipStream_t st) {
   if (causal)
-    return ds ? launch_bwd_t<T, GPROJ, true, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st)
-              : launch_bwd_t<T, GPROJ, true, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
-  return launch_bwd_t<T, GPROJ, false, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
+    return ds ? launch_bwd_t<T, GPROJ, true, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st)
+              : launch_bwd_t<T, GPROJ, true, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
+  return launch_bwd_t<T, GPROJ, false, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
 }
 
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
                       float* Rws, float* Lws, int BH, int H, int grp, int win, const int* ds,
-                      int N,
+                      const uint8_t* bm, int N,
                       int causal, float scale, int gproj, int passes, hipStream_t st) {
   if (dt == 0) {
     if (gproj)
-      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
-    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
+      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
+    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
   }
   if (gproj)
-    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
-  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, N, scale, passes, st);
+    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
+  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
 }
 
 }  // namespace fbd

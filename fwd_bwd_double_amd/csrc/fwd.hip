@@ -26,6 +26,8 @@
 // groups per wave halve LDS reads per FLOP but cost occupancy).  The row sum
 // l adds the bf16-rounded probabilities -- the values the P V product uses --
 // with v_dot2_f32_bf16.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -35,14 +37,16 @@ constexpr int FWD_WAVES = FBD_FWD_WAVES;
 constexpr int FWD_NT = 64 * FWD_WAVES;
 constexpr int FWD_G = FBD_FWD_G;                      // 32-query groups per wave
 constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;    // query rows per workgroup
+static_assert(FWD_BLK == 128, "a workgroup owns one 128-row block of the block-sparse mask");
 
-template <class T, int BN, bool CAUSAL, bool DOCS>
+template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK>
 __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,
                                                      int H, int grp, int win,
-                                                     const int* __restrict__ DS, int nblk,
+                                                     const int* __restrict__ DS,
+                                                     const uint8_t* __restrict__ BMK, int nblk,
                                                      float scale) {
   // two buffers as separate objects, used in a loop unrolled by two, so the
   // compiler can tell the copy of the next tile never aliases the reads of
@@ -102,15 +106,24 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
   const int jend = CAUSAL ? min(N, q0 + FWD_BLK) : N;
   const int ntiles = (jend - jbeg + BN - 1) / BN;
   constexpr int NS = BN / 32;   // 32-key sub-blocks per tile
+  // block-sparse mask (a compile-time variant, so the unmasked kernel keeps
+  // its registers): the workgroup's row of 128 x 128 blocks; tiles in a
+  // dropped block are never loaded
+  const int nbm = (N + 127) >> 7;
+  const uint8_t* bmr = BMASK ? BMK + ((size_t)(wk.head / H) * nbm + (q0 >> 7)) * nbm : nullptr;
+  auto kept = [&](int t) { return !BMASK || bmr[(jbeg + t * BN) >> 7] != 0; };
 
+  // the loop visits every tile index, keeping its counted form; a tile of a
+  // dropped block is neither loaded nor computed
   auto tile = [&](int t, const T* Ks, const T* Vs, T* Kn, T* Vn) {
     const int j0 = jbeg + t * BN;
     wait_dma();
     __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
-    if (t + 1 < ntiles) {
+    if (t + 1 < ntiles && kept(t + 1)) {
       dma_tile<T, BN, FWD_WAVES>(rk, j0 + BN, Kn, wave, lane);
       dma_tile<T, BN, FWD_WAVES>(rv, j0 + BN, Vn, wave, lane);
     }
+    if (!kept(t)) return;
     // Every wave computes every 32-key sub-block of the tile; keys after a
     // row (causal) or past N are masked to -inf.  Identical control flow in
     // all waves keeps the accumulators in fixed registers.
@@ -205,18 +218,22 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
       negm[g] = zero16() - m[g];
     }
   };
-  dma_tile<T, BN, FWD_WAVES>(rk, jbeg, K0, wave, lane);
-  dma_tile<T, BN, FWD_WAVES>(rv, jbeg, V0, wave, lane);
+  if (!BMASK || (ntiles > 0 && kept(0))) {
+    dma_tile<T, BN, FWD_WAVES>(rk, jbeg, K0, wave, lane);
+    dma_tile<T, BN, FWD_WAVES>(rv, jbeg, V0, wave, lane);
+  }
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, K0, V0, K1, V1);
     if (t + 1 < ntiles) tile(t + 1, K1, V1, K0, V0);
   }
+  // a row left with no visible key (possible only under a block mask) gets
+  // O = 0 and LSE = -inf
 #pragma unroll
   for (int g = 0; g < FWD_G; ++g) {
     const int qg = qw + g * WROWS;
     const int my_i = qg + (lane & 31);
     const float lt = half_sum(l[g]);
-    const float inv = 1.f / lt;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     float out[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) out[v] = o[g][0][v] * inv;
@@ -225,36 +242,47 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
     for (int v = 0; v < 16; ++v) out[v] = o[g][1][v] * inv;
     st_cols(O + hoff, N, qg, 32, lane, out);
     if (h == 0 && my_i < N)
-      LSE[(size_t)wk.head * N + my_i] = scale * m[g] + __builtin_amdgcn_logf(lt) * LN2;
+      LSE[(size_t)wk.head * N + my_i] =
+          lt > 0.f ? scale * m[g] + __builtin_amdgcn_logf(lt) * LN2 : -INFINITY;
   }
 }
 
 template <class T, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               int BH, int H, int grp, int win, const int* ds, int N,
-                               float scale, hipStream_t st) {
+                               int BH, int H, int grp, int win, const int* ds,
+                               const uint8_t* bm, int N, float scale, hipStream_t st) {
   constexpr int BN = sizeof(T) == 2 ? FBD_FWD_BN : 64;
   const int nblk = (N + FWD_BLK - 1) / FWD_BLK;
-  if (ds)
-    hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL, true>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, win, ds,
-                       nblk, scale);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL, false>), dim3(nblk * BH), dim3(FWD_NT), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, BH, H, grp, win,
-                       ds, nblk, scale);
+  auto run = [&](auto docs, auto bmask) {
+    hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL, decltype(docs)::value, decltype(bmask)::value>),
+                       dim3(nblk * BH), dim3(FWD_NT), 0, st, (const T*)Q, (const T*)K,
+                       (const T*)V, (T*)O, LSE, N, BH, H, grp, win, ds, bm, nblk, scale);
+  };
+  using Y = std::true_type;
+  using F = std::false_type;
+  if constexpr (CAUSAL) {
+    if (ds) {
+      if (bm) run(Y{}, Y{});
+      else run(Y{}, F{});
+      return hipGetLastError();
+    }
+  }
+  if (bm) run(F{}, Y{});
+  else run(F{}, F{});
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int BH, int H, int grp, int win, const int* ds, int N, int causal,
-                      float scale, hipStream_t st) {
+                      int BH, int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
+                      int causal, float scale, hipStream_t st) {
   if (dt == 0) {
-    if (causal) return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
-    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
+    if (causal)
+      return launch_fwd_t<bf16, true>(Q, K, V, O, LSE, BH, H, grp, win, ds, bm, N, scale, st);
+    return launch_fwd_t<bf16, false>(Q, K, V, O, LSE, BH, H, grp, win, ds, bm, N, scale, st);
   }
-  if (causal) return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
-  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, H, grp, win, ds, N, scale, st);
+  if (causal)
+    return launch_fwd_t<float, true>(Q, K, V, O, LSE, BH, H, grp, win, ds, bm, N, scale, st);
+  return launch_fwd_t<float, false>(Q, K, V, O, LSE, BH, H, grp, win, ds, bm, N, scale, st);
 }
 
 }  // namespace fbd

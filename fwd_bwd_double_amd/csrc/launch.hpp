@@ -66,26 +66,38 @@ namespace fbd {
 // visible to query i iff i - win < j <= i (a value >= N is plain causal).
 // ds: nullptr, or (B, N) int32 first visible key of each query row (document
 // masks: key j visible to query i of batch b iff ds[b][i] <= j <= i).
+// bm: nullptr, or a (B, nb, nb) byte block-sparse mask, nb = ceil(N / 128):
+// bm[b][qb][kb] == 0 drops queries 128 qb .. and keys 128 kb .. of batch b
+// (on top of the other masks); dropped blocks are never loaded.
 // Pointers are device pointers.
 // passes (backward and BoB): bit 0 = row pass, bit 1 = column pass.
 hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int BH, int H, int grp, int win, const int* ds, int N, int causal,
-                      float scale, hipStream_t st);
+                      int BH, int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
+                      int causal, float scale, hipStream_t st);
 
 // Backward workspace: D, r, and -LSE*log2(e) per row (written by the row pass,
 // read by the column pass).
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
                       float* Rws, float* Lws, int BH, int H, int grp, int win, const int* ds,
-                      int N, int causal, float scale, int gproj, int passes, hipStream_t st);
+                      const uint8_t* bm, int N, int causal, float scale, int gproj, int passes,
+                      hipStream_t st);
 
 // BoB workspace: D, alpha, beta, -LSE*log2(e) and kappa = alpha*D + beta per row.
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
-                      int win, const int* ds, int N, int causal, float scale, int passes,
-                      hipStream_t st);
+                      int win, const int* ds, const uint8_t* bm, int N, int causal, float scale,
+                      int passes, hipStream_t st);
+
+// The fp32 half of launch_bob (same arguments, dt implied).
+hipError_t launch_bob_f32(const void* Q, const void* K, const void* V, const void* O,
+                          const float* LSE, const void* dO, const void* gdQ, const void* gdK,
+                          const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
+                          float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
+                          int win, const int* ds, const uint8_t* bm, int N, int causal,
+                          float scale, int passes, hipStream_t st);
 
 // FP8 forward.  Quantisation pre-pass: E4M3 codes of Q and K (optionally
 // rotated by diag(signs) H / 8 when rotate != 0) with one power-of-two scale

@@ -361,6 +361,14 @@ __device__ __forceinline__ int first_above(const int* __restrict__ ds, int lo, i
   return a;
 }
 
+// Block-sparse masks: a (B, nb, nb) byte array over 128 x 128 blocks of
+// (query, key) positions, nb = ceil(N / 128), row-major by query block; a zero
+// drops the block.  A row pass reads its 128-row block's row of the array, a
+// column pass its 128-key block's column (stride nb).  The kernels take the
+// mask as a compile-time variant and keep their counted tile loops: every
+// tile index is visited, and a tile of a dropped block is neither loaded
+// (its prefetch is skipped) nor computed.
+
 // First visible key of query row i under the causal mask: i - win + 1 for a
 // sliding window, raised to the row's document start when ds is given (row
 // index clamped into the head for padding rows past N).

@@ -171,7 +171,8 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Extended forms: shared keys and values, and a sliding window.  The FlashBoB
+ * Extended forms: shared keys and values, a sliding window, document masks
+ * and block-sparse masks.  The FlashBoB
  * page (rit.work, flashbob-second-order-attention), in its closing paragraph
  * on where the method applies, names shared keys and values and flexible
  * masks among the extensions after plain multi-head attention.
@@ -200,23 +201,35 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
  * outside the documents: a key block's column pass finds the last query row
  * it reaches with a wave-parallel search of doc_start.
  *
- * With Hkv == H, window == 0 and no doc_start these equal attn_fwd / attn_bwd
- * / attn_bob.  Hkv outside the range above, window < 0 or a doc_start that
- * overlaps an output is ATTN_EINVAL; a misaligned doc_start is ATTN_EALIGN;
+ * Block-sparse masks (block_mask != NULL, causal or not): a device (B, nb,
+ * nb) uint8 array, nb = ceil(N / 128), row-major (query block, then key
+ * block), read-only, any alignment.  block_mask[b][qb][kb] == 0 hides keys
+ * 128 kb .. 128 kb + 127 from queries 128 qb .. 128 qb + 127 of batch b (all
+ * heads), on top of the other masks; such blocks are never loaded, so the
+ * cost follows the kept blocks.  A query left with no visible key gets O = 0,
+ * LSE = -infinity and zero gradients and BoB outputs (the oracle's
+ * convention for an empty softmax row).
+ *
+ * With Hkv == H, window == 0, no doc_start and no block_mask these equal
+ * attn_fwd / attn_bwd / attn_bob.  Hkv outside the range above, window < 0 or
+ * a doc_start or block_mask that overlaps an output is ATTN_EINVAL; a
+ * misaligned doc_start is ATTN_EALIGN;
  * window > 0 or doc_start with causal == 0 is ATTN_EUNSUPPORTED; other
  * arguments and errors as for the multi-head entry points (workspace sizes
  * count the H query heads).  The backward and BoB must get the same causal,
- * window and doc_start as the forward.
+ * window, doc_start and block_mask as the forward.
  */
 attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V,
-                        int causal, int64_t window, const int32_t* doc_start, float scale,
+                        int causal, int64_t window, const int32_t* doc_start,
+                        const uint8_t* block_mask, float scale,
                         void* O, float* LSE, void* stream);
 
 attn_status attn_bwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V, const void* O,
                         const float* LSE, const void* dO,
-                        int causal, int64_t window, const int32_t* doc_start, float scale,
+                        int causal, int64_t window, const int32_t* doc_start,
+                        const uint8_t* block_mask, float scale,
                         int gproj, void* dQ, void* dK, void* dV,
                         void* ws, size_t ws_bytes, void* stream);
 
@@ -224,7 +237,8 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
                         const void* Q, const void* K, const void* V, const void* O,
                         const float* LSE, const void* dO,
                         const void* g_dQ, const void* g_dK, const void* g_dV,
-                        int causal, int64_t window, const int32_t* doc_start, float scale,
+                        int causal, int64_t window, const int32_t* doc_start,
+                        const uint8_t* block_mask, float scale,
                         void* g_Q, void* g_K, void* g_V, void* g_dO,
                         void* ws, size_t ws_bytes, void* stream);
 

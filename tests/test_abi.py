@@ -104,8 +104,8 @@ def test_hvp_rejects_bad_arguments_before_launch(lib):
 
 def test_extended_forms_reject_bad_heads_and_windows(lib):
     p = [FAKE * (i + 1) for i in range(3)]
-    call = lambda H, Hkv, causal=1, window=0, ds=None: lib.attn_fwd_ex(
-        0, 1, H, Hkv, 8, 64, *p, causal, window, ds, 0.125, FAKE * 4, FAKE * 5, None)
+    call = lambda H, Hkv, causal=1, window=0, ds=None, bm=None: lib.attn_fwd_ex(
+        0, 1, H, Hkv, 8, 64, *p, causal, window, ds, bm, 0.125, FAKE * 4, FAKE * 5, None)
     for H, Hkv in ((4, 3), (4, 0), (4, 8), (4, -1)):
         assert call(H, Hkv) == 1
     assert call(4, 2, window=-1) == 1
@@ -113,6 +113,7 @@ def test_extended_forms_reject_bad_heads_and_windows(lib):
     assert call(4, 2, causal=0, ds=FAKE * 7) == 2  # so do document masks
     assert call(4, 2, ds=FAKE * 7 + 2) == 3        # doc_start must be 4-byte aligned
     assert call(4, 2, ds=FAKE * 4) == 1            # and must not overlap an output
+    assert call(4, 2, bm=FAKE * 5 + 1) == 1        # a block mask must not overlap an output
 
 
 def test_fp8_workspace_layout(lib):

@@ -461,3 +461,69 @@ def test_document_masks(N, mean_len, window, H, Hkv, dtype):
             check(k, f64(t), ref[k], t1)
         for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
             check(k, f64(t), ref[k], t2)
+
+
+# ------------------------------------------ block-sparse masks (128 x 128 blocks)
+def block_masks(B, N, seed, density, keep_diag):
+    """Seeded (B, nb, nb) uint8 block mask, nb = ceil(N / 128): each block kept
+    with the given probability; the diagonal blocks kept when asked."""
+    rng = np.random.default_rng(seed)
+    nb = (N + 127) // 128
+    m = (rng.random((B, nb, nb)) < density).astype(np.uint8)
+    if keep_diag:
+        m[:, np.arange(nb), np.arange(nb)] = 1
+    return m
+
+
+def check_lse_with_empty_rows(got, ref, t):
+    """Rows with no visible key have LSE = -inf on both sides; the others are
+    compared by rel-L2."""
+    empty = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), empty), "empty rows differ"
+    say(f"    empty rows: {int(empty.sum())}")
+    check("LSE", got[~empty], ref[~empty], t)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("N,causal,density,keep_diag,window,mean_len,H,Hkv", [
+    (300, True, 0.6, True, 0, 0, 2, 2),
+    (1000, False, 0.4, False, 0, 0, 4, 2),
+    (1000, True, 0.5, True, 200, 0, 2, 1),
+    (2048, True, 0.7, True, 0, 300, 2, 2),
+    (333, True, 0.5, False, 0, 0, 3, 3),
+])
+def test_block_sparse_masks(N, causal, density, keep_diag, window, mean_len, H, Hkv, dtype):
+    import fwd_bwd_double_amd as fbd
+    w = synthetic.Workload(f"bsparse-{dtype}", 2, H, N, 64, dtype, 9700 + N + H, causal=causal,
+                           qkv_std=1.0)
+    x, g, a = inputs(w)
+    for n in ("k", "v", "g_dk", "g_dv"):
+        g[n] = g[n][:, :Hkv].contiguous()
+        a[n] = a[n][:, :Hkv]
+    bm = block_masks(2, N, 31 + N, density, keep_diag)
+    tbm = torch.from_numpy(bm).cuda()
+    docs = doc_starts(2, N, 79 + N, mean_len) if mean_len else None
+    ds = torch.from_numpy(docs.astype(np.int32)).cuda() if mean_len else None
+    say(f"[gpu] block-sparse B=2 H={H} Hkv={Hkv} N={N} causal={causal} density={density} "
+        f"keep_diag={keep_diag} window={window} docs={bool(mean_len)} dtype={dtype} "
+        f"kept={int(bm.sum())}/{bm.size}")
+    o, lse = fbd.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, window=window,
+                          doc_start=ds, block_mask=tbm)
+    t1, t2 = (1e-5, 1e-5) if dtype == "fp32" else (2e-2, 5e-2)
+    ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                         causal=causal, with_bwd=True, window=window, docs=docs, block_mask=bm)
+    f64 = synthetic.to_f64
+    for gproj in (False, True):
+        dq, dk, dv = fbd.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal,
+                                  scale=w.scale, gproj=gproj, window=window, doc_start=ds,
+                                  block_mask=tbm)
+        gq, gk, gv, gdo = fbd.attn_bob(g["q"], g["k"], g["v"], o, lse, g["do"], g["g_dq"],
+                                       g["g_dk"], g["g_dv"], causal=causal, scale=w.scale,
+                                       window=window, doc_start=ds, block_mask=tbm)
+        torch.cuda.synchronize()
+        check("O", f64(o), ref["O"], t1)
+        check_lse_with_empty_rows(f64(lse), ref["LSE"], t1)
+        for k, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            check(k, f64(t), ref[k], t1)
+        for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
+            check(k, f64(t), ref[k], t2)
