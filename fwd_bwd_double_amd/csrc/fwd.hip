@@ -11,7 +11,9 @@
 // subtracting the max before scaling makes the largest weight exactly 1 (GProj
 // page, rit.work flashattention-bf16-gradient-gproj, section "Why the error
 // shows up at the end of training", on fusing the scale and the max into one
-// operation).  The subtraction of the running max costs no VALU work: the
+// operation).  For bf16 the subtraction and the scaling share one FMA: the
+// weight at the max is then within 2^-10 of 1, and the bf16 rounding of P,
+// which both l and P V use, makes it exactly 1 again.  The subtraction of the running max costs no VALU work: the
 // score MFMAs start from -m in their accumulator.  Only when a row's max grows
 // inside a tile is the growth subtracted explicitly.  Key tiles entirely in
 // the future of the workgroup's rows are never loaded (explainer page, section
@@ -155,11 +157,17 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
         const int js = j0 + sb * 32;
         if (CAUSAL ? (js + 31 > qg || (DOCS ? js < rs_w[g] : js <= qg + 31 - win))
                    : (js + 32 > N)) {
+          // causal without documents: key j is visible iff my_i - win < j <=
+          // my_i, i.e. (unsigned)(my_i - j) < win, one compare per element
+          const int d0 = my_i - js - 4 * h;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-            const bool early = DOCS ? j < rs[g] : j <= my_i - win;
-            x[sb][g][v] = (CAUSAL ? (j > my_i || early) : (j >= N)) ? -INFINITY : x[sb][g][v];
+            bool hide;
+            if constexpr (!CAUSAL) hide = j >= N;
+            else if constexpr (DOCS) hide = j > my_i || j < rs[g];
+            else hide = (unsigned)(d0 - 8 * (v >> 2) - (v & 3)) >= (unsigned)win;
+            x[sb][g][v] = hide ? -INFINITY : x[sb][g][v];
           }
         }
       }
@@ -191,8 +199,18 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
       for (int g = 0; g < FWD_G; ++g) {
         float p[16];
         if (sub[g]) {
+          if constexpr (sizeof(T) == 2) {
+            // one FMA: the weight at the max is 2^e with |e| < 2^-10 (the
+            // rounding of base * sl2), which the bf16 rounding of P below
+            // takes to exactly 1, so l and P V still see the exact 1
+            const float nb = -base[g] * sl2;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f((x[sb][g][v] - base[g]) * sl2);
+            for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(x[sb][g][v], sl2, nb));
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              p[v] = __builtin_amdgcn_exp2f((x[sb][g][v] - base[g]) * sl2);
+          }
         } else {
 #pragma unroll
           for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[sb][g][v] * sl2);
