@@ -359,11 +359,14 @@ __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
     // sb's registers 4a .. 4a+3 in word 4 sb + a
     float p[2][16];
     if (__any(base != 0.f)) {
+      // one FMA: the weight at the max is 256 * 2^e with |e| < 2^-10, which
+      // the E4M3 rounding takes to exactly 256
+      const float off = fmaf(-base, sl2c, 8.f);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          p[sb][v] = __builtin_amdgcn_exp2f(fmaf(x[sb][v] - base, sl2c, 8.f));
+          p[sb][v] = __builtin_amdgcn_exp2f(fmaf(x[sb][v], sl2c, off));
     } else {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
