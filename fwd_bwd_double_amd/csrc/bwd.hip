@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) e[k] = p[8 * tt + k] * (ds[8 * tt + k] - Di);
         const Frag<T> df = pack8<T>(e);
-        if constexpr (GPROJ) r += frag_sum(df);
+        if constexpr (GPROJ) r = frag_acc_sum(df, r);   // v_dot2 on the bf16 pairs
         mma(dq0, ld_tr(Ks, 0, jt + tt, lane), df);
         mma(dq1, ld_tr(Ks, 32, jt + tt, lane), df);
       }
