@@ -169,10 +169,13 @@ def dequantize_cols(codes, exps):
     return np.ldexp(e4m3_decode(codes), np.asarray(exps)[..., None, :])
 
 
-def fwd_fp8(Q, K, V, causal=True, scale=None, signs=None):
+def fwd_fp8(Q, K, V, causal=True, scale=None, signs=None, window=0, docs=None,
+            block_mask=None):
     """FP8 forward model.  Q is (B, H, N, 64); K, V are (B, Hkv, N, 64) with
     H a multiple of Hkv.  ``signs`` is None for plain (naive) block
-    quantisation, else the rotation's 64-bit sign mask.
+    quantisation, else the rotation's 64-bit sign mask.  window, docs and
+    block_mask are the masks of the exact forward (attention.fwd); a row they
+    leave empty has O = 0, LSE = -inf and zero weights.
 
     Returns a dict:
       O, LSE   exact attention on the dequantised operands (fp64);
@@ -200,20 +203,22 @@ def fwd_fp8(Q, K, V, causal=True, scale=None, signs=None):
     qh = dequantize_rows(cq, eq)
     kh = np.repeat(dequantize_rows(ck, ek), g, axis=1)
     vh = np.repeat(dequantize_cols(cv, ev), g, axis=1)
-    O, LSE = _fwd_exact(qh, kh, vh, causal=causal, scale=c)
+    O, LSE = _fwd_exact(qh, kh, vh, causal=causal, scale=c, window=window, docs=docs,
+                        block_mask=block_mask)
     W = np.empty_like(O)
     U = np.empty_like(O)
     A = np.empty_like(LSE)
     idx = np.arange(N)
     for b in range(B):
         for h in range(H):
-            s = c * (qh[b, h] @ kh[b, h].T)
-            s = np.where(_visible(idx, N, causal), s, -np.inf)
-            p = np.exp(s - LSE[b, h][:, None])
+            vis = _visible(idx, N, causal, window, None if docs is None else np.asarray(docs)[b],
+                           None if block_mask is None else np.asarray(block_mask)[b])
+            s = np.where(vis, c * (qh[b, h] @ kh[b, h].T), -np.inf)
+            live = np.isfinite(LSE[b, h])[:, None]
+            p = np.where(vis & live, np.exp(s - np.where(live, LSE[b, h][:, None], 0.0)), 0.0)
             W[b, h] = p @ np.abs(vh[b, h])
-            U[b, h] = p.max(axis=1)[:, None] * (np.where(np.isfinite(s), 1.0, 0.0)
-                                               @ np.abs(vh[b, h]))
+            U[b, h] = p.max(axis=1)[:, None] * (np.where(vis, 1.0, 0.0) @ np.abs(vh[b, h]))
             sa = np.abs(qh[b, h]) @ np.abs(kh[b, h]).T
-            A[b, h] = np.where(np.isfinite(s), sa, 0.0).max(axis=1)
+            A[b, h] = np.where(vis, sa, 0.0).max(axis=1)
     return {"O": O, "LSE": LSE, "W": W, "U": U, "A": A, "scale": c,
             "codes": {"q": cq, "k": ck, "v": cv, "eq": eq, "ek": ek, "ev": ev}}

@@ -196,3 +196,25 @@ def test_rotation_lowers_error_with_outlier_channels():
         r = fp8.fwd_fp8(q, k, v, causal=True, scale=scale, signs=signs)
         err[name] = np.linalg.norm(r["O"] - o) / np.linalg.norm(o)
     assert err["rotated"] < err["naive"] / 1.5, err
+
+
+def test_fwd_fp8_masks_exact_on_representable_inputs():
+    # the masks of the exact forward carry over: on inputs the format holds
+    # exactly, the FP8 model with a window, documents or a block mask is the
+    # exact masked forward, and an emptied row has zero weights
+    rng = np.random.default_rng(9)
+    B, H, N = 1, 2, 300
+    q = _representable(rng, (B, H, N, 64))
+    k = _representable(rng, (B, H, N, 64))
+    v = _representable(rng, (B, H, N, 64), per_col=True)
+    starts = np.zeros((1, N), dtype=np.int64)      # documents [0,90) [90,200) [200,300)
+    starts[0, 90:200] = 90
+    starts[0, 200:] = 200
+    bm = np.array([[[0, 0, 0], [1, 1, 0], [1, 0, 1]]], dtype=np.uint8)
+    for kw in (dict(window=37), dict(docs=starts), dict(block_mask=bm)):
+        r = fp8.fwd_fp8(q, k, v, causal=True, scale=0.125, **kw)
+        o, lse = oracle.fwd(q, k, v, causal=True, scale=0.125, **kw)
+        np.testing.assert_array_equal(r["O"], o)
+        np.testing.assert_array_equal(r["LSE"], lse)
+    assert np.all(np.isneginf(r["LSE"][..., :128]))
+    assert np.all(r["W"][..., :128, :] == 0) and np.all(r["A"][..., :128] == 0)
