@@ -90,7 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fp8_quantize.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, u64, vp, sz,
                                       vp]
     lib.attn_fp8_quantize.restype = i32
-    lib.attn_fwd_fp8.argtypes = [i32, i64, i64, i64, i64, i64, vp, sz, i32, f32, vp, vp, vp]
+    lib.attn_fwd_fp8.argtypes = [i32, i64, i64, i64, i64, i64, vp, sz, i32, i64, vp, vp, f32, vp,
+                                 vp, vp]
     lib.attn_fwd_fp8.restype = i32
     lib.attn_status_str.argtypes = [i32]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -397,9 +398,12 @@ def attn_fp8_quantize(q, k, v, signs: Optional[int] = None,
 
 def attn_fwd_fp8_codes(workspace: torch.Tensor, B: int, H: int, Hkv: int, N: int,
                        dtype=torch.bfloat16, causal: bool = True, scale: Optional[float] = None,
-                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       window: int = 0, doc_start: Optional[torch.Tensor] = None,
+                       block_mask: Optional[torch.Tensor] = None
                        ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O (dtype), LSE (fp32) of the forward on the codes of an FP8 workspace."""
+    """O (dtype), LSE (fp32) of the forward on the codes of an FP8 workspace;
+    window, doc_start and block_mask as in attn_fwd."""
     lib = load()
     dev = workspace.device
     if dev.type != "cuda" or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -410,16 +414,19 @@ def attn_fwd_fp8_codes(workspace: torch.Tensor, B: int, H: int, Hkv: int, N: int
     _check("lse", lse, o, torch.float32, (B, H, N))
     c = 0.125 if scale is None else float(scale)
     st = lib.attn_fwd_fp8(_dt(o), B, H, Hkv, N, 64, workspace.data_ptr(), workspace.numel(),
-                          1 if causal else 0, c, o.data_ptr(), lse.data_ptr(), _stream(dev))
+                          1 if causal else 0, int(window), _docs(o, doc_start),
+                          _bmask(o, block_mask), c, o.data_ptr(), lse.data_ptr(), _stream(dev))
     _raise("attn_fwd_fp8", st)
     return o, lse
 
 
 def attn_fwd_fp8(q, k, v, causal: bool = True, scale: Optional[float] = None,
-                 signs: Optional[int] = None, workspace: Optional[torch.Tensor] = None
-                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+                 signs: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                 window: int = 0, doc_start: Optional[torch.Tensor] = None,
+                 block_mask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """O, LSE of attention with both products in E4M3 (see attn_fp8_quantize
-    for `signs`); shapes and dtypes as attn_fwd, no window or document mask."""
+    for `signs`); shapes, dtypes and masks as attn_fwd."""
     ws = attn_fp8_quantize(q, k, v, signs, workspace)
     B, H, N, _ = q.shape
-    return attn_fwd_fp8_codes(ws, B, H, k.shape[1], N, q.dtype, causal, _scale(q, scale))
+    return attn_fwd_fp8_codes(ws, B, H, k.shape[1], N, q.dtype, causal, _scale(q, scale),
+                              window=window, doc_start=doc_start, block_mask=block_mask)

@@ -431,22 +431,27 @@ attn_status attn_fp8_quantize(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, 
 }
 
 attn_status attn_fwd_fp8(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* ws, size_t ws_bytes, int causal, float scale, void* O,
-                         float* LSE, void* stream) {
+                         const void* ws, size_t ws_bytes, int causal, int64_t window,
+                         const int32_t* doc_start, const uint8_t* block_mask, float scale,
+                         void* O, float* LSE, void* stream) {
   attn_status st = fp8_shape(dt, B, H, Hkv, N, d, scale);
   if (st != ATTN_OK) return st;
+  int win = 0;
+  if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
   const F8Layout L = fp8_layout(B, H, Hkv, N);
   if (!ws || ws_bytes < L.total) return ATTN_EWORKSPACE;
   const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
   st = check_ptrs({{ws, L.total}}, {{O, t}, {LSE, s}});
   if (st != ATTN_OK) return st;
+  if ((st = check_docs(doc_start, causal, B, N, {{O, t}, {LSE, s}})) != ATTN_OK) return st;
+  if ((st = check_block_mask(block_mask, B, N, {{O, t}, {LSE, s}})) != ATTN_OK) return st;
   const char* w = static_cast<const char*>(ws);
   return finish(fbd::launch_fwd_fp8(
       (int)dt, (const uint8_t*)(w + L.off[ATTN_FP8_Q]), (const uint8_t*)(w + L.off[ATTN_FP8_K]),
       (const uint8_t*)(w + L.off[ATTN_FP8_VT]), (const int*)(w + L.off[ATTN_FP8_EQ]),
       (const int*)(w + L.off[ATTN_FP8_EK]), (const int*)(w + L.off[ATTN_FP8_EV]), O, LSE,
-      (int)(B * H), (int)H, (int)(H / Hkv), (int)N, causal ? 1 : 0, scale,
-      (hipStream_t)stream));
+      (int)(B * H), (int)H, (int)(H / Hkv), win, doc_start, block_mask, (int)N, causal ? 1 : 0,
+      scale, (hipStream_t)stream));
 }
 
 }  // extern "C"

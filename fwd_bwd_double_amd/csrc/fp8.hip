@@ -270,12 +270,13 @@ __device__ __forceinline__ f32x16 splat16(float x) {
 
 constexpr int F8_BLK = 128;   // query rows per workgroup: 4 waves x 32
 
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, bool DOCS, bool BMASK>
 __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
     const uint8_t* __restrict__ V8T, const int* __restrict__ EQ, const int* __restrict__ EK,
     const int* __restrict__ EV, T* __restrict__ O, float* __restrict__ LSE, int N, int NP,
-    int nb, int BH, int H, int grp, int nblk, float scale) {
+    int nb, int BH, int H, int grp, int win, const int* __restrict__ DS,
+    const uint8_t* __restrict__ BMK, int nblk, float scale) {
   __shared__ __attribute__((aligned(16))) uint8_t K0[64 * 64];
   __shared__ __attribute__((aligned(16))) uint8_t V0[64 * 64];
   __shared__ __attribute__((aligned(16))) uint8_t K1[64 * 64];
@@ -308,20 +309,31 @@ __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
   bool seen = false;
   f32x16 o0 = zero16(), o1 = zero16();
 
+  // the masks of the bf16 forward: keys from each row's start (sliding
+  // window, document), block-sparse tiles skipped (a compile-time variant)
+  const int* ds = DOCS ? DS + (size_t)(wk.head / H) * N : nullptr;
+  const int rs = DOCS ? row_start(ds, my_i, win, N) : 0;           // this lane's row
+  const int rs_w = DOCS ? __builtin_amdgcn_readlane(rs, 31) : 0;   // the wave's largest
+  const int rs0 = DOCS ? row_start(ds, q0, win, N) : q0 - win + 1;
+  const int jbeg = CAUSAL ? min(max(0, rs0), q0) / 64 * 64 : 0;
   const int jend = CAUSAL ? min(N, q0 + F8_BLK) : N;
-  const int ntiles = (jend + 63) / 64;
+  const int ntiles = (jend - jbeg + 63) / 64;
+  const int nbm = (N + 127) >> 7;
+  const uint8_t* bmr = BMASK ? BMK + ((size_t)(wk.head / H) * nbm + (q0 >> 7)) * nbm : nullptr;
+  auto kept = [&](int t) { return !BMASK || bmr[(jbeg + t * 64) >> 7] != 0; };
 
   auto tile = [&](int t, const uint8_t* Ks, const uint8_t* Vs, uint8_t* Kn, uint8_t* Vn) {
-    const int j0 = t * 64;
+    const int j0 = jbeg + t * 64;
     wait_dma();
     __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
-    if (t + 1 < ntiles) {
+    if (t + 1 < ntiles && kept(t + 1)) {
       dma8(rk, (uint32_t)(j0 + 64) * HD, HD, Kn, wave, lane);
       dma8(rv, (uint32_t)(j0 + 64), (uint32_t)NP, Vn, wave, lane);
     }
+    if (!kept(t)) return;
     // scores in units of 2^et: x = S / 2^et - m / 2^et (the accumulator
     // starts from -m / 2^et, exact: a power-of-two scaling)
-    const int et = eq + ek[t];
+    const int et = eq + ek[j0 >> 6];
     const float c = __builtin_amdgcn_ldexpf(1.f, et);
     const float sl2c = sl2 * c;
     f32x16 x[2];
@@ -331,11 +343,15 @@ __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int js = j0 + sb * 32;
-      if (CAUSAL ? js + 31 > qw : js + 32 > N) {
+      if (CAUSAL ? (js + 31 > qw || (DOCS ? js < rs_w : js <= qw + 31 - win)) : (js + 32 > N)) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = js + 8 * (v >> 2) + 4 * h + (v & 3);
-          x[sb][v] = (CAUSAL ? j > my_i : j >= N) ? -INFINITY : x[sb][v];
+          bool hide;
+          if constexpr (!CAUSAL) hide = j >= N;
+          else if constexpr (DOCS) hide = j > my_i || j < rs;
+          else hide = (unsigned)(my_i - j) >= (unsigned)win;
+          x[sb][v] = hide ? -INFINITY : x[sb][v];
         }
       }
     }
@@ -384,14 +400,17 @@ __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
     o0 = mma8(ld8(Vs, lane & 31, h), pb, o0);
     o1 = mma8(ld8(Vs, 32 + (lane & 31), h), pb, o1);
   };
-  dma8(rk, 0u, HD, K0, wave, lane);
-  dma8(rv, 0u, (uint32_t)NP, V0, wave, lane);
+  if (!BMASK || (ntiles > 0 && kept(0))) {
+    dma8(rk, (uint32_t)jbeg * HD, HD, K0, wave, lane);
+    dma8(rv, (uint32_t)jbeg, (uint32_t)NP, V0, wave, lane);
+  }
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, K0, V0, K1, V1);
     if (t + 1 < ntiles) tile(t + 1, K1, V1, K0, V0);
   }
+  // a row left with no visible key (block masks only): O = 0, LSE = -inf
   const float lt = half_sum(l);
-  const float inv = 1.f / lt;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int* ev = EV + (size_t)kvh * HD;
 #pragma unroll
   for (int mf = 0; mf < 2; ++mf) {
@@ -407,7 +426,8 @@ __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
     st_cols(O + (size_t)wk.head * N * HD, N, qw, 32 * mf, lane, out);
   }
   if (h == 0 && my_i < N)
-    LSE[(size_t)wk.head * N + my_i] = scale * m + (__builtin_amdgcn_logf(lt) - 8.f) * LN2;
+    LSE[(size_t)wk.head * N + my_i] =
+        lt > 0.f ? scale * m + (__builtin_amdgcn_logf(lt) - 8.f) * LN2 : -INFINITY;
 }
 
 hipError_t launch_fp8_quantize(int dt, const void* Q, const void* K, const void* V, uint8_t* Q8,
@@ -432,21 +452,26 @@ hipError_t launch_fp8_quantize(int dt, const void* Q, const void* K, const void*
 
 hipError_t launch_fwd_fp8(int dt, const uint8_t* Q8, const uint8_t* K8, const uint8_t* V8T,
                           const int* EQ, const int* EK, const int* EV, void* O, float* LSE,
-                          int BH, int H, int grp, int N, int causal, float scale,
-                          hipStream_t st) {
+                          int BH, int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
+                          int causal, float scale, hipStream_t st) {
   const int nb = (N + 63) / 64, NP = nb * 64;
   const int nblk = (N + F8_BLK - 1) / F8_BLK;
-  auto run = [&](auto tag, auto cz) -> hipError_t {
+  auto run = [&](auto tag, auto cz, auto dz, auto bz) -> hipError_t {
     using T = decltype(tag);
-    constexpr bool C = decltype(cz)::value;
-    hipLaunchKernelGGL((fwd_fp8_kernel<T, C>), dim3(nblk * BH), dim3(256), 0, st, Q8, K8, V8T,
-                       EQ, EK, EV, (T*)O, LSE, N, NP, nb, BH, H, grp, nblk, scale);
+    hipLaunchKernelGGL((fwd_fp8_kernel<T, decltype(cz)::value, decltype(dz)::value,
+                                       decltype(bz)::value>),
+                       dim3(nblk * BH), dim3(256), 0, st, Q8, K8, V8T, EQ, EK, EV, (T*)O, LSE, N,
+                       NP, nb, BH, H, grp, win, ds, bm, nblk, scale);
     return hipGetLastError();
   };
-  using CT = std::true_type;
-  using CF = std::false_type;
-  if (dt == 0) return causal ? run(bf16{}, CT{}) : run(bf16{}, CF{});
-  return causal ? run(float{}, CT{}) : run(float{}, CF{});
+  auto masks = [&](auto tag) -> hipError_t {
+    using Y = std::true_type;
+    using F = std::false_type;
+    if (!causal) return bm ? run(tag, F{}, F{}, Y{}) : run(tag, F{}, F{}, F{});
+    if (ds) return bm ? run(tag, Y{}, Y{}, Y{}) : run(tag, Y{}, Y{}, F{});
+    return bm ? run(tag, Y{}, F{}, Y{}) : run(tag, Y{}, F{}, F{});
+  };
+  return dt == 0 ? masks(bf16{}) : masks(float{});
 }
 
 }  // namespace fbd

@@ -110,7 +110,7 @@ hipError_t launch_fp8_quantize(int dt, const void* Q, const void* K, const void*
                                uint64_t signs, hipStream_t st);
 hipError_t launch_fwd_fp8(int dt, const uint8_t* Q8, const uint8_t* K8, const uint8_t* V8T,
                           const int* EQ, const int* EK, const int* EV, void* O, float* LSE,
-                          int BH, int H, int grp, int N, int causal, float scale,
-                          hipStream_t st);
+                          int BH, int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
+                          int causal, float scale, hipStream_t st);
 
 }  // namespace fbd

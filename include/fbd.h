@@ -297,7 +297,8 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
  * Two calls.  attn_fp8_quantize reads Q (B, H, N, 64) and K, V (B, Hkv, N,
  * 64) of type dt and writes the codes and exponents into the workspace.
  * attn_fwd_fp8 reads only the workspace and writes O (B, H, N, 64) of type dt
- * and LSE (B, H, N) fp32, the same outputs as attn_fwd_ex, computed with both
+ * and LSE (B, H, N) fp32, the same outputs as attn_fwd_ex (with its window,
+ * doc_start and block_mask, same rules and errors), computed with both
  * products on the E4M3 matrix cores.  The probabilities are rounded to E4M3
  * as 256 P against the running row max; l sums the unrounded values.
  * The workspace is device memory of attn_fp8_workspace_bytes(B, H, Hkv, N)
@@ -332,8 +333,9 @@ attn_status attn_fp8_quantize(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, 
                               void* stream);
 
 attn_status attn_fwd_fp8(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
-                         const void* ws, size_t ws_bytes, int causal, float scale, void* O,
-                         float* LSE, void* stream);
+                         const void* ws, size_t ws_bytes, int causal, int64_t window,
+                         const int32_t* doc_start, const uint8_t* block_mask, float scale,
+                         void* O, float* LSE, void* stream);
 
 /* Text of a status code (static storage). */
 const char* attn_status_str(attn_status s);

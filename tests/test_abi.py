@@ -146,7 +146,12 @@ def test_fp8_rejects_bad_arguments_before_launch(lib):
     assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 64, q + 8, k, v, 1, 5, ws, need, None) == 3
     # the workspace overlapping an input
     assert lib.attn_fp8_quantize(0, B, H, Hkv, N, 64, q, k, v, 1, 5, k, need, None) == 1
-    assert lib.attn_fwd_fp8(0, B, H, Hkv, N, 64, ws, need - 1, 1, 0.125, o, lse, None) == 4
-    assert lib.attn_fwd_fp8(0, B, H, Hkv, N, 64, ws, need, 1, 0.0, o, lse, None) == 1
-    assert lib.attn_fwd_fp8(0, B, H, Hkv, N, 64, ws, need, 1, 0.125, ws, lse, None) == 1
-    assert lib.attn_fwd_fp8(7, B, H, Hkv, N, 64, ws, need, 1, 0.125, o, lse, None) == 2
+    f8 = lambda dt=0, nb=need, causal=1, win=0, ds=None, bm=None, sc=0.125, out=o: \
+        lib.attn_fwd_fp8(dt, B, H, Hkv, N, 64, ws, nb, causal, win, ds, bm, sc, out, lse, None)
+    assert f8(nb=need - 1) == 4
+    assert f8(sc=0.0) == 1
+    assert f8(out=ws) == 1                  # the output overlaps the workspace
+    assert f8(dt=7) == 2
+    assert f8(causal=0, win=4) == 2         # a window needs the causal mask
+    assert f8(ds=FAKE * 7 + 2) == 3         # doc_start must be 4-byte aligned
+    assert f8(bm=lse) == 1                  # a block mask must not overlap an output

@@ -88,18 +88,24 @@ def fwd_bound(ref, dtype):
 
 def check_fwd(o, lse, ref, dtype):
     og, lg = to_f64(o), to_f64(lse)
-    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg) | np.isneginf(ref["LSE"]))
     bound = fwd_bound(ref, dtype)
     err = np.abs(og - ref["O"])
-    worst = float((err / bound).max())
-    e_o, e_l = rel_l2(og, ref["O"]), rel_l2(lg, ref["LSE"])
-    dl = float(np.abs(lg - ref["LSE"]).max())
+    worst = float(np.where(bound > 0, err / np.where(bound > 0, bound, 1.0),
+                           np.where(err > 0, np.inf, 0.0)).max())
+    fin = np.isfinite(ref["LSE"])
+    e_o, e_l = rel_l2(og, ref["O"]), rel_l2(lg[fin], ref["LSE"][fin])
+    dl = float(np.abs(lg[fin] - ref["LSE"][fin]).max()) if fin.any() else 0.0
     say(f"    O rel-L2 {e_o:.3e}, max err / bound {worst:.3f}; LSE rel-L2 {e_l:.2e} "
-        f"max abs {dl:.2e}")
+        f"max abs {dl:.2e}; empty rows {int((~fin).sum())}")
     assert worst <= 1.0, worst
-    # LSE: the score sums (c eps A) plus exp2 / log2 rounding
-    lb = ref["scale"] * MMA_EPS * ref["A"] + 4e-6 * (1 + np.abs(ref["LSE"]))
-    lw = float((np.abs(lg - ref["LSE"]) / lb).max())
+    # LSE: the score sums (c eps A) plus exp2 / log2 rounding; rows a block
+    # mask leaves empty are -inf on both sides
+    empty = np.isneginf(ref["LSE"])
+    assert np.array_equal(np.isneginf(lg), empty)
+    lsafe = np.where(empty, 0.0, ref["LSE"])
+    lb = ref["scale"] * MMA_EPS * ref["A"] + 4e-6 * (1 + np.abs(lsafe))
+    lw = float((np.abs(np.where(empty, 0.0, lg) - lsafe) / lb).max())
     say(f"    LSE max err / bound {lw:.3f}")
     assert lw <= 1.0, lw
     return e_o
@@ -189,3 +195,33 @@ def test_workspace_errors():
         fbd.attn_fp8_quantize(g["q"], g["k"], g["v"], None, small)
     with pytest.raises(fbd.AttnError):
         fbd.attn_fwd_fp8_codes(small, 1, 2, 2, 64)
+
+
+MASK_CASES = [("window", 333, 50, 0, None, 2, 2), ("docs", 1000, 0, 150, None, 2, 2),
+              ("block", 300, 0, 0, 0.4, 2, 1), ("all", 1000, 200, 300, 0.6, 4, 2)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("name,N,window,mean_len,density,H,Hkv", MASK_CASES)
+def test_forward_masks(name, N, window, mean_len, density, H, Hkv, dtype):
+    """The FP8 forward under the bf16 forward's masks: sliding window, packed
+    documents, block-sparse (with rows left empty) and all three together."""
+    from test_gpu_parity import block_masks, doc_starts
+    B = 2
+    say(f"[gpu] fp8 masks {name} B={B} H={H} Hkv={Hkv} N={N} window={window} "
+        f"docs={mean_len} density={density} {dtype}")
+    x = synthetic.fp8_inputs(8500 + N, B, H, Hkv, N, dtype, outlier_channels=(9,),
+                             outlier_mag=5.0)
+    signs = synthetic.sign_mask(8500 + N)
+    docs = doc_starts(B, N, 81 + N, mean_len) if mean_len else None
+    bm = block_masks(B, N, 33 + N, density, False) if density else None
+    g = {k: v.cuda() for k, v in x.items()}
+    o, lse = fbd.attn_fwd_fp8(
+        g["q"], g["k"], g["v"], causal=True, scale=0.125 / 5, signs=signs, window=window,
+        doc_start=None if docs is None else torch.from_numpy(docs.astype(np.int32)).cuda(),
+        block_mask=None if bm is None else torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    a = {k: to_f64(v) for k, v in x.items()}
+    ref = fp8.fwd_fp8(a["q"], a["k"], a["v"], causal=True, scale=0.125 / 5, signs=signs,
+                      window=window, docs=docs, block_mask=bm)
+    check_fwd(o, lse, ref, dtype)
