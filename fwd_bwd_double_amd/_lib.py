@@ -266,7 +266,7 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
-    beta, -LSE*log2(e) and kappa = alpha*D + beta afterwards."""
+    beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) afterwards."""
     lib = load()
     Hkv = _kv_heads(q, k)
     kvs = _kv_shape(q, Hkv)

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     Aws[soff + my_i] = alpha;
     Bws[soff + my_i] = beta;
     Lws[soff + my_i] = -lse2;
-    Kws[soff + my_i] = alpha * Di + beta;
+    Kws[soff + my_i] = -(alpha * Di + beta);   // -kappa: the column pass's U starts there
   }
 }
 
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const uint8_t* __restrict__ BMK, float scale) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
-  // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, kappa of the tile's rows
+  // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, -kappa of the tile's rows
   struct Buf {
     T q[BM * HD], dO[BM * HD], a[BM * HD];
     float nl[BM], D[BM], al[BM], ka[BM];
@@ -400,19 +400,19 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
         mma(gv1, ld_tr(dOs, 32, it + tt, lane), hf);
       }
       // Sh = P o (W (dP - D) + U - alpha dP - beta) = P o (h (dP - D) + U - kappa)
-      // with U = dO C^T and kappa = alpha D + beta per row:  gK += Sh^T Q
-      f32x16 u = zero16();
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(u, ld_row(dOs, ib, kb, lane), cf[kb]);
+      // with U = dO C^T and kappa = alpha D + beta per row:  gK += Sh^T Q.
+      // The U product starts from the rows' -kappa, so no subtraction remains.
+      f32x16 u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sK[ib + 8 * q + 4 * h]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = 4 * q + r;
-          u[v] = ps[v] * (__builtin_fmaf(hv[v], dpd[v], u[v]) - k4[r]);
-        }
+        for (int r = 0; r < 4; ++r) u[4 * q + r] = k4[r];
       }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(u, ld_row(dOs, ib, kb, lane), cf[kb]);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) u[v] = ps[v] * __builtin_fmaf(hv[v], dpd[v], u[v]);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         float sh[8];

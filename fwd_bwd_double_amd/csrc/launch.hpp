@@ -83,7 +83,7 @@ hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const
                       const uint8_t* bm, int N, int causal, float scale, int gproj, int passes,
                       hipStream_t st);
 
-// BoB workspace: D, alpha, beta, -LSE*log2(e) and kappa = alpha*D + beta per row.
+// BoB workspace: D, alpha, beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) per row.
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,

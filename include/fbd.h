@@ -113,7 +113,7 @@ attn_status attn_bwd(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace of attn_bob in bytes: five fp32 arrays of B*H*N rows, in order
- * D, alpha, beta, -LSE*log2(e) and kappa = alpha*D + beta, all written by the
+ * D, alpha, beta, -LSE*log2(e) and -kappa = -(alpha*D + beta), all written by the
  * row pass for the column pass. */
 size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
