@@ -19,9 +19,11 @@ sample of the same workload on this host.
 on the same workload instead of the step, one JSON line.
 
 `--sweep` instead times each operation separately over sequence lengths
-1k .. 256k (H=12, d=64, B = max(1, 16384/N), causal, GProj on) and the other
-workload shapes, printing one JSON line per case; it includes the FP8 forward
-(quantisation pre-pass and the forward on the codes, against the fp8 peak).
+1k .. 256k (H=12, d=64, B = max(1, 16384/N), causal, GProj on), the other
+workload shapes and the extended forms (grouped-query heads, a sliding window,
+packed documents, a block-sparse mask, the HVP call), printing one JSON line
+per case; it includes the FP8 forward (quantisation pre-pass and the forward
+on the codes, against the fp8 peak).
 """
 from __future__ import annotations
 
@@ -252,10 +254,12 @@ def fp8_bench(args):
 def sweep():
     """Each operation timed on its own (HIP events on the launch stream; median
     of the repetitions after a warm-up) for N = 1k .. 256k with H = 12, d = 64,
-    B = max(1, 16384 / N), and for the gpt2s-layer (B8 H12 N1024) and
-    large-key (B1 H12 N16384) shapes.  Inputs: seeded device-side normal draws
-    with the BoB workload's distributions (Q, K, V, dO ~ 0.5 N(0,1),
-    cotangents ~ N(0,1)), rounded to bf16."""
+    B = max(1, 16384 / N), for the gpt2s-layer (B8 H12 N1024) and large-key
+    (B1 H12 N16384) shapes, and for the extended forms: grouped-query heads,
+    a sliding window, packed documents, a block-sparse mask and the HVP call.
+    Inputs: seeded device-side normal draws with the BoB workload's
+    distributions (Q, K, V, dO ~ 0.5 N(0,1), cotangents ~ N(0,1)), rounded to
+    bf16.  FLOP rates count the (query, key) pairs each case leaves visible."""
     import numpy as np
     import torch
 
@@ -263,57 +267,99 @@ def sweep():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cases = [("gpt2s-layer", 8, 12, 1024, 0.0), ("large-key", 1, 12, 16384, 0.0)]
-    cases += [(f"sweep-N{n}", max(1, 16384 // n), 12, n, 0.0)
+
+    def case(name, B, H, N, **kw):
+        return dict(name=name, B=B, H=H, N=N, Hkv=kw.get("Hkv", H), window=kw.get("window", 0),
+                    mean_doc=kw.get("mean_doc", 0), density=kw.get("density", 0.0),
+                    hvp=kw.get("hvp", False))
+
+    cases = [case("gpt2s-layer", 8, 12, 1024), case("large-key", 1, 12, 16384)]
+    cases += [case(f"sweep-N{n}", max(1, 16384 // n), 12, n)
               for n in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144)]
-    # block-sparse: each 128 x 128 block below the diagonal kept with
-    # probability 1/2 (seeded), diagonal blocks kept
-    cases += [("bsparse-N16384", 1, 12, 16384, 0.5)]
+    cases += [
+        # grouped-query: 12 query heads over 4 key/value heads
+        case("gqa3-N16384", 1, 12, 16384, Hkv=4),
+        # causal sliding window of 4096 keys
+        case("window4k-N65536", 1, 12, 65536, window=4096),
+        # packed documents, lengths ~ geometric with mean 4096 (seeded)
+        case("docs4k-N65536", 1, 12, 65536, mean_doc=4096),
+        # block-sparse: each 128 x 128 block below the diagonal kept with
+        # probability 1/2 (seeded), diagonal blocks kept
+        case("bsparse-N16384", 1, 12, 16384, density=0.5),
+        # the Hessian-vector product call (fwd, bwd, BoB in one call)
+        case("hvp-N4096", 4, 12, 4096, hvp=True),
+    ]
     d = 64
-    for name, B, H, N, density in cases:
+    for cs in cases:
+        name, B, H, N, Hkv = cs["name"], cs["B"], cs["H"], cs["N"], cs["Hkv"]
         gen = torch.Generator(device=dev)
         gen.manual_seed(1000 + N)
 
-        def draw(std):
-            return (torch.randn((B, H, N, d), generator=gen, device=dev) * std).to(torch.bfloat16)
+        def draw(std, heads=H):
+            return (torch.randn((B, heads, N, d), generator=gen, device=dev) * std).to(
+                torch.bfloat16)
 
-        q, k, v, do = draw(0.5), draw(0.5), draw(0.5), draw(0.5)
-        a, bk, c = draw(1.0), draw(1.0), draw(1.0)
+        q, k, v, do = draw(0.5), draw(0.5, Hkv), draw(0.5, Hkv), draw(0.5)
+        a, bk, c = draw(1.0), draw(1.0, Hkv), draw(1.0, Hkv)
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), device=dev)
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-        gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4))
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+        gq, gk, gv, gdo = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(k),
+                           torch.empty_like(q))
         ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
         ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
-        bm, pairs = None, B * H * N * (N + 1) / 2
-        if density:
+        i = np.arange(N, dtype=np.float64)
+        vis = i + 1                                   # visible keys per query row
+        bm = ds = None
+        win = cs["window"]
+        if win:
+            vis = np.minimum(vis, win)
+        if cs["mean_doc"]:
+            rng = np.random.default_rng(77)
+            starts = np.zeros((B, N), dtype=np.int64)
+            for b in range(B):
+                r = 0
+                while r < N:
+                    n = int(min(N - r, rng.geometric(1.0 / cs["mean_doc"])))
+                    starts[b, r:r + n] = r
+                    r += n
+            ds = torch.from_numpy(starts.astype(np.int32)).to(dev)
+            vis = (np.arange(N)[None] - starts + 1).astype(np.float64)
+        pairs = H * float(np.broadcast_to(vis, (B, N)).sum())
+        if cs["density"]:
             nb = (N + 127) // 128
             rng = np.random.default_rng(2024)
-            keep = (rng.random((B, nb, nb)) < density) | np.eye(nb, dtype=bool)[None]
+            keep = (rng.random((B, nb, nb)) < cs["density"]) | np.eye(nb, dtype=bool)[None]
             bm = torch.from_numpy(keep.astype(np.uint8)).to(dev)
             pairs = H * float((np.tril(keep.astype(np.float64), -1)).sum() * 128 * 128 +
                               keep[:, np.arange(nb), np.arange(nb)].sum() * 128 * 129 / 2)
-        ws8 = torch.empty(fbd.fp8_workspace_bytes(B, H, H, N), device=dev, dtype=torch.uint8)
-        o8 = torch.empty_like(q)
-        signs = 0x9E3779B97F4A7C15
         sc = 1.0 / 8.0
+        mk = dict(window=win, doc_start=ds, block_mask=bm)
         ops = {
-            "fwd": lambda: fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse,
-                                        block_mask=bm),
+            "fwd": lambda: fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse, **mk),
             "bwd": lambda: fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=sc, gproj=True,
-                                        workspace=ws_b, outs=(dq, dk, dv), block_mask=bm),
+                                        workspace=ws_b, outs=(dq, dk, dv), **mk),
             "bob": lambda: fbd.attn_bob(q, k, v, o, lse, do, a, bk, c, causal=True, scale=sc,
-                                        workspace=ws_bb, outs=(gq, gk, gv, gdo), block_mask=bm),
-            # FP8 forward: the quantisation pre-pass (rotated) and the forward on the codes
-            "fp8_quant": lambda: fbd.attn_fp8_quantize(q, k, v, signs, ws8),
-            "fp8_fwd": lambda: fbd.attn_fwd_fp8_codes(ws8, B, H, H, N, torch.bfloat16, True, sc,
-                                                      out=o8, lse=lse),
+                                        workspace=ws_bb, outs=(gq, gk, gv, gdo), **mk),
         }
-        if density:   # the FP8 forward takes no block mask
-            ops.pop("fp8_quant")
-            ops.pop("fp8_fwd")
+        plain = Hkv == H and not (win or cs["mean_doc"] or cs["density"] or cs["hvp"])
+        if plain:
+            ws8 = torch.empty(fbd.fp8_workspace_bytes(B, H, H, N), device=dev, dtype=torch.uint8)
+            o8 = torch.empty_like(q)
+            signs = 0x9E3779B97F4A7C15
+            # FP8 forward: the quantisation pre-pass (rotated) and the forward on the codes
+            ops["fp8_quant"] = lambda: fbd.attn_fp8_quantize(q, k, v, signs, ws8)
+            ops["fp8_fwd"] = lambda: fbd.attn_fwd_fp8_codes(ws8, B, H, H, N, torch.bfloat16,
+                                                            True, sc, out=o8, lse=lse)
+        if cs["hvp"]:
+            ws_h = torch.empty(fbd.hvp_workspace_bytes(B, H, N) // 4, device=dev)
+            ops = {"hvp": lambda: fbd.attn_hvp(q, k, v, do, a, bk, c, causal=True, scale=sc,
+                                               gproj=True, workspace=ws_h)}
         exec_units = {"fwd": UNITS["fwd"], "bwd": UNITS["bwd_row"] + UNITS["bwd_col"],
-                      "bob": UNITS["bob_row"] + UNITS["bob_col"]}
+                      "bob": UNITS["bob_row"] + UNITS["bob_col"], "fp8_fwd": UNITS["fwd"]}
+        exec_units["hvp"] = exec_units["fwd"] + exec_units["bwd"] + exec_units["bob"]
+        conv = {"fwd": CONV["fwd"], "bwd": CONV["bwd"], "bob": CONV["bob"],
+                "fp8_fwd": CONV["fwd"], "hvp": CONV["fwd"] + CONV["bwd"] + CONV["bob"]}
         reps = 3 if N >= 65536 else 10
         res = {}
         for op, fn in ops.items():
@@ -332,22 +378,22 @@ def sweep():
                 res[op] = {"ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9}
                 continue
             peak = PEAK_FP8_TFLOPS if op == "fp8_fwd" else PEAK_BF16_TFLOPS
-            u = exec_units["fwd" if op == "fp8_fwd" else op]
             res[op] = {"ms": ms,
-                       "conv_tflops": CONV["fwd" if op == "fp8_fwd" else op] * d * pairs
-                       / (ms * 1e-3) / 1e12,
-                       "executed_frac_mfma_peak": u * 2 * d * pairs / (ms * 1e-3) / 1e12 / peak}
-        line = {"case": name, "B": B, "H": H, "N": N, "d": d, "causal": True, "gproj": True,
-                "block_density": density, "pairs": pairs,
+                       "conv_tflops": conv[op] * d * pairs / (ms * 1e-3) / 1e12,
+                       "executed_frac_mfma_peak":
+                           exec_units[op] * 2 * d * pairs / (ms * 1e-3) / 1e12 / peak}
+        line = {"case": name, "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "causal": True,
+                "gproj": True, "window": win, "mean_doc": cs["mean_doc"],
+                "block_density": cs["density"], "pairs": pairs,
                 "dtype": "bf16", "data": "synthetic", "ops": res,
                 "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9}
         print(json.dumps(line), flush=True)
-        print(f"[sweep] {name:14s} " + "  ".join(
+        print(f"[sweep] {name:15s} " + "  ".join(
             f"{op} {r['ms']:9.3f} ms " + (f"{r['gbs']:7.0f} GB/s" if "gbs" in r else
                                           f"{r['conv_tflops']:7.1f} TF "
                                           f"{100 * r['executed_frac_mfma_peak']:5.1f}%")
             for op, r in res.items()), file=sys.stderr, flush=True)
-        del q, k, v, do, a, bk, c, o, lse, dq, dk, dv, gq, gk, gv, gdo, ws_b, ws_bb, ws8, o8
+        del q, k, v, do, a, bk, c, o, lse, dq, dk, dv, gq, gk, gv, gdo, ws_b, ws_bb, ops
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
 
