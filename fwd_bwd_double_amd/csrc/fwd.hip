@@ -11,11 +11,15 @@
 // subtracting the max before scaling makes the largest weight exactly 1 (GProj
 // page, rit.work flashattention-bf16-gradient-gproj, section "Why the error
 // shows up at the end of training", on fusing the scale and the max into one
-// operation).  For bf16 the subtraction and the scaling share one FMA: the
-// weight at the max is then within 2^-10 of 1, and the bf16 rounding of P,
-// which both l and P V use, makes it exactly 1 again.  The subtraction of the running max costs no VALU work: the
-// score MFMAs start from -m in their accumulator.  Only when a row's max grows
-// inside a tile is the growth subtracted explicitly.  Key tiles entirely in
+// operation).  fp32 operands keep that order exactly: the score MFMAs start
+// from -m in their accumulator, so they arrive as S - m, and only a row whose
+// max grew inside a tile subtracts the growth before the scaling.  For bf16
+// the score MFMAs start from zero (no accumulator image of -m to rebuild per
+// tile) and the subtraction and the scaling share the FMA that forms the
+// exponent, (S - m) * scale * log2(e) as one rounding of S * c - m * c: the
+// weight at the max is then 2^e with |e| at most half an ulp of m * c, which
+// the bf16 rounding of P (the value both l and P V use) takes to exactly 1
+// while |m * c| < 2^15.  Key tiles entirely in
 // the future of the workgroup's rows are never loaded (explainer page, section
 // "Causal masking is where trading gets a discount").
 //
@@ -64,20 +68,22 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
   const auto rk = make_rsrc(K + kvoff, hbytes);
   const auto rv = make_rsrc(V + kvoff, hbytes);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar, so the DMA's LDS addresses stay in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = wk.blk * FWD_BLK;
   const int qw = q0 + wave * FWD_G * WROWS;
   const int h = lane >> 5;
   const float sl2 = scale * LOG2E;
 
   // Per query group: running max m (raw score units), running sum l and the
-  // output accumulator o.  The score products of a tile start from -m in the
-  // MFMA accumulator (negm), so they arrive as x = S - m: the max is
-  // subtracted without a VALU op.  The max, and with it the rescale of o and
+  // output accumulator o.  fp32: the score products of a tile start from -m
+  // in the MFMA accumulator (negm) and arrive as x = S - m.  bf16: they start
+  // from zero and arrive as x = S.  The max, and with it the rescale of o and
   // l, is updated once per key tile.  `seen` marks rows that have met a
   // visible key (until then m is a placeholder 0 and nothing is
   // accumulated): with a sliding window a row's first visible key can lie
   // beyond the block's first tile.
+  constexpr bool ACC_M = sizeof(T) == 4;   // scores arrive as S - m
   Frag<T> qf[FWD_G][4];
   float m[FWD_G], l[FWD_G];
   bool seen[FWD_G];
@@ -137,16 +143,17 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
       for (int kb = 0; kb < 4; ++kb) kr[kb] = ld_row(Ks, sb * 32, kb, lane);
 #pragma unroll
       for (int g = 0; g < FWD_G; ++g) {
-        x[sb][g] = negm[g];
+        x[sb][g] = ACC_M ? negm[g] : zero16();
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) mma(x[sb][g], kr[kb], qf[g][kb]);
       }
     }
     // Online-softmax update per query group.  On the first tile there is no
-    // history: m becomes the exact tile max.  Later, base = max(x) > 0 where
-    // a row's max grew; subtracting base before scaling gives the new row
-    // max weight exactly 1.
-    float base[FWD_G];
+    // history: m becomes the exact tile max.  fp32: later, base = max(x) > 0
+    // where a row's max grew; subtracting base before scaling gives the new
+    // row max weight exactly 1.  bf16: m becomes max(m, max(x)) and the
+    // exponent subtracts m * scale (nb).
+    float base[FWD_G], nb[FWD_G];
     bool sub[FWD_G];
 #pragma unroll
     for (int g = 0; g < FWD_G; ++g) {
@@ -177,20 +184,32 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
 #pragma unroll
         for (int v = 0; v < 16; ++v) xm = fmaxf(xm, x[sb][g][v]);
       xm = half_max(xm);
-      // a row meeting its first visible key takes that tile's max as m (x is
-      // the raw score there); a row already seen subtracts the growth of its
-      // max and rescales; a row with no visible key yet keeps everything zero
+      // a row meeting its first visible key takes that tile's max as m; a row
+      // already seen moves m by the growth of its max and rescales; a row
+      // with no visible key yet keeps everything zero
       const bool fresh = !seen[g] && xm > -INFINITY;
-      base[g] = seen[g] ? fmaxf(xm, 0.f) : (fresh ? xm : 0.f);
-      if (__any(seen[g] && xm > 0.f)) {
-        const float alpha = seen[g] ? __builtin_amdgcn_exp2f(-base[g] * sl2) : 1.f;
-        l[g] *= alpha;
-        o[g][0] *= alpha;
-        o[g][1] *= alpha;
+      if constexpr (ACC_M) {
+        base[g] = seen[g] ? fmaxf(xm, 0.f) : (fresh ? xm : 0.f);
+        if (__any(seen[g] && xm > 0.f)) {
+          const float alpha = seen[g] ? __builtin_amdgcn_exp2f(-base[g] * sl2) : 1.f;
+          l[g] *= alpha;
+          o[g][0] *= alpha;
+          o[g][1] *= alpha;
+        }
+        m[g] += base[g];
+        sub[g] = __any(base[g] != 0.f);
+      } else {
+        const float mn = seen[g] ? fmaxf(m[g], xm) : (fresh ? xm : 0.f);
+        if (__any(seen[g] && xm > m[g])) {
+          const float alpha = seen[g] ? __builtin_amdgcn_exp2f((m[g] - mn) * sl2) : 1.f;
+          l[g] *= alpha;
+          o[g][0] *= alpha;
+          o[g][1] *= alpha;
+        }
+        m[g] = mn;
+        nb[g] = -mn * sl2;
       }
-      m[g] += base[g];
       seen[g] = seen[g] || fresh;
-      sub[g] = __any(base[g] != 0.f);
     }
 #pragma unroll
     for (int sb = 0; sb < NS; ++sb) {
@@ -198,19 +217,16 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
 #pragma unroll
       for (int g = 0; g < FWD_G; ++g) {
         float p[16];
-        if (sub[g]) {
-          if constexpr (sizeof(T) == 2) {
-            // one FMA: the weight at the max is 2^e with |e| < 2^-10 (the
-            // rounding of base * sl2), which the bf16 rounding of P below
-            // takes to exactly 1, so l and P V still see the exact 1
-            const float nb = -base[g] * sl2;
+        if constexpr (!ACC_M) {
+          // one FMA per weight: the weight at the max is 2^e with |e| at
+          // most half an ulp of m * sl2, which the bf16 rounding below takes
+          // to exactly 1, so l and P V still see the exact 1
 #pragma unroll
-            for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(x[sb][g][v], sl2, nb));
-          } else {
+          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(x[sb][g][v], sl2, nb[g]));
+        } else if (sub[g]) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              p[v] = __builtin_amdgcn_exp2f((x[sb][g][v] - base[g]) * sl2);
-          }
+          for (int v = 0; v < 16; ++v)
+            p[v] = __builtin_amdgcn_exp2f((x[sb][g][v] - base[g]) * sl2);
         } else {
 #pragma unroll
           for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(x[sb][g][v] * sl2);
@@ -231,9 +247,9 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
         }
       }
     }
+    if constexpr (ACC_M) {
 #pragma unroll
-    for (int g = 0; g < FWD_G; ++g) {
-      negm[g] = zero16() - m[g];
+      for (int g = 0; g < FWD_G; ++g) negm[g] = zero16() - m[g];
     }
   };
   if (!BMASK || (ntiles > 0 && kept(0))) {
