@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
   const auto rk = make_rsrc(K + kvoff, hbytes);
   const auto rv = make_rsrc(V + kvoff, hbytes);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = wk.blk * BLK;
   const int qw = q0 + wave * WROWS;
   const int my_i = qw + (lane & 31);
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   const size_t hoff = (size_t)wk.head * N * HD;   // key-side tensors
   const int qh0 = first_q_head(wk.head, H, grp);
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k0 = wk.blk * BLK;
   const int kw = k0 + wave * WROWS;
   const int my_j = kw + (lane & 31);

@@ -286,7 +286,8 @@ __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
   const int kvh = kv_head(wk.head, H, grp);
   const auto rk = make_rsrc(K8 + (size_t)kvh * N * HD, (uint32_t)N * HD);
   const auto rv = make_rsrc(V8T + (size_t)kvh * HD * NP, (uint32_t)HD * NP);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6),
+            h = lane >> 5;
   const int q0 = wk.blk * F8_BLK;
   const int qw = q0 + wave * WROWS;
   const int my_i = qw + (lane & 31);
