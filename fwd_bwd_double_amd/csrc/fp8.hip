@@ -360,10 +360,10 @@ __global__ __launch_bounds__(256, FBD_FP8_OCC) void fwd_fp8_kernel(
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) xm = fmaxf(xm, x[sb][v]);
+      for (int v = 0; v < 16; ++v) xm = vmax(xm, x[sb][v]);
     xm = half_max(xm);
     const bool fresh = !seen && xm > -INFINITY;
-    const float base = seen ? fmaxf(xm, 0.f) : (fresh ? xm : 0.f);
+    const float base = seen ? vmax(xm, 0.f) : (fresh ? xm : 0.f);
     if (__any(seen && xm > 0.f)) {
       const float alpha = seen ? __builtin_amdgcn_exp2f(-base * sl2c) : 1.f;
       l *= alpha;

@@ -182,14 +182,14 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
 #pragma unroll
       for (int sb = 0; sb < NS; ++sb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) xm = fmaxf(xm, x[sb][g][v]);
+        for (int v = 0; v < 16; ++v) xm = vmax(xm, x[sb][g][v]);
       xm = half_max(xm);
       // a row meeting its first visible key takes that tile's max as m; a row
       // already seen moves m by the growth of its max and rescales; a row
       // with no visible key yet keeps everything zero
       const bool fresh = !seen[g] && xm > -INFINITY;
       if constexpr (ACC_M) {
-        base[g] = seen[g] ? fmaxf(xm, 0.f) : (fresh ? xm : 0.f);
+        base[g] = seen[g] ? vmax(xm, 0.f) : (fresh ? xm : 0.f);
         if (__any(seen[g] && xm > 0.f)) {
           const float alpha = seen[g] ? __builtin_amdgcn_exp2f(-base[g] * sl2) : 1.f;
           l[g] *= alpha;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
         m[g] += base[g];
         sub[g] = __any(base[g] != 0.f);
       } else {
-        const float mn = seen[g] ? fmaxf(m[g], xm) : (fresh ? xm : 0.f);
+        const float mn = seen[g] ? vmax(m[g], xm) : (fresh ? xm : 0.f);
         if (__any(seen[g] && xm > m[g])) {
           const float alpha = seen[g] ? __builtin_amdgcn_exp2f((m[g] - mn) * sl2) : 1.f;
           l[g] *= alpha;

@@ -72,10 +72,17 @@ __device__ __forceinline__ float half_sum(float x) {
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Maximum of two scores.  The NaN-propagating maximum lowers to
+// v_maximum3_f32 on gfx950 with no canonicalising moves of its inputs (fmaxf's
+// NaN-ignoring form adds one v_max_f32 x, x per operand read from an MFMA
+// result); scores are finite or -inf, where the two agree.
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Sum of the eight element-type values of an operand fragment, added to acc
