@@ -10,10 +10,12 @@ GPU; torch provides device memory and the stream, the kernels do the work.
 """
 from ._lib import (AttnError, attn_bob, attn_bwd, attn_fwd, attn_hvp,  # noqa: F401
                    bob_workspace_bytes, bwd_workspace_bytes, hvp_workspace_bytes, load,
+                   bob_ex_workspace_bytes, bwd_ex_workspace_bytes,
                    LIB_PATH, attn_fwd_fp8, attn_fp8_quantize, attn_fwd_fp8_codes, fp8_parts,
                    fp8_workspace_bytes)
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bob", "attn_hvp", "bwd_workspace_bytes",
-           "bob_workspace_bytes", "hvp_workspace_bytes", "AttnError", "load", "LIB_PATH",
+           "bob_workspace_bytes", "hvp_workspace_bytes", "bwd_ex_workspace_bytes",
+           "bob_ex_workspace_bytes", "AttnError", "load", "LIB_PATH",
            "attn_fwd_fp8", "attn_fp8_quantize", "attn_fwd_fp8_codes", "fp8_parts",
            "fp8_workspace_bytes"]

@@ -66,6 +66,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_passes.restype = i32
     lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
     lib.attn_bob_passes.restype = i32
+    for fn in (lib.attn_bwd_ex_workspace_bytes, lib.attn_bob_ex_workspace_bytes):
+        fn.argtypes = [i64, i64, i64, i64]
+        fn.restype = sz
     # extended forms: Hkv after H; the window, doc_start and block_mask after causal
     lib.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, vp, vp, f32,
                                 vp, vp, vp]
@@ -179,6 +182,14 @@ def bob_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(load().attn_bob_workspace_bytes(B, H, N))
 
 
+def bwd_ex_workspace_bytes(B: int, H: int, Hkv: int, N: int) -> int:
+    return int(load().attn_bwd_ex_workspace_bytes(B, H, Hkv, N))
+
+
+def bob_ex_workspace_bytes(B: int, H: int, Hkv: int, N: int) -> int:
+    return int(load().attn_bob_ex_workspace_bytes(B, H, Hkv, N))
+
+
 def hvp_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(load().attn_hvp_workspace_bytes(B, H, N))
 
@@ -218,7 +229,9 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
              block_mask: Optional[torch.Tensor] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV of <dO, O>.  `workspace` (fp32, >= bwd_workspace_bytes) holds
-    the row states D, r and -LSE*log2(e), each B*H*N floats, afterwards.
+    the row states D, r and -LSE*log2(e), each B*H*N floats, afterwards; when
+    none is given, grouped-query heads get one of bwd_ex_workspace_bytes,
+    which lets the column pass split each group over several workgroups.
     passes: 1 row pass, 2 column pass, 3 both."""
     lib = load()
     Hkv = _kv_heads(q, k)
@@ -239,7 +252,7 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
     ext = Hkv != H or window != 0 or doc_start is not None or block_mask is not None
     if ext and passes != 3:
         raise ValueError("grouped-query or masked backward runs both passes (passes=3)")
-    need = lib.attn_bwd_workspace_bytes(B, H, N)
+    need = lib.attn_bwd_ex_workspace_bytes(B, H, Hkv, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     if workspace.device != q.device or not workspace.is_contiguous():
@@ -266,7 +279,9 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
-    beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) afterwards."""
+    beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) afterwards; when none is
+    given, grouped-query heads get one of bob_ex_workspace_bytes (split column
+    pass)."""
     lib = load()
     Hkv = _kv_heads(q, k)
     kvs = _kv_shape(q, Hkv)
@@ -288,7 +303,7 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
     ext = Hkv != H or window != 0 or doc_start is not None or block_mask is not None
     if ext and passes != 3:
         raise ValueError("grouped-query or masked BoB runs both passes (passes=3)")
-    need = lib.attn_bob_workspace_bytes(B, H, N)
+    need = lib.attn_bob_ex_workspace_bytes(B, H, Hkv, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     if workspace.device != q.device or not workspace.is_contiguous():

@@ -121,6 +121,27 @@ attn_status check_ptrs(const std::vector<Arg>& ins, const std::vector<Arg>& outs
   return ATTN_OK;
 }
 
+// Column-pass slices for grouped-query heads.  A column-pass workgroup owns
+// a (key block, key head) pair and streams all grp query heads of the group;
+// at few key heads that leaves too few, too long workgroups for 256 CUs (and
+// the causal blocks' unequal lengths no longer even out).  The smallest
+// divisor nsl of grp that gives at least 1536 workgroups (six per CU) splits
+// each group into nsl slices of query heads (nsl = grp when none does); the
+// slices write fp32 partial sums that one more kernel adds up.
+int col_slices(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
+  const int64_t grp = H / Hkv;
+  const int64_t wgs = (N + 127) / 128 * B * Hkv;
+  for (int64_t s = 1; s < grp; ++s)
+    if (grp % s == 0 && wgs * s >= 1536) return (int)s;
+  return (int)grp;
+}
+// Bytes of the partial sums of nsl slices (two fp32 key-side tensors each),
+// placed after the row states at a 256-byte boundary.
+size_t part_bytes(int64_t B, int64_t Hkv, int64_t N, int nsl) {
+  return nsl > 1 ? (size_t)2 * nsl * (size_t)B * Hkv * N * 64 * sizeof(float) : 0;
+}
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 attn_status finish(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -155,6 +176,20 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
 size_t attn_bob_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
   return (size_t)5 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+size_t attn_bwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
+  if (B <= 0 || H <= 0 || N <= 0 || check_heads(H, Hkv) != ATTN_OK) return 0;
+  const size_t base = attn_bwd_workspace_bytes(B, H, N);
+  const int nsl = col_slices(B, H, Hkv, N);
+  return nsl > 1 ? round256(base) + part_bytes(B, Hkv, N, nsl) : base;
+}
+
+size_t attn_bob_ex_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
+  if (B <= 0 || H <= 0 || N <= 0 || check_heads(H, Hkv) != ATTN_OK) return 0;
+  const size_t base = attn_bob_workspace_bytes(B, H, N);
+  const int nsl = col_slices(B, H, Hkv, N);
+  return nsl > 1 ? round256(base) + part_bytes(B, Hkv, N, nsl) : base;
 }
 
 attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
@@ -196,8 +231,13 @@ static attn_status bwd_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
   int win = 0;
   if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
-  const size_t need = attn_bwd_workspace_bytes(B, H, N);
+  size_t need = attn_bwd_workspace_bytes(B, H, N);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  // split column pass when the workspace also holds the partial sums
+  int nsl = col_slices(B, H, Hkv, N);
+  const size_t poff = round256(need);
+  if (nsl > 1 && ws_bytes >= poff + part_bytes(B, Hkv, N, nsl)) need = poff + part_bytes(B, Hkv, N, nsl);
+  else nsl = 1;
   const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
   const size_t tk = (size_t)B * Hkv * N * d * elem_size(dt);
   st = check_ptrs({{Q, t}, {K, tk}, {V, tk}, {O, t}, {LSE, s}, {dO, t}},
@@ -213,7 +253,8 @@ static attn_status bwd_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   float* Lws = Rws + bhn;
   return finish(fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws,
                                 (int)(B * H), (int)H, (int)(H / Hkv), win, doc_start, block_mask,
-                                (int)N, causal ? 1 : 0, scale, gproj ? 1 : 0, passes,
+                                (int)N, causal ? 1 : 0, scale, gproj ? 1 : 0, passes, nsl,
+                                nsl > 1 ? (float*)((char*)ws + poff) : nullptr,
                                 (hipStream_t)stream));
 }
 
@@ -257,8 +298,13 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
   int win = 0;
   if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
-  const size_t need = attn_bob_workspace_bytes(B, H, N);
+  size_t need = attn_bob_workspace_bytes(B, H, N);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  // split column pass when the workspace also holds the partial sums
+  int nsl = col_slices(B, H, Hkv, N);
+  const size_t poff = round256(need);
+  if (nsl > 1 && ws_bytes >= poff + part_bytes(B, Hkv, N, nsl)) need = poff + part_bytes(B, Hkv, N, nsl);
+  else nsl = 1;
   const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
   const size_t tk = (size_t)B * Hkv * N * d * elem_size(dt);
   st = check_ptrs({{Q, t}, {K, tk}, {V, tk}, {O, t}, {LSE, s}, {dO, t}, {g_dQ, t}, {g_dK, tk},
@@ -280,7 +326,9 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
   return finish(fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, g_Q, g_K, g_V,
                                 g_dO, Dws, Aws, Bws, Lws, Kws, (int)(B * H), (int)H,
                                 (int)(H / Hkv), win, doc_start, block_mask, (int)N,
-                                causal ? 1 : 0, scale, passes, (hipStream_t)stream));
+                                causal ? 1 : 0, scale, passes, nsl,
+                                nsl > 1 ? (float*)((char*)ws + poff) : nullptr,
+                                (hipStream_t)stream));
 }
 
 attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -347,11 +395,12 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
       fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, 1, nw, nullptr, nullptr, n, c, scale, hs);
   if (e == hipSuccess && ngrad == 3)
     e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, w0, w0 + bhn, w0 + 2 * bhn, bh,
-                        h, 1, nw, nullptr, nullptr, n, c, scale, gproj ? 1 : 0, 3, hs);
+                        h, 1, nw, nullptr, nullptr, n, c, scale, gproj ? 1 : 0, 3, 1, nullptr,
+                        hs);
   if (e == hipSuccess)
     e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, w0,
                         w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, h, 1, nw, nullptr,
-                        nullptr, n, c, scale, 3, hs);
+                        nullptr, n, c, scale, 3, 1, nullptr, hs);
   return finish(e);
 }
 

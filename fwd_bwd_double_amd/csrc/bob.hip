@@ -12,12 +12,13 @@ hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
                       int win, const int* ds, const uint8_t* bm, int N, int causal, float scale,
-                      int passes, hipStream_t st) {
+                      int passes, int nsl, float* Part, hipStream_t st) {
   if (dt != 0)
     return launch_bob_f32(Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws,
-                          Lws, Kws, BH, H, grp, win, ds, bm, N, causal, scale, passes, st);
+                          Lws, Kws, BH, H, grp, win, ds, bm, N, causal, scale, passes, nsl,
+                          Part, st);
 #define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, Lws, Kws, \
-                     BH, H, grp, win, ds, bm, N, scale, passes, st
+                     BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st
   if (!causal) return launch_bob_t<bf16, false, false>(FBD_BOB_ARGS);
   return ds ? launch_bob_t<bf16, true, true>(FBD_BOB_ARGS)
             : launch_bob_t<bf16, true, false>(FBD_BOB_ARGS);

@@ -245,7 +245,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     const T* __restrict__ Bk, const T* __restrict__ C, const float* __restrict__ Dws,
     const float* __restrict__ Aws, const float* __restrict__ Kws, T* __restrict__ gK,
     T* __restrict__ gV, int N, int BH, int H, int grp, int win, const int* __restrict__ DS,
-    const uint8_t* __restrict__ BMK, float scale) {
+    const uint8_t* __restrict__ BMK, float scale, int nsl, float* __restrict__ Part) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q, dO, g_dQ tiles and the -LSE*log2(e), D, alpha, -kappa of the tile's rows
@@ -257,11 +257,15 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
 
-  // workgroup = (key block, key/value head); the query heads sharing that
-  // key head stream past in turn, accumulating into the same gK, gV
-  const Work wk = col_work(BH / grp);
-  const size_t hoff = (size_t)wk.head * N * HD;   // key-side tensors
-  const int qh0 = first_q_head(wk.head, H, grp);
+  // workgroup = (key block, key/value head, slice of its query heads); the
+  // slice's query heads stream past in turn, accumulating into the same gK,
+  // gV (one slice: the whole group, written as the result; several: fp32
+  // partial sums, added up afterwards)
+  const Work wk = col_work(BH / grp * nsl);
+  const int kvh = wk.head / nsl, sl = wk.head - kvh * nsl;
+  const int hps = grp / nsl;                      // query heads per slice
+  const size_t hoff = (size_t)kvh * N * HD;       // key-side tensors
+  const int qh0 = first_q_head(kvh, H, grp) + sl * hps;
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k0 = wk.blk * BLK;
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   int iend = CAUSAL ? min(N, kmax + win) : N;
   if (CAUSAL && DOCS) iend = min(iend, first_above(ds, min(N, k0 + BLK), N, kmax, lane));
   const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
-  const int nsteps = ntiles * grp;      // (query head, query tile) steps
+  const int nsteps = ntiles * hps;      // (query head, query tile) steps
   // block-sparse mask (a compile-time variant): the workgroup's column of
   // 128 x 128 blocks; every step index is visited, and a step whose query
   // tile lies in a dropped block is neither loaded nor computed
@@ -430,18 +434,26 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
     if (u + 1 < nsteps) tile(u + 1, B1, B0);
   }
   float out[16];
+  T* const ok = gK + hoff;
+  T* const ov = gV + hoff;
+  float* const pk = nsl > 1 ? Part + ((size_t)sl * (BH / grp) + kvh) * N * HD : nullptr;
+  float* const pv = nsl > 1 ? pk + (size_t)nsl * (BH / grp) * N * HD : nullptr;
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = scale * gk0[v];
-  st_cols(gK + hoff, N, kw, 0, lane, out);
+  if (nsl == 1) st_cols(ok, N, kw, 0, lane, out);
+  else st_cols(pk, N, kw, 0, lane, out);
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = scale * gk1[v];
-  st_cols(gK + hoff, N, kw, 32, lane, out);
+  if (nsl == 1) st_cols(ok, N, kw, 32, lane, out);
+  else st_cols(pk, N, kw, 32, lane, out);
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = gv0[v];
-  st_cols(gV + hoff, N, kw, 0, lane, out);
+  if (nsl == 1) st_cols(ov, N, kw, 0, lane, out);
+  else st_cols(pv, N, kw, 0, lane, out);
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = gv1[v];
-  st_cols(gV + hoff, N, kw, 32, lane, out);
+  if (nsl == 1) st_cols(ov, N, kw, 32, lane, out);
+  else st_cols(pv, N, kw, 32, lane, out);
 }
 
 template <class T, bool CAUSAL, bool DOCS>
@@ -450,9 +462,7 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
                                float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
                                int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
-                               float scale,
-                               int passes,
-                               hipStream_t st) {
+                               float scale, int passes, int nsl, float* Part, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
@@ -475,14 +485,17 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
   if (!(passes & 2)) return hipSuccess;
   auto col = [&](auto bmask) {
     hipLaunchKernelGGL((bob_col_kernel<T, BM, CAUSAL, DOCS, decltype(bmask)::value>),
-                       dim3(nblk * (BH / grp)), dim3(NT), 0, st, (const T*)Q, (const T*)K,
-                       (const T*)V, (const float*)Lws, (const T*)dO, (const T*)gdQ,
-                       (const T*)gdK, (const T*)gdV, (const float*)Dws, (const float*)Aws,
-                       (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, win, ds, bm, scale);
+                       dim3(nblk * (BH / grp) * nsl), dim3(NT), 0, st, (const T*)Q,
+                       (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO,
+                       (const T*)gdQ, (const T*)gdK, (const T*)gdV, (const float*)Dws,
+                       (const float*)Aws, (const float*)Kws, (T*)gK, (T*)gV, N, BH, H, grp, win,
+                       ds, bm, scale, nsl, Part);
   };
   if (bm) col(std::true_type{});
   else col(std::false_type{});
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsl == 1) return e;
+  return launch_sum_slices(sizeof(T) == 2 ? 0 : 1, Part, nsl, BH / grp, N, gK, gV, st);
 }
 
 }  // namespace fbd

@@ -180,7 +180,8 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ Lws, const T* __restrict__ dO, const float* __restrict__ Dws,
     const float* __restrict__ Rws, T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int H,
-    int grp, int win, const int* __restrict__ DS, const uint8_t* __restrict__ BMK, float scale) {
+    int grp, int win, const int* __restrict__ DS, const uint8_t* __restrict__ BMK, float scale,
+    int nsl, float* __restrict__ Part) {
   static_assert(BM % 64 == 0, "row statistics move in 64-row DMA instructions");
   // two buffers as separate objects (loop unrolled by two); each holds the
   // Q and dO tiles and the -LSE*log2(e), D (, r) of the tile's rows
@@ -193,12 +194,15 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
 
-  // workgroup = (key block, key/value head); the query heads sharing that
-  // key head stream past in turn and their contributions accumulate into the
-  // same dK, dV registers
-  const Work wk = col_work(BH / grp);
-  const size_t hoff = (size_t)wk.head * N * HD;   // key-side tensors
-  const int qh0 = first_q_head(wk.head, H, grp);
+  // workgroup = (key block, key/value head, slice of its query heads); the
+  // slice's query heads stream past in turn and their contributions
+  // accumulate into the same dK, dV registers (one slice: the whole group,
+  // written as the result; several: fp32 partial sums, added up afterwards)
+  const Work wk = col_work(BH / grp * nsl);
+  const int kvh = wk.head / nsl, sl = wk.head - kvh * nsl;
+  const int hps = grp / nsl;                      // query heads per slice
+  const size_t hoff = (size_t)kvh * N * HD;       // key-side tensors
+  const int qh0 = first_q_head(kvh, H, grp) + sl * hps;
   const uint32_t hbytes = (uint32_t)N * HD * sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k0 = wk.blk * BLK;
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
   int iend = CAUSAL ? min(N, kmax + win) : N;
   if (CAUSAL && DOCS) iend = min(iend, first_above(ds, min(N, k0 + BLK), N, kmax, lane));
   const int ntiles = iend > istart ? (iend - istart + BM - 1) / BM : 0;
-  const int nsteps = ntiles * grp;      // (query head, query tile) steps
+  const int nsteps = ntiles * hps;      // (query head, query tile) steps
   // block-sparse mask (a compile-time variant): the workgroup's column of
   // 128 x 128 blocks; every step index is visited, and a step whose query
   // tile lies in a dropped block is neither loaded nor computed
@@ -338,18 +342,72 @@ __global__ __launch_bounds__(NT, FBD_BWD_COL_OCC) void bwd_col_kernel(
     if (u + 1 < nsteps) tile(u + 1, B1, B0);
   }
   float out[16];
+  if (nsl == 1) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = scale * dk0[v];
-  st_cols(dK + hoff, N, kw, 0, lane, out);
+    for (int v = 0; v < 16; ++v) out[v] = scale * dk0[v];
+    st_cols(dK + hoff, N, kw, 0, lane, out);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = scale * dk1[v];
-  st_cols(dK + hoff, N, kw, 32, lane, out);
+    for (int v = 0; v < 16; ++v) out[v] = scale * dk1[v];
+    st_cols(dK + hoff, N, kw, 32, lane, out);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = dv0[v];
-  st_cols(dV + hoff, N, kw, 0, lane, out);
+    for (int v = 0; v < 16; ++v) out[v] = dv0[v];
+    st_cols(dV + hoff, N, kw, 0, lane, out);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = dv1[v];
-  st_cols(dV + hoff, N, kw, 32, lane, out);
+    for (int v = 0; v < 16; ++v) out[v] = dv1[v];
+    st_cols(dV + hoff, N, kw, 32, lane, out);
+  } else {
+    float* pk = Part + ((size_t)sl * (BH / grp) + kvh) * N * HD;
+    float* pv = pk + (size_t)nsl * (BH / grp) * N * HD;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = scale * dk0[v];
+    st_cols(pk, N, kw, 0, lane, out);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = scale * dk1[v];
+    st_cols(pk, N, kw, 32, lane, out);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = dv0[v];
+    st_cols(pv, N, kw, 0, lane, out);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[v] = dv1[v];
+    st_cols(pv, N, kw, 32, lane, out);
+  }
+}
+
+// Sum of the nsl fp32 partial key-side gradients of the split column passes:
+// Part holds nsl (B*Hkv, N, 64) blocks for K, then nsl for V; n4 = B*Hkv*N*16
+// groups of four values.  One thread per group, slices added in order.
+template <class T>
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ Part, int nsl,
+                                                         size_t n4, T* __restrict__ gK,
+                                                         T* __restrict__ gV) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* p = reinterpret_cast<const f32x4*>(Part);
+  f32x4 a = p[i], b = p[(size_t)nsl * n4 + i];
+  for (int s = 1; s < nsl; ++s) {
+    a += p[(size_t)s * n4 + i];
+    b += p[(size_t)(nsl + s) * n4 + i];
+  }
+  if constexpr (sizeof(T) == 2) {
+    reinterpret_cast<bf16x4*>(gK)[i] = bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    reinterpret_cast<bf16x4*>(gV)[i] = bf16x4{(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+  } else {
+    reinterpret_cast<f32x4*>(gK)[i] = a;
+    reinterpret_cast<f32x4*>(gV)[i] = b;
+  }
+}
+
+hipError_t launch_sum_slices(int dt, const float* Part, int nsl, int BHkv, int N, void* gK,
+                             void* gV, hipStream_t st) {
+  const size_t n4 = (size_t)BHkv * N * (HD / 4);
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  if (dt == 0)
+    hipLaunchKernelGGL(sum_slices_kernel<bf16>, grid, dim3(256), 0, st, Part, nsl, n4, (bf16*)gK,
+                       (bf16*)gV);
+  else
+    hipLaunchKernelGGL(sum_slices_kernel<float>, grid, dim3(256), 0, st, Part, nsl, n4,
+                       (float*)gK, (float*)gV);
+  return hipGetLastError();
 }
 
 template <class T, bool GPROJ, bool CAUSAL, bool DOCS>
@@ -357,7 +415,7 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
                                const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
                                float* Dws, float* Rws, float* Lws, int BH, int H, int grp,
                                int win, const int* ds, const uint8_t* bm, int N, float scale, int passes,
-                               hipStream_t st) {
+                               int nsl, float* Part, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
@@ -370,9 +428,10 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
   };
   auto col = [&](auto bmask) {
     hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL, DOCS, decltype(bmask)::value>),
-                       dim3(nblk * (BH / grp)), dim3(NT), 0, st, (const T*)Q, (const T*)K,
-                       (const T*)V, (const float*)Lws, (const T*)dO, (const float*)Dws,
-                       (const float*)Rws, (T*)dK, (T*)dV, N, BH, H, grp, win, ds, bm, scale);
+                       dim3(nblk * (BH / grp) * nsl), dim3(NT), 0, st, (const T*)Q,
+                       (const T*)K, (const T*)V, (const float*)Lws, (const T*)dO,
+                       (const float*)Dws, (const float*)Rws, (T*)dK, (T*)dV, N, BH, H, grp, win,
+                       ds, bm, scale, nsl, Part);
   };
   if (passes & 1) {
     if (bm) row(std::true_type{});
@@ -383,7 +442,9 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
   if (!(passes & 2)) return hipSuccess;
   if (bm) col(std::true_type{});
   else col(std::false_type{});
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsl == 1) return e;
+  return launch_sum_slices(sizeof(T) == 2 ? 0 : 1, Part, nsl, BH / grp, N, dK, dV, st);
 }
 
 template <class T, bool GPROJ>
@@ -391,27 +452,27 @@ static hipError_t launch_bwd_c(int causal, const void* Q, const void* K, const v
                                const void* O, const float* LSE, const void* dO, void* dQ,
                                void* dK, void* dV, float* Dws, float* Rws, float* Lws, int BH,
                                int H, int grp, int win, const int* ds, const uint8_t* bm, int N, float scale,
-                               int passes,
-                               hipStream_t st) {
+                               int passes, int nsl, float* Part, hipStream_t st) {
   if (causal)
-    return ds ? launch_bwd_t<T, GPROJ, true, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st)
-              : launch_bwd_t<T, GPROJ, true, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
-  return launch_bwd_t<T, GPROJ, false, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
+    return ds ? launch_bwd_t<T, GPROJ, true, true>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st)
+              : launch_bwd_t<T, GPROJ, true, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st);
+  return launch_bwd_t<T, GPROJ, false, false>(Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st);
 }
 
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
                       float* Rws, float* Lws, int BH, int H, int grp, int win, const int* ds,
                       const uint8_t* bm, int N,
-                      int causal, float scale, int gproj, int passes, hipStream_t st) {
+                      int causal, float scale, int gproj, int passes, int nsl, float* Part,
+                      hipStream_t st) {
   if (dt == 0) {
     if (gproj)
-      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
-    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
+      return launch_bwd_c<bf16, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st);
+    return launch_bwd_c<bf16, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st);
   }
   if (gproj)
-    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
-  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, st);
+    return launch_bwd_c<float, true>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st);
+  return launch_bwd_c<float, false>(causal, Q, K, V, O, LSE, dO, dQ, dK, dV, Dws, Rws, Lws, BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st);
 }
 
 }  // namespace fbd

@@ -75,13 +75,21 @@ hipError_t launch_fwd(int dt, const void* Q, const void* K, const void* V, void*
                       int BH, int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
                       int causal, float scale, hipStream_t st);
 
+// Column-pass slices (backward and BoB): nsl divides grp.  With nsl == 1 a
+// column-pass workgroup owns a (key block, key head) pair and writes its
+// key-side results once; with nsl > 1 it owns a (key block, key head, slice of
+// grp / nsl query heads) triple and writes fp32 partial sums into Part
+// (2 * nsl * (BH / grp) * N * 64 floats: the nsl key-gradient blocks, then the
+// nsl value-gradient blocks), which a second kernel adds up, in slice order,
+// into the outputs.  Part is unused (may be null) when nsl == 1.
+//
 // Backward workspace: D, r, and -LSE*log2(e) per row (written by the row pass,
 // read by the column pass).
 hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, void* dQ, void* dK, void* dV, float* Dws,
                       float* Rws, float* Lws, int BH, int H, int grp, int win, const int* ds,
                       const uint8_t* bm, int N, int causal, float scale, int gproj, int passes,
-                      hipStream_t st);
+                      int nsl, float* Part, hipStream_t st);
 
 // BoB workspace: D, alpha, beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) per row.
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
@@ -89,7 +97,7 @@ hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
                       int win, const int* ds, const uint8_t* bm, int N, int causal, float scale,
-                      int passes, hipStream_t st);
+                      int passes, int nsl, float* Part, hipStream_t st);
 
 // The fp32 half of launch_bob (same arguments, dt implied).
 hipError_t launch_bob_f32(const void* Q, const void* K, const void* V, const void* O,
@@ -97,7 +105,12 @@ hipError_t launch_bob_f32(const void* Q, const void* K, const void* V, const voi
                           const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                           float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
                           int win, const int* ds, const uint8_t* bm, int N, int causal,
-                          float scale, int passes, hipStream_t st);
+                          float scale, int passes, int nsl, float* Part, hipStream_t st);
+
+// Adds the nsl slices of Part (layout above, BHkv = BH / grp key heads) into
+// gK and gV of type dt.
+hipError_t launch_sum_slices(int dt, const float* Part, int nsl, int BHkv, int N, void* gK,
+                             void* gV, hipStream_t st);
 
 // FP8 forward.  Quantisation pre-pass: E4M3 codes of Q and K (optionally
 // rotated by diag(signs) H / 8 when rotate != 0) with one power-of-two scale

@@ -187,6 +187,18 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
  * each key-side block is still written once.  Hkv == H is multi-head
  * attention; Hkv == 1 is multi-query attention.
  *
+ * Split column passes (grouped-query heads only): when a group's column
+ * workgroups alone would be too few to fill the chip (under 1536 of them),
+ * each group's query heads are divided into slices that separate workgroups
+ * stream; each slice writes fp32 partial sums of its key-side results into
+ * the workspace, and one more kernel adds the slices up, in a fixed order,
+ * into dK, dV (g_K, g_V).  This happens only when ws_bytes is at least
+ * attn_bwd_ex_workspace_bytes (attn_bob_ex_workspace_bytes); a workspace of
+ * attn_bwd_workspace_bytes (attn_bob_workspace_bytes) runs the unsplit
+ * column pass, whose results differ only in the fp32 summation order over a
+ * group.  The partial sums sit after the row states at the next 256-byte
+ * boundary; the row-state layout is unchanged.
+ *
  * Sliding window (window > 0, causal only): key j is visible to query i iff
  * i - window < j <= i.  Tiles wholly outside the window are never loaded.
  * window == 0 is plain causal (or full, with causal == 0) attention.
@@ -219,6 +231,13 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
  * count the H query heads).  The backward and BoB must get the same causal,
  * window, doc_start and block_mask as the forward.
  */
+/* Workspace bytes that let attn_bwd_ex / attn_bob_ex split their column
+ * passes (see above): the multi-head size when no split applies (Hkv == H, or
+ * enough key blocks), else that size rounded up to 256 bytes plus
+ * 2 * nslices * B * Hkv * N * 64 floats.  0 for invalid sizes. */
+size_t attn_bwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N);
+size_t attn_bob_ex_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N);
+
 attn_status attn_fwd_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                         const void* Q, const void* K, const void* V,
                         int causal, int64_t window, const int32_t* doc_start,

@@ -41,6 +41,32 @@ def test_workspace_sizes(lib):
     assert fbd.bwd_workspace_bytes(0, 3, 5) == 0
 
 
+def test_split_column_pass_workspace_sizes(lib):
+    # grouped-query heads: the column passes split a group into the fewest
+    # slices (a divisor of H / Hkv) that give 1536 workgroups of 128 keys, or
+    # into single heads when none does; the partial sums (two fp32 key-side
+    # tensors per slice) follow the row states at a 256-byte boundary
+    def split(base, B, Hkv, N, nsl):
+        return (base + 255) // 256 * 256 + 2 * nsl * B * Hkv * N * 64 * 4
+    for B, H, N in ((1, 12, 16384), (2, 4, 300)):   # multi-head: never split
+        assert fbd.bwd_ex_workspace_bytes(B, H, H, N) == fbd.bwd_workspace_bytes(B, H, N)
+        assert fbd.bob_ex_workspace_bytes(B, H, H, N) == fbd.bob_workspace_bytes(B, H, N)
+    # 128 key blocks x 4 key heads = 512 workgroups: three slices of one head
+    assert fbd.bwd_ex_workspace_bytes(1, 12, 4, 16384) == split(3 * 12 * 16384 * 4, 1, 4, 16384, 3)
+    assert fbd.bob_ex_workspace_bytes(1, 12, 4, 16384) == split(5 * 12 * 16384 * 4, 1, 4, 16384, 3)
+    # 2048 workgroups already: no split
+    assert fbd.bwd_ex_workspace_bytes(4, 12, 4, 16384) == fbd.bwd_workspace_bytes(4, 12, 16384)
+    # 400 key blocks x 2 key heads = 800: two slices of two heads reach 1600
+    assert fbd.bwd_ex_workspace_bytes(1, 8, 2, 51200) == split(3 * 8 * 51200 * 4, 1, 2, 51200, 2)
+    # 32 x 2 = 64: even single heads stay below 1536, so four slices
+    assert fbd.bob_ex_workspace_bytes(1, 8, 2, 4096) == split(5 * 8 * 4096 * 4, 1, 2, 4096, 4)
+    # a row-state size that is not a multiple of 256 bytes is rounded up
+    assert fbd.bwd_ex_workspace_bytes(1, 3, 1, 5) == split(3 * 3 * 5 * 4, 1, 1, 5, 3)
+    for bad in ((1, 12, 5, 64), (1, 12, 0, 64), (1, 4, 8, 64), (0, 4, 2, 64)):
+        assert fbd.bwd_ex_workspace_bytes(*bad) == 0
+        assert fbd.bob_ex_workspace_bytes(*bad) == 0
+
+
 def test_status_strings(lib):
     for s in range(6):
         assert lib.attn_status_str(s)

@@ -356,11 +356,20 @@ def test_grouped_query(H, Hkv, N, causal, dtype):
     ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
                          causal=causal, with_bwd=True)
     f64 = synthetic.to_f64
-    for gproj in (False, True):
+    B = 2
+    ws_bwd = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device="cuda")
+    ws_bob = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device="cuda")
+    # split: the binding's default workspace (grouped-query size: at these
+    # sizes every query head gets its own column workgroups and the slices'
+    # fp32 partial sums are added afterwards); unsplit: the multi-head size
+    for gproj, split in ((False, True), (True, True), (True, False)):
+        say(f"[gpu]   gproj={gproj} split={split}")
+        wb, wq = (None, None) if split else (ws_bwd, ws_bob)
         dq, dk, dv = fbd.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal,
-                                  scale=w.scale, gproj=gproj)
+                                  scale=w.scale, gproj=gproj, workspace=wb)
         gq, gk, gv, gdo = fbd.attn_bob(g["q"], g["k"], g["v"], o, lse, g["do"], g["g_dq"],
-                                       g["g_dk"], g["g_dv"], causal=causal, scale=w.scale)
+                                       g["g_dk"], g["g_dv"], causal=causal, scale=w.scale,
+                                       workspace=wq)
         torch.cuda.synchronize()
         assert dk.shape == g["k"].shape and gk.shape == g["k"].shape
         check("O", f64(o), ref["O"], t1)
@@ -369,6 +378,40 @@ def test_grouped_query(H, Hkv, N, causal, dtype):
             check(k, f64(t), ref[k], t1)
         for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
             check(k, f64(t), ref[k], t2)
+
+
+def test_grouped_query_two_head_slices():
+    # 400 key blocks x 2 key heads: the column passes split each group of four
+    # query heads into two slices of two heads (the slice-offset arithmetic
+    # the smaller cases, with one head per slice, do not reach).  Too large
+    # for the dense oracle; the unsplit column passes, checked against the
+    # oracle above, are the reference here: only the fp32 summation order over
+    # a group differs, so the bf16 results agree to rounding.
+    import fwd_bwd_double_amd as fbd
+    B, H, Hkv, N = 1, 8, 2, 51200
+    assert fbd.bwd_ex_workspace_bytes(B, H, Hkv, N) > fbd.bwd_workspace_bytes(B, H, N)
+    w = synthetic.Workload("gqa-slices", B, H, N, 64, "bf16", 8700, causal=True)
+    gen = torch.Generator(device="cuda").manual_seed(8700)
+    r = lambda h, sd: (sd * torch.randn(B, h, N, 64, device="cuda", generator=gen)).bfloat16()
+    q, do, gdq = r(H, .5), r(H, .5), r(H, 1.)
+    k, v, gdk, gdv = r(Hkv, .5), r(Hkv, .5), r(Hkv, 1.), r(Hkv, 1.)
+    say(f"[gpu] gqa two-head slices B={B} H={H} Hkv={Hkv} N={N}")
+    o, lse = fbd.attn_fwd(q, k, v, causal=True, scale=w.scale)
+    ws_bwd = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device="cuda")
+    ws_bob = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device="cuda")
+    res = {}
+    for split in (True, False):
+        wb, wq = (None, None) if split else (ws_bwd, ws_bob)
+        _, dk, dv = fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=w.scale, gproj=True,
+                                 workspace=wb)
+        _, gk, gv, _ = fbd.attn_bob(q, k, v, o, lse, do, gdq, gdk, gdv, causal=True,
+                                    scale=w.scale, workspace=wq)
+        res[split] = [t.double().cpu().numpy() for t in (dk, dv, gk, gv)]
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dK", "dV", "gK", "gV"), res[True], res[False]):
+        e = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        say(f"[gpu]   {name}: split vs unsplit rel-L2 {e:.2e}")
+        assert e <= 2e-3, (name, e)
 
 
 # ------------------------------------------------- causal sliding window
