@@ -46,6 +46,15 @@ METRIC = "attn fwd/bwd/BoB TFLOP/s & % bf16 MFMA peak, GPT-2S head shape, N≤26
 UNITS = {"fwd": 2, "bwd_row": 4, "bwd_col": 5, "bob_row": 11, "bob_col": 8}
 # FLOP convention per unmasked pair, in units of d
 CONV = {"fwd": 4, "bwd": 10, "bob": 38}
+# Algorithmic HBM bytes per launch as (tensors, row arrays): (B, H, N, d)
+# tensors read or written once, and (B, H, N) fp32 arrays.  fwd: Q, K, V, O
+# and LSE.  bwd_row: Q, K, V, O, dO, dQ; LSE in, D, r, -LSE log2(e) out.
+# bwd_col: Q, K, V, dO, dK, dV; -LSE log2(e), D, r.  bob_row: Q, K, V, O, dO
+# and the three cotangents in, g_Q and g_dO out; LSE in, D, alpha, beta,
+# -LSE log2(e), -kappa out.  bob_col: Q, K, V, dO, g_dQ, g_dK, g_dV in, g_K,
+# g_V out; -LSE log2(e), D, alpha, -kappa.
+ALG_BYTES = {"fwd": (4, 1), "bwd_row": (6, 4), "bwd_col": (6, 3), "bob_row": (10, 6),
+             "bob_col": (9, 4)}
 
 
 def parse():
@@ -62,6 +71,11 @@ def parse():
     p.add_argument("--fp8", action="store_true",
                    help="time the FP8 forward (rotated quantisation pre-pass + E4M3 forward) on "
                         "the step's workload instead of the step (one JSON line)")
+    p.add_argument("--workload", default="bob-B4H12N4096",
+                   choices=["bob-B4H12N4096", "gpt2s-layer-B8H12N1024"],
+                   help="workload the step runs on: the BoB workload (the reported line) or "
+                        "the GPT-2-Small layer shape, where each kernel is short and the "
+                        "memory traffic matters (for counter runs)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a plain copy "
                         "kernel of known size, to calibrate memory counters)")
@@ -86,7 +100,7 @@ def main():
     import fwd_bwd_double_amd as fbd
     import synthetic
 
-    w = synthetic.WORKLOADS[4]
+    w = {x.name: x for x in synthetic.WORKLOADS.values()}[args.workload]
     B, H, N, d = w.B, w.H, w.N, w.d
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -151,8 +165,15 @@ def main():
     per_kernel = {n: {"ms": kern_ms[n],
                       "executed_tflops": UNITS[n] * unit / (kern_ms[n] * 1e-3) / 1e12}
                   for n in names}
+    # algorithmic bytes: one touch of every input and output, in units of one
+    # (B, H, N, d) tensor (t) and one (B, H, N) fp32 row-statistic array (r)
+    t_b, r_b = B * H * N * d * x["q"].element_size(), B * H * N * 4
+    alg_bytes = {n: a * t_b + b * r_b for n, (a, b) in ALG_BYTES.items()}
     for n in names:
         per_kernel[n]["frac_mfma_peak"] = per_kernel[n]["executed_tflops"] / PEAK_BF16_TFLOPS
+        per_kernel[n]["alg_bytes"] = alg_bytes[n]
+        per_kernel[n]["alg_gbs"] = alg_bytes[n] / (kern_ms[n] * 1e-3) / 1e9
+        per_kernel[n]["frac_hbm_peak"] = per_kernel[n]["alg_gbs"] / HBM_PEAK_GBS
     op_ms = {"fwd": kern_ms["fwd"], "bwd": kern_ms["bwd_row"] + kern_ms["bwd_col"],
              "bob": kern_ms["bob_row"] + kern_ms["bob_col"]}
     per_op = {op: {"ms": op_ms[op],
@@ -169,7 +190,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, w, args.cpu_heads)
+        cpu = cpu_baseline(x, w, min(args.cpu_heads, B * H))
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
@@ -201,7 +222,7 @@ def fp8_bench(args):
     import fwd_bwd_double_amd as fbd
     import synthetic
 
-    w = synthetic.WORKLOADS[4]
+    w = {x.name: x for x in synthetic.WORKLOADS.values()}[args.workload]
     B, H, N, d = w.B, w.H, w.N, w.d
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
