@@ -84,6 +84,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_hvp.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32,
                              vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_hvp.restype = i32
+    lib.attn_hvp_ex_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_hvp_ex_workspace_bytes.restype = sz
+    lib.attn_hvp_ex.argtypes = ([i32, i64, i64, i64, i64, i64] + [vp] * 7 + [i32, i64, vp, vp, f32, i32]
+                                + [vp] * 10 + [sz, vp])
+    lib.attn_hvp_ex.restype = i32
     # FP8 forward
     u64 = ctypes.c_uint64
     lib.attn_fp8_workspace_bytes.argtypes = [i64, i64, i64, i64]
@@ -324,32 +329,43 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
 
 
 def attn_hvp(q, k, v, do, v_q, v_k, v_v, causal: bool = True, scale: Optional[float] = None,
-             gproj: bool = False, grad: bool = True, workspace: Optional[torch.Tensor] = None):
+             gproj: bool = False, grad: bool = True, workspace: Optional[torch.Tensor] = None,
+             window: int = 0, doc_start: Optional[torch.Tensor] = None,
+             block_mask: Optional[torch.Tensor] = None):
     """Hessian-vector product of Phi(q, k, v) = <do, O(q, k, v)> (do fixed) with
     v = (v_q, v_k, v_v), in one library call (forward, optional backward, BoB).
     Returns a dict with O, LSE, Hv_q, Hv_k, Hv_v, Hv_do (the derivative of
-    <v, grad Phi> with respect to do) and, when `grad`, dQ, dK, dV."""
+    <v, grad Phi> with respect to do) and, when `grad`, dQ, dK, dV.  k, v, v_k
+    and v_v may have fewer heads than q (grouped-query); window, doc_start and
+    block_mask as in attn_fwd."""
     lib = load()
-    for n, t in (("k", k), ("v", v), ("do", do), ("v_q", v_q), ("v_k", v_k), ("v_v", v_v)):
-        _check(n, t, q)
     _check("q", q, q)
+    Hkv = _kv_heads(q, k)
+    kvs = _kv_shape(q, Hkv)
+    for n, t in (("do", do), ("v_q", v_q)):
+        _check(n, t, q)
+    for n, t in (("k", k), ("v", v), ("v_k", v_k), ("v_v", v_v)):
+        _check(n, t, q, shape=kvs)
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
-    hq, hk, hv, hdo = (torch.empty_like(q) for _ in range(4))
+    hq, hdo = torch.empty_like(q), torch.empty_like(q)
+    hk, hv = torch.empty_like(k), torch.empty_like(k)
     dq = dk = dv = None
     if grad:
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    need = lib.attn_hvp_workspace_bytes(B, H, N)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    need = lib.attn_hvp_ex_workspace_bytes(B, H, Hkv, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
     ptr = (lambda t: None if t is None else t.data_ptr())
-    st = lib.attn_hvp(_dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                      v_q.data_ptr(), v_k.data_ptr(), v_v.data_ptr(), 1 if causal else 0,
-                      _scale(q, scale), 1 if gproj else 0, o.data_ptr(), lse.data_ptr(), ptr(dq),
+    st = lib.attn_hvp_ex(_dt(q), B, H, Hkv, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                      do.data_ptr(), v_q.data_ptr(), v_k.data_ptr(), v_v.data_ptr(),
+                      1 if causal else 0, int(window), _docs(q, doc_start),
+                      _bmask(q, block_mask), _scale(q, scale), 1 if gproj else 0,
+                      o.data_ptr(), lse.data_ptr(), ptr(dq),
                       ptr(dk), ptr(dv), hq.data_ptr(), hk.data_ptr(), hv.data_ptr(),
                       hdo.data_ptr(), workspace.data_ptr(), ws_bytes, _stream(q.device))
     _raise("attn_hvp", st)

@@ -361,8 +361,65 @@ attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
 }
 
 size_t attn_hvp_workspace_bytes(int64_t B, int64_t H, int64_t N) {
-  // the BoB row states; the backward's three arrays fit in the same space
   return attn_bob_workspace_bytes(B, H, N);
+}
+
+size_t attn_hvp_ex_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
+  return attn_bob_ex_workspace_bytes(B, H, Hkv, N);
+}
+
+attn_status attn_hvp_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V, const void* dO,
+                        const void* v_Q, const void* v_K, const void* v_V, int causal,
+                        int64_t window, const int32_t* doc_start, const uint8_t* block_mask,
+                        float scale, int gproj, void* O, float* LSE, void* dQ, void* dK,
+                        void* dV, void* Hv_Q, void* Hv_K, void* Hv_V, void* Hv_dO, void* ws,
+                        size_t ws_bytes, void* stream) {
+  attn_status st = check_shape(dt, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, Hkv)) != ATTN_OK) return st;
+  int win = 0;
+  if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
+  const int ngrad = (dQ != nullptr) + (dK != nullptr) + (dV != nullptr);
+  if (ngrad != 0 && ngrad != 3) return ATTN_EINVAL;
+  // the backward's row states (D, r, -LSE log2(e)) and then BoB's (D, alpha,
+  // beta, -LSE log2(e), -kappa) share the front of the workspace; the split
+  // column passes' partial sums, when the workspace holds them, follow BoB's
+  size_t need = attn_bob_workspace_bytes(B, H, N);
+  if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
+  int nsl = col_slices(B, H, Hkv, N);
+  const size_t poff = round256(need);
+  if (nsl > 1 && ws_bytes >= poff + part_bytes(B, Hkv, N, nsl)) need = poff + part_bytes(B, Hkv, N, nsl);
+  else nsl = 1;
+  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
+  const size_t tk = (size_t)B * Hkv * N * d * elem_size(dt);
+  std::vector<Arg> outs = {{O, t}, {LSE, s}, {Hv_Q, t}, {Hv_K, tk}, {Hv_V, tk}, {Hv_dO, t},
+                           {ws, need}};
+  if (ngrad == 3) {
+    outs.push_back({dQ, t});
+    outs.push_back({dK, tk});
+    outs.push_back({dV, tk});
+  }
+  st = check_ptrs({{Q, t}, {K, tk}, {V, tk}, {dO, t}, {v_Q, t}, {v_K, tk}, {v_V, tk}}, outs);
+  if (st != ATTN_OK) return st;
+  if ((st = check_docs(doc_start, causal, B, N, outs)) != ATTN_OK) return st;
+  if ((st = check_block_mask(block_mask, B, N, outs)) != ATTN_OK) return st;
+  const int bh = (int)(B * H), n = (int)N, c = causal ? 1 : 0, h = (int)H, grp = (int)(H / Hkv);
+  const hipStream_t hs = (hipStream_t)stream;
+  const size_t bhn = (size_t)B * H * N;
+  float* w0 = static_cast<float*>(ws);
+  float* part = nsl > 1 ? (float*)((char*)ws + poff) : nullptr;
+  hipError_t e = fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, grp, win, doc_start,
+                                 block_mask, n, c, scale, hs);
+  if (e == hipSuccess && ngrad == 3)
+    e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, w0, w0 + bhn, w0 + 2 * bhn, bh,
+                        h, grp, win, doc_start, block_mask, n, c, scale, gproj ? 1 : 0, 3, nsl,
+                        part, hs);
+  if (e == hipSuccess)
+    e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, w0,
+                        w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, h, grp, win,
+                        doc_start, block_mask, n, c, scale, 3, nsl, part, hs);
+  return finish(e);
 }
 
 attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
@@ -370,43 +427,10 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
                      const void* v_K, const void* v_V, int causal, float scale, int gproj,
                      void* O, float* LSE, void* dQ, void* dK, void* dV, void* Hv_Q, void* Hv_K,
                      void* Hv_V, void* Hv_dO, void* ws, size_t ws_bytes, void* stream) {
-  attn_status st = check_shape(dt, B, H, N, d, scale);
-  if (st != ATTN_OK) return st;
-  const int ngrad = (dQ != nullptr) + (dK != nullptr) + (dV != nullptr);
-  if (ngrad != 0 && ngrad != 3) return ATTN_EINVAL;
-  const size_t need = attn_hvp_workspace_bytes(B, H, N);
-  if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
-  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
-  std::vector<Arg> outs = {{O, t}, {LSE, s}, {Hv_Q, t}, {Hv_K, t}, {Hv_V, t}, {Hv_dO, t},
-                           {ws, need}};
-  if (ngrad == 3) {
-    outs.push_back({dQ, t});
-    outs.push_back({dK, t});
-    outs.push_back({dV, t});
-  }
-  st = check_ptrs({{Q, t}, {K, t}, {V, t}, {dO, t}, {v_Q, t}, {v_K, t}, {v_V, t}}, outs);
-  if (st != ATTN_OK) return st;
-  const int bh = (int)(B * H), n = (int)N, c = causal ? 1 : 0;
-  const hipStream_t hs = (hipStream_t)stream;
-  const size_t bhn = (size_t)B * H * N;
-  float* w0 = static_cast<float*>(ws);
-  const int h = (int)H, nw = kNoWindow;
-  hipError_t e =
-      fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, 1, nw, nullptr, nullptr, n, c, scale, hs);
-  if (e == hipSuccess && ngrad == 3)
-    e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, w0, w0 + bhn, w0 + 2 * bhn, bh,
-                        h, 1, nw, nullptr, nullptr, n, c, scale, gproj ? 1 : 0, 3, 1, nullptr,
-                        hs);
-  if (e == hipSuccess)
-    e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, w0,
-                        w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, h, 1, nw, nullptr,
-                        nullptr, n, c, scale, 3, 1, nullptr, hs);
-  return finish(e);
+  return attn_hvp_ex(dt, B, H, H, N, d, Q, K, V, dO, v_Q, v_K, v_V, causal, 0, nullptr, nullptr,
+                     scale, gproj, O, LSE, dQ, dK, dV, Hv_Q, Hv_K, Hv_V, Hv_dO, ws, ws_bytes,
+                     stream);
 }
-
-// ---------------------------------------------------------------------------
-// FP8 forward: quantisation pre-pass and forward on the codes.
-// ---------------------------------------------------------------------------
 
 }  // extern "C"
 

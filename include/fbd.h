@@ -292,6 +292,27 @@ attn_status attn_hvp(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
                      void* Hv_Q, void* Hv_K, void* Hv_V, void* Hv_dO,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* The Hessian-vector product over the extended forms: Hkv key/value heads, a
+ * causal sliding window, document starts and a block-sparse mask, with the
+ * meanings, shapes and errors of attn_fwd_ex / attn_bwd_ex / attn_bob_ex.
+ * K, V, v_K, v_V, dK, dV, Hv_K and Hv_V are (B, Hkv, N, d).  The Hessian is
+ * that of Phi = <dO, O> as a function of the shared K and V, so Hv_K and
+ * Hv_V are sums over each group's query heads, as dK and dV are.  ws must
+ * hold attn_hvp_workspace_bytes(B, H, N); with
+ * attn_hvp_ex_workspace_bytes(B, H, Hkv, N) the grouped-query column passes
+ * split (as in attn_bwd_ex).  attn_hvp is the Hkv == H case with no masks
+ * beyond causal. */
+size_t attn_hvp_ex_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N);
+
+attn_status attn_hvp_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                        const void* Q, const void* K, const void* V, const void* dO,
+                        const void* v_Q, const void* v_K, const void* v_V,
+                        int causal, int64_t window, const int32_t* doc_start,
+                        const uint8_t* block_mask, float scale, int gproj,
+                        void* O, float* LSE, void* dQ, void* dK, void* dV,
+                        void* Hv_Q, void* Hv_K, void* Hv_V, void* Hv_dO,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * FP8 forward with optional incoherent processing.
  *

@@ -128,6 +128,26 @@ def test_hvp_rejects_bad_arguments_before_launch(lib):
     assert hvp_call(lib, grad=(FAKE * 11, FAKE * 12, FAKE)) == 1     # dV aliases Q
 
 
+def test_hvp_ex_rejects_bad_arguments_before_launch(lib):
+    # Q K V dO vQ vK vV, then O LSE dQ dK dV HvQ HvK HvV HvdO, then ws
+    p = [FAKE * (i + 1) for i in range(7)]
+    out = [FAKE * (20 + i) for i in range(9)]
+    def call(H=4, Hkv=2, causal=1, window=0, ds=None, bm=None, ws_bytes=None, d=64):
+        need = fbd.load().attn_hvp_ex_workspace_bytes(1, H, max(Hkv, 1), 8)
+        return lib.attn_hvp_ex(0, 1, H, Hkv, 8, d, *p, causal, window, ds, bm, 0.125, 0, *out,
+                               FAKE * 40, need if ws_bytes is None else ws_bytes, None)
+    assert lib.attn_hvp_ex_workspace_bytes(1, 4, 2, 8) == fbd.bob_ex_workspace_bytes(1, 4, 2, 8)
+    assert lib.attn_hvp_ex_workspace_bytes(2, 3, 3, 5) == fbd.hvp_workspace_bytes(2, 3, 5)
+    for H, Hkv in ((4, 3), (4, 0), (4, 8)):
+        assert call(H=H, Hkv=Hkv) == 1
+    assert call(d=32) == 2
+    assert call(window=-1) == 1
+    assert call(causal=0, window=4) == 2          # a window needs the causal mask
+    assert call(causal=0, ds=FAKE * 50) == 2      # so do document masks
+    assert call(ds=FAKE * 50 + 2) == 3            # doc_start must be 4-byte aligned
+    assert call(ws_bytes=fbd.hvp_workspace_bytes(1, 4, 8) - 4) == 4
+
+
 def test_extended_forms_reject_bad_heads_and_windows(lib):
     p = [FAKE * (i + 1) for i in range(3)]
     call = lambda H, Hkv, causal=1, window=0, ds=None, bm=None: lib.attn_fwd_ex(

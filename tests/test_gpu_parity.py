@@ -570,3 +570,46 @@ def test_block_sparse_masks(N, causal, density, keep_diag, window, mean_len, H, 
             check(k, f64(t), ref[k], t1)
         for k, t in (("gQ", gq), ("gK", gk), ("gV", gv), ("gdO", gdo)):
             check(k, f64(t), ref[k], t2)
+
+
+# ------------------------------------------- HVP over the extended forms
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("H,Hkv,N,window,mean_len,density", [
+    (4, 2, 300, 0, 0, 0.0),      # grouped-query (split column passes)
+    (4, 1, 333, 100, 0, 0.0),    # multi-query with a sliding window
+    (4, 2, 300, 0, 60, 0.0),     # packed documents
+    (2, 2, 1000, 0, 0, 0.5),     # block-sparse, multi-head
+])
+def test_hvp_extended_forms(H, Hkv, N, window, mean_len, density, dtype):
+    # H v of <dO, O(Q, K, V)> with shared keys and masks: BoB with the
+    # direction v as the cotangents, key-side parts summed over each group
+    import fwd_bwd_double_amd as fbd
+    w = synthetic.Workload(f"hvp-ex-{dtype}", 2, H, N, 64, dtype, 9900 + N + H + Hkv,
+                           causal=True, qkv_std=1.0)
+    x, g, a = inputs(w)
+    for n in ("k", "v", "g_dk", "g_dv"):
+        g[n] = g[n][:, :Hkv].contiguous()
+        a[n] = a[n][:, :Hkv]
+    docs = doc_starts(2, N, 55 + N, mean_len) if mean_len else None
+    bm = block_masks(2, N, 66 + N, density, True) if density else None
+    ds = torch.from_numpy(docs.astype(np.int32)).cuda() if docs is not None else None
+    bmt = torch.from_numpy(bm).cuda() if bm is not None else None
+    say(f"[gpu] attn_hvp ex B=2 H={H} Hkv={Hkv} N={N} window={window} mean_len={mean_len} "
+        f"density={density} dtype={dtype}")
+    r = fbd.attn_hvp(g["q"], g["k"], g["v"], g["do"], g["g_dq"], g["g_dk"], g["g_dv"],
+                     scale=w.scale, gproj=True, window=window, doc_start=ds, block_mask=bmt)
+    torch.cuda.synchronize()
+    assert r["Hv_k"].shape == g["k"].shape and r["dK"].shape == g["k"].shape
+    ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                         with_bwd=True, window=window, docs=docs, block_mask=bm)
+    t1, t2 = (1e-5, 1e-5) if dtype == "fp32" else (2e-2, 5e-2)
+    f64 = synthetic.to_f64
+    check("O", f64(r["O"]), ref["O"], t1)
+    if bm is None:
+        check("LSE", f64(r["LSE"]), ref["LSE"], t1)
+    else:
+        check_lse_with_empty_rows(f64(r["LSE"]), ref["LSE"], t1)
+    for k in ("dQ", "dK", "dV"):
+        check(k, f64(r[k]), ref[k], t1)
+    for k, rk in (("Hv_q", "gQ"), ("Hv_k", "gK"), ("Hv_v", "gV"), ("Hv_do", "gdO")):
+        check(k, f64(r[k]), ref[rk], t2)
