@@ -327,8 +327,9 @@ def sweep():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
         gq, gk, gv, gdo = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(k),
                            torch.empty_like(q))
-        ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
-        ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
+        # grouped-query sizes: room for the split column passes' partial sums
+        ws_b = torch.empty(fbd.bwd_ex_workspace_bytes(B, H, Hkv, N) // 4, device=dev)
+        ws_bb = torch.empty(fbd.bob_ex_workspace_bytes(B, H, Hkv, N) // 4, device=dev)
         i = np.arange(N, dtype=np.float64)
         vis = i + 1                                   # visible keys per query row
         bm = ds = None
