@@ -89,7 +89,7 @@ def main():
     if args.fp8 and args.gpus == 1:
         return fp8_bench(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads would shard across GPUs with no exchange); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
