@@ -196,37 +196,64 @@ __global__ __launch_bounds__(256) void fp8_vmax_kernel(const T* __restrict__ V,
   }
 }
 
-// V codes, transposed: one workgroup per 64-key tile of one head; thread ->
-// column d = tid % 64 and keys 16 kg .. 16 kg + 15 of the tile (kg = tid / 64),
-// so each load instruction of a wave reads one whole row.  The thread's four
-// 4-key words s = 4 kg .. 4 kg + 3 go to stored words 2 kg, 8 + 2 kg, 2 kg + 1,
-// 9 + 2 kg (stored word w holds source word 2 (w % 8) + w / 8).
+// V codes, transposed: one workgroup per 64-key tile of one head.  The tile's
+// sixteen 4-key words per column are stored in the order stored word w holds
+// source word 2 (w % 8) + w / 8.
 template <class T>
 __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const T* __restrict__ V,
                                                           const uint32_t* __restrict__ VMAX,
                                                           uint8_t* __restrict__ V8T,
                                                           int* __restrict__ EV, int N, int NP,
                                                           int ntile) {
+  // workgroup: one 64-key tile of one head.  Loads are row-major and whole
+  // rows wide (a lane takes 4 keys x 4 columns; the 16 lanes of a key group
+  // cover one 128-byte bf16 row per instruction); each lane packs its column
+  // codes into 4-key words, the words meet in LDS as a 64 x 16 word tile of
+  // V^T in stored order, and each lane then writes 16 contiguous bytes of
+  // one V^T row
+  __shared__ uint32_t sw[HD][17];   // [column][stored word], padded
   const int head = blockIdx.x / ntile, t = blockIdx.x % ntile;
-  const int d = threadIdx.x & 63, kg = threadIdx.x >> 6;
-  const int e = blk_exp(__uint_as_float(VMAX[(size_t)head * HD + d]));
-  if (t == 0 && kg == 0) EV[(size_t)head * HD + d] = e;
-  const int k0 = t * 64 + kg * 16;
-  const T* p = V + (size_t)head * N * HD + d;
-  int w[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int dg = lane & 15, s = (lane >> 4) + 4 * (tid >> 6);   // columns 4dg.., key group s
+  const int d0 = 4 * dg;
+  int e[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    float x[4];
+  for (int c = 0; c < 4; ++c) e[c] = blk_exp(__uint_as_float(VMAX[(size_t)head * HD + d0 + c]));
+  if (t == 0 && s == 0) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int key = k0 + 4 * s + b;
-      x[b] = key < N ? __builtin_amdgcn_ldexpf((float)p[(size_t)key * HD], -e) : 0.f;
-    }
-    w[s] = f8x4(x[0], x[1], x[2], x[3]);
+    for (int c = 0; c < 4; ++c) EV[(size_t)head * HD + d0 + c] = e[c];
   }
-  uint8_t* row = V8T + ((size_t)head * HD + d) * NP + t * 64;
-  *reinterpret_cast<int2*>(row + 8 * kg) = make_int2(w[0], w[2]);
-  *reinterpret_cast<int2*>(row + 32 + 8 * kg) = make_int2(w[1], w[3]);
+  const T* p = V + (size_t)head * N * HD + d0;
+  float x[4][4];   // [key][column]
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int key = t * 64 + 4 * s + b;
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = key < N ? *reinterpret_cast<const uint2*>(p + (size_t)key * HD)
+                              : make_uint2(0, 0);
+      const bf16x4 v4 = __builtin_bit_cast(bf16x4, u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[b][c] = (float)v4[c];
+    } else {
+      const f32x4 v4 = key < N ? *reinterpret_cast<const f32x4*>(p + (size_t)key * HD)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[b][c] = v4[c];
+    }
+  }
+  // key group s is stored as word 8 (s & 1) + (s >> 1) of its 64-key group
+  const int w = 8 * (s & 1) + (s >> 1);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    sw[d0 + c][w] = (uint32_t)f8x4(__builtin_amdgcn_ldexpf(x[0][c], -e[c]),
+                                   __builtin_amdgcn_ldexpf(x[1][c], -e[c]),
+                                   __builtin_amdgcn_ldexpf(x[2][c], -e[c]),
+                                   __builtin_amdgcn_ldexpf(x[3][c], -e[c]));
+  __syncthreads();
+  const int d = tid >> 2, part = tid & 3;
+  const uint4 o = make_uint4(sw[d][4 * part], sw[d][4 * part + 1], sw[d][4 * part + 2],
+                             sw[d][4 * part + 3]);
+  *reinterpret_cast<uint4*>(V8T + ((size_t)head * HD + d) * NP + t * 64 + 16 * part) = o;
 }
 
 // ---------------------------------------------------------------------------
