@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="time fwd, bwd and BoB separately over N = 1k .. 256k and the other "
                         "workload shapes (one JSON line per case) instead of the step")
+    p.add_argument("--case", default=None,
+                   help="with --sweep: only the named cases (comma-separated), e.g. "
+                        "sweep-N262144 for a counter run on the longest sequence")
     p.add_argument("--fp8", action="store_true",
                    help="time the FP8 forward (rotated quantisation pre-pass + E4M3 forward) on "
                         "the step's workload instead of the step (one JSON line)")
@@ -85,7 +88,7 @@ def parse():
 def main():
     args = parse()
     if args.sweep and args.gpus == 1:
-        return sweep()
+        return sweep(args.case)
     if args.fp8 and args.gpus == 1:
         return fp8_bench(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -272,7 +275,7 @@ def fp8_bench(args):
     print(json.dumps(line), flush=True)
 
 
-def sweep():
+def sweep(only=None):
     """Each operation timed on its own (HIP events on the launch stream; median
     of the repetitions after a warm-up) for N = 1k .. 256k with H = 12, d = 64,
     B = max(1, 16384 / N), for the gpt2s-layer (B8 H12 N1024) and large-key
@@ -311,6 +314,10 @@ def sweep():
         case("hvp-N4096", 4, 12, 4096, hvp=True),
     ]
     d = 64
+    if only:
+        cases = [c for c in cases if c["name"] in only.split(",")]
+        if not cases:
+            raise SystemExit(f"--case {only}: no such sweep case")
     for cs in cases:
         name, B, H, N, Hkv = cs["name"], cs["B"], cs["H"], cs["N"], cs["Hkv"]
         gen = torch.Generator(device=dev)
