@@ -20,11 +20,12 @@ The page leaves the details open.  The readings taken here:
     in as a 64-bit mask (bit i set: s_i = -1).  R is orthogonal, so
     (Q R)(K R)^T = Q K^T.  It is applied to the rows of Q and K only; the
     output is linear in V, so V is quantised as it is.
-  * The rotation runs in fp32 as the fast Walsh-Hadamard transform: six
-    butterfly stages with strides 1, 2, 4, ..., 32, each mapping a pair to
-    (a + b, a - b), then an exact multiply by 1/8.  The quantised codes
-    depend on these fp32 roundings, so the model and the kernel both use
-    them.
+  * The rotated values are the exact products x R, formed here in fp64 as
+    a plain matrix product with R written out from its definition (no fast
+    transform).  A kernel that rotates in fp32 rounds them; the tests allow
+    a code one step away exactly where the exact value lies within that
+    rounding's bound of a rounding boundary (and an exponent one away where
+    a block's largest magnitude lies that close to a power of two).
   * Blocks: Q and K get one scale per 64 consecutive rows of a head.  V gets
     one scale per column of a head.  P V is accumulated per output column
     over all keys, so a column scale costs one multiply at the end.  Scales
@@ -95,29 +96,28 @@ def sign_vector(signs: int) -> np.ndarray:
     return np.array([-1.0 if (int(signs) >> i) & 1 else 1.0 for i in range(64)])
 
 
-def fwht_f32(x) -> np.ndarray:
-    """Unnormalised Walsh-Hadamard transform along the last axis (length 64)
-    in fp32: y = H x for the Sylvester H.  Stages with strides 1, 2, ..., 32
-    each replace a pair (a, b) by (a + b, a - b)."""
-    y = np.array(x, dtype=np.float32, copy=True)
-    n = y.shape[-1]
-    assert n == 64
-    h = 1
-    while h < n:
-        y = y.reshape(*y.shape[:-1], n // (2 * h), 2, h)
-        a = y[..., 0, :].copy()
-        b = y[..., 1, :].copy()
-        y[..., 0, :] = a + b
-        y[..., 1, :] = a - b
-        y = y.reshape(*y.shape[:-3], n)
-        h *= 2
-    return y
+def hadamard(n: int = 64) -> np.ndarray:
+    """The n x n Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i & j)."""
+    i = np.arange(n)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    pop = np.zeros_like(bits)
+    while bits.any():
+        pop += bits & 1
+        bits >>= 1
+    return np.where(pop % 2 == 1, -1.0, 1.0)
+
+
+def rotation(signs: int) -> np.ndarray:
+    """R = diag(s) H / 8 (64 x 64, orthogonal)."""
+    return sign_vector(signs)[:, None] * hadamard(64) / 8.0
 
 
 def rotate(x, signs: int) -> np.ndarray:
-    """Rows of x times R = diag(s) H / 8, in fp32 (input rounded to fp32 first)."""
-    xs = np.asarray(x, dtype=np.float32) * sign_vector(signs).astype(np.float32)
-    return fwht_f32(xs) * np.float32(0.125)
+    """Rows of x times R in fp64: the signed sums of 64 bf16 or fp32 terms
+    err by at most 64 * 2^-53 * sum_k |x_k| / 8, some 2^-23 of what one fp32
+    rounding of the same sums may err, so these are the exact values for
+    every purpose the codes serve."""
+    return np.asarray(x, dtype=np.float64) @ rotation(signs)
 
 
 def block_exponent(amax) -> np.ndarray:
@@ -134,17 +134,17 @@ def quantize_rows(X, rotate_signs=None):
     may be short) with one exponent per block.  Returns (codes uint8
     (..., N, 64), exps int64 (..., ceil(N/64)))."""
     X = np.asarray(X)
-    x32 = rotate(X, rotate_signs) if rotate_signs is not None else X.astype(np.float32)
-    N = x32.shape[-2]
+    xr = rotate(X, rotate_signs) if rotate_signs is not None else X.astype(np.float64)
+    N = xr.shape[-2]
     nb = (N + ROW_BLOCK - 1) // ROW_BLOCK
-    codes = np.empty(x32.shape, dtype=np.uint8)
-    exps = np.empty(x32.shape[:-2] + (nb,), dtype=np.int64)
+    codes = np.empty(xr.shape, dtype=np.uint8)
+    exps = np.empty(xr.shape[:-2] + (nb,), dtype=np.int64)
     for b in range(nb):
-        blk = x32[..., b * ROW_BLOCK:(b + 1) * ROW_BLOCK, :]
+        blk = xr[..., b * ROW_BLOCK:(b + 1) * ROW_BLOCK, :]
         e = block_exponent(np.abs(blk).max(axis=(-2, -1)))
         exps[..., b] = e
-        scaled = np.ldexp(blk.astype(np.float64), -e[..., None, None])
-        codes[..., b * ROW_BLOCK:(b + 1) * ROW_BLOCK, :] = e4m3_encode(scaled)
+        codes[..., b * ROW_BLOCK:(b + 1) * ROW_BLOCK, :] = e4m3_encode(
+            np.ldexp(blk, -e[..., None, None]))
     return codes, exps
 
 

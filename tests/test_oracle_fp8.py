@@ -58,15 +58,17 @@ def test_encode_rejects_out_of_range():
         fp8.e4m3_encode([np.nan])
 
 
-def test_fwht_is_hadamard():
+def test_hadamard_and_rotation_match_scipy():
+    # the Sylvester matrix against scipy's; the rotation against a plain
+    # product with it, exactly on small integers (every fp64 step exact)
     H = scipy.linalg.hadamard(64).astype(np.float64)
+    np.testing.assert_array_equal(fp8.hadamard(64), H)
     rng = np.random.default_rng(1)
+    signs = 0x8000000000000001 | int(rng.integers(0, 2 ** 62))
+    s = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(64)])
     xi = rng.integers(-1000, 1000, size=(5, 64)).astype(np.float64)
-    # small integers: every fp32 step is exact
-    np.testing.assert_array_equal(fp8.fwht_f32(xi).astype(np.float64), xi @ H.T)
-    xf = rng.standard_normal((50, 64))
-    got = fp8.fwht_f32(xf).astype(np.float64)
-    np.testing.assert_allclose(got, xf @ H.T, rtol=0, atol=1e-5 * np.abs(xf).sum(axis=1).max())
+    np.testing.assert_array_equal(fp8.rotate(xi, signs), (xi * s) @ H / 8.0)
+    np.testing.assert_array_equal(fp8.rotation(signs), np.diag(s) @ H / 8.0)
 
 
 def test_rotation_is_orthogonal_with_signs():
@@ -78,10 +80,10 @@ def test_rotation_is_orthogonal_with_signs():
     np.testing.assert_allclose(R @ R.T, np.eye(64), atol=1e-15)
     q = rng.standard_normal((40, 64))
     k = rng.standard_normal((40, 64))
-    qr = fp8.rotate(q, signs).astype(np.float64)
-    kr = fp8.rotate(k, signs).astype(np.float64)
-    np.testing.assert_allclose(qr, q.astype(np.float32).astype(np.float64) @ R, atol=2e-6)
-    np.testing.assert_allclose(qr @ kr.T, q @ k.T, atol=2e-4)
+    qr = fp8.rotate(q, signs)
+    kr = fp8.rotate(k, signs)
+    np.testing.assert_allclose(qr, q @ R, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(qr @ kr.T, q @ k.T, rtol=0, atol=1e-12)
 
 
 def test_block_exponent_range():
@@ -104,7 +106,7 @@ def test_quantisation_error_bound():
         codes, exps = fp8.quantize_rows(x, signs)
         ref = x.astype(np.float32).astype(np.float64)
         if signs is not None:
-            ref = fp8.rotate(x, signs).astype(np.float64)
+            ref = fp8.rotate(x, signs)
         deq = fp8.dequantize_rows(codes, exps)
         e = np.repeat(exps, 64, axis=-1)[..., :200, None].astype(np.float64)
         bound = np.maximum(2.0 ** -4 * np.abs(ref), np.ldexp(2.0 ** -10, e.astype(np.int64)))
@@ -218,3 +220,41 @@ def test_fwd_fp8_masks_exact_on_representable_inputs():
         np.testing.assert_array_equal(r["LSE"], lse)
     assert np.all(np.isneginf(r["LSE"][..., :128]))
     assert np.all(r["W"][..., :128, :] == 0) and np.all(r["A"][..., :128] == 0)
+
+
+def test_fp8_weights_against_brute_force():
+    """W, U and A of fwd_fp8 against their definitions written as plain loops
+    over (row, key, channel) on a tiny case (dequantised operands from the
+    returned codes, probabilities from math.exp of the masked scores):
+      W_id = sum_j P_ij |v_jd|,   U_id = max_j P_ij * sum_{j visible} |v_jd|,
+      A_i  = max_{j visible} sum_d |q_id| |k_jd|."""
+    import math
+    rng = np.random.default_rng(10)
+    B, H, N = 1, 1, 7
+    q = rng.standard_normal((B, H, N, 64)) * 2
+    k = rng.standard_normal((B, H, N, 64))
+    v = rng.standard_normal((B, H, N, 64))
+    for causal, kw in ((True, {}), (False, {}), (True, dict(window=3))):
+        r = fp8.fwd_fp8(q, k, v, causal=causal, scale=0.2, signs=0xDEADBEEF, **kw)
+        c = r["codes"]
+        qh = fp8.dequantize_rows(c["q"], c["eq"])[0, 0]
+        kh = fp8.dequantize_rows(c["k"], c["ek"])[0, 0]
+        vh = fp8.dequantize_cols(c["v"], c["ev"])[0, 0]
+        win = kw.get("window", 0)
+        for i in range(N):
+            vis = [j for j in range(N) if (not causal or (j <= i and (win == 0 or j > i - win)))]
+            s = {j: 0.2 * sum(qh[i, t] * kh[j, t] for t in range(64)) for j in vis}
+            mx = max(s.values())
+            e = {j: math.exp(s[j] - mx) for j in vis}
+            tot = sum(e.values())
+            p = {j: e[j] / tot for j in vis}
+            for dd in range(64):
+                w = sum(p[j] * abs(vh[j, dd]) for j in vis)
+                u = max(p.values()) * sum(abs(vh[j, dd]) for j in vis)
+                assert abs(r["W"][0, 0, i, dd] - w) <= 1e-12 * max(w, 1e-300)
+                assert abs(r["U"][0, 0, i, dd] - u) <= 1e-12 * max(u, 1e-300)
+            a = max(sum(abs(qh[i, t]) * abs(kh[j, t]) for t in range(64)) for j in vis)
+            assert abs(r["A"][0, 0, i] - a) <= 1e-12 * a
+            o = [sum(p[j] * vh[j, dd] for j in vis) for dd in range(64)]
+            np.testing.assert_allclose(r["O"][0, 0, i], o, rtol=0, atol=1e-12)
+            assert abs(r["LSE"][0, 0, i] - (mx + math.log(tot))) <= 1e-12 * (1 + abs(mx))
