@@ -118,16 +118,20 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _check(name: str, t: torch.Tensor, like: torch.Tensor, dtype=None, shape=None):
+    """t is a dense tensor of the given dtype and shape (default: like's) on
+    like's GPU.  The kernels read every tensor as a dense (.., N, d) array
+    from its data pointer, so a strided view (a slice of a packed tensor, a
+    permutation) is rejected, never reinterpreted."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device != like.device or t.device.type != "cuda":
-        raise ValueError(f"{name} must be on the GPU device of q ({like.device})")
     if t.dtype != (like.dtype if dtype is None else dtype):
         raise TypeError(f"{name} has dtype {t.dtype}")
     if tuple(t.shape) != tuple(like.shape if shape is None else shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.device != like.device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU device of q ({like.device})")
 
 
 def _stream(dev) -> ctypes.c_void_p:
@@ -239,6 +243,7 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
     which lets the column pass split each group over several workgroups.
     passes: 1 row pass, 2 column pass, 3 both."""
     lib = load()
+    _check("q", q, q)
     Hkv = _kv_heads(q, k)
     kvs = _kv_shape(q, Hkv)
     for n, t in (("o", o), ("do", do)):
@@ -288,6 +293,7 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
     given, grouped-query heads get one of bob_ex_workspace_bytes (split column
     pass)."""
     lib = load()
+    _check("q", q, q)
     Hkv = _kv_heads(q, k)
     kvs = _kv_shape(q, Hkv)
     for n, t in (("o", o), ("do", do), ("g_dq", g_dq)):

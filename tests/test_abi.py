@@ -201,3 +201,32 @@ def test_fp8_rejects_bad_arguments_before_launch(lib):
     assert f8(causal=0, win=4) == 2         # a window needs the causal mask
     assert f8(ds=FAKE * 7 + 2) == 3         # doc_start must be 4-byte aligned
     assert f8(bm=lse) == 1                  # a block mask must not overlap an output
+
+
+@pytest.mark.parametrize("op", ["fwd", "bwd", "bob", "hvp"])
+@pytest.mark.parametrize("view", ["slice", "permute"])
+def test_binding_rejects_strided_q(op, view):
+    # The kernels read q through its data pointer as a dense (B, H, N, d)
+    # array.  A view with the right shape but other strides -- the first 64
+    # channels of a packed (B, H, N, 192) tensor, or a (B, N, H, d) tensor
+    # permuted to (B, H, N, d) -- must be rejected before anything is
+    # allocated or launched.  CPU tensors suffice: the layout checks come
+    # before the device check.
+    B, H, N, d = 1, 2, 8, 64
+    dense = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    if view == "slice":
+        q = torch.zeros(B, H, N, 3 * d, dtype=torch.bfloat16)[..., :d]
+    else:
+        q = torch.zeros(B, N, H, d, dtype=torch.bfloat16).permute(0, 2, 1, 3)
+    assert q.shape == dense.shape and not q.is_contiguous()
+    lse = torch.zeros(B, H, N)
+    t = dense
+    with pytest.raises(ValueError, match="q must be contiguous"):
+        if op == "fwd":
+            fbd.attn_fwd(q, t, t)
+        elif op == "bwd":
+            fbd.attn_bwd(q, t, t, t, lse, t, outs=(t, t, t))
+        elif op == "bob":
+            fbd.attn_bob(q, t, t, t, lse, t, t, t, t, outs=(t, t, t, t))
+        else:
+            fbd.attn_hvp(q, t, t, t, t, t, t)
