@@ -19,8 +19,10 @@
 // exponent, (S - m) * scale * log2(e) as one rounding of S * c - m * c: the
 // weight at the max is then 2^e with |e| at most half an ulp of m * c, which
 // the bf16 rounding of P (the value both l and P V use) takes to exactly 1
-// while |m * c| < 2^15.  Key tiles entirely in
-// the future of the workgroup's rows are never loaded (explainer page, section
+// while |m * c * log2(e)| < 2^16.  A wave with a row at 2^15 or beyond there
+// subtracts the max first instead (one more VALU operation per weight, only
+// in such tiles), so the largest weight is exactly 1 always.  Key tiles
+// entirely in the future of the workgroup's rows are never loaded (explainer page, section
 // "Causal masking is where trading gets a discount").
 //
 // K and V tiles reach LDS by buffer -> LDS DMA into two alternating buffers:
@@ -208,6 +210,10 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
         }
         m[g] = mn;
         nb[g] = -mn * sl2;
+        // the one-FMA exponent errs at the max by up to half an ulp of
+        // m * c * log2(e); below 2^15 that rounds away in bf16, beyond it a
+        // wave subtracts first (rare: scores of that size are extreme)
+        sub[g] = __any(!(__builtin_fabsf(nb[g]) < 32768.f));
       }
       seen[g] = seen[g] || fresh;
     }
@@ -217,12 +223,16 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
 #pragma unroll
       for (int g = 0; g < FWD_G; ++g) {
         float p[16];
-        if constexpr (!ACC_M) {
+        if (!ACC_M && !sub[g]) {
           // one FMA per weight: the weight at the max is 2^e with |e| at
-          // most half an ulp of m * sl2, which the bf16 rounding below takes
-          // to exactly 1, so l and P V still see the exact 1
+          // most half an ulp of m * sl2 (< 2^15), which the bf16 rounding
+          // below takes to exactly 1, so l and P V still see the exact 1
 #pragma unroll
           for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(x[sb][g][v], sl2, nb[g]));
+        } else if (!ACC_M) {
+          // subtract, then scale: exactly 2^0 at the max
+#pragma unroll
+          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f((x[sb][g][v] - m[g]) * sl2);
         } else if (sub[g]) {
 #pragma unroll
           for (int v = 0; v < 16; ++v)
