@@ -10,16 +10,9 @@ import torch
 
 import oracle
 import synthetic
-from gpu_util import inputs, rel_l2, say, tol
+from gpu_util import check, inputs, say, tol
 
 pytestmark = pytest.mark.gpu
-
-
-def check(name, got, ref, t):
-    e = rel_l2(got, ref)
-    say(f"    {name}: rel-L2 {e:.3e} (tol {t:.0e})")
-    assert np.all(np.isfinite(got)), name
-    assert e <= t, (name, e, t)
 
 
 def leaves(g, Hkv):
