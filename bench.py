@@ -2,21 +2,28 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
   attn_fwd -> attn_bwd (row pass, column pass; GProj on) -> attn_bob (row
-  pass, column pass), causal, on the BoB workload B=4, H=12, N=4096, d=64,
-  bf16 inputs with fp32 accumulation (Q, K, V, dO ~ 0.5 N(0,1), cotangents
-  ~ N(0,1), seeded).  Inputs are resident in device memory before timing.
+  pass, column pass), causal, bf16 inputs with fp32 accumulation, d = 64,
+  seeded inputs (Q, K, V, dO ~ 0.5 N(0,1), cotangents ~ N(0,1)) resident in
+  device memory before timing.  The reported line runs on the long-context
+  workload B=1, H=12, N=262144 (the FlashBoB page's 262k tokens).
 
 Prints ONE JSON line.  `value` is the step's model TFLOP/s under the FLOP
 convention (per unmasked causal (query, key) pair and head: forward 4d,
-backward 10d, backward-over-backward 38d); `roofline` is the dominant kernel's
-executed contraction FLOPs per launch over its HIP-event-timed duration against
-the bf16 dense MFMA peak; `cpu_baseline` is the fp64 oracle timed on a bounded
-sample of the same workload on this host.
+backward 10d, backward-over-backward 38d -- the 19 contraction units of the
+two-pass scheme); `value_min_work` counts the backward-over-backward as the
+12 units a single dense pass would need (24d).  `roofline` is the dominant
+kernel's executed contraction FLOPs per launch over its HIP-event-timed
+duration against the bf16 dense MFMA peak; `cpu_baseline` is the fp64 oracle
+timed on a bounded sample of the same workload on this host.  `extra` holds
+the B4 H12 N4096 step, the GPT-2-Small layer shape B8 H12 N1024 timed with
+the caches flushed before every kernel (HBM-bound: achieved GB/s of its
+algorithmic bytes), and the backward's time with GProj off and on.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
+                    [--no-extra] [--workload NAME]
 
 `--fp8` times the FP8 forward (rotated quantisation pre-pass + E4M3 forward)
-on the same workload instead of the step, one JSON line.
+on the B4 H12 N4096 workload instead of the step, one JSON line.
 
 `--sweep` instead times each operation separately over sequence lengths
 1k .. 256k (H=12, d=64, B = max(1, 16384/N), causal, GProj on), the other
@@ -40,12 +47,18 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
 HBM_PEAK_GBS = 8000.0
 METRIC = "attn fwd/bwd/BoB TFLOP/s & % bf16 MFMA peak, GPT-2S head shape, N≤262k"
+HEADLINE = "bob-long-B1H12N262144"
+FLUSH_BYTES = 512 << 20     # written between kernels: evicts L2 (8 x 4 MB) and MALL (256 MB)
 
 # Contraction units (N x N x d products, 2d FLOP per unmasked pair) executed
 # by each kernel; GProj adds one unit to each backward pass.
 UNITS = {"fwd": 2, "bwd_row": 4, "bwd_col": 5, "bob_row": 11, "bob_col": 8}
+UNITS_NO_GPROJ = {"bwd_row": 3, "bwd_col": 4}
 # FLOP convention per unmasked pair, in units of d
 CONV = {"fwd": 4, "bwd": 10, "bob": 38}
+# minimal work: a backward-over-backward in one dense pass (S, dP, W twice, U,
+# then g_Q, g_K twice each, g_V, g_dO twice) is 12 units
+CONV_MIN = {"fwd": 4, "bwd": 10, "bob": 24}
 # Algorithmic HBM bytes per launch as (tensors, row arrays): (B, H, N, d)
 # tensors read or written once, and (B, H, N) fp32 arrays.  fwd: Q, K, V, O
 # and LSE.  bwd_row: Q, K, V, O, dO, dQ; LSE in, D, r, -LSE log2(e) out.
@@ -55,16 +68,18 @@ CONV = {"fwd": 4, "bwd": 10, "bob": 38}
 # g_V out; -LSE log2(e), D, alpha, -kappa.
 ALG_BYTES = {"fwd": (4, 1), "bwd_row": (6, 4), "bwd_col": (6, 3), "bob_row": (10, 6),
              "bob_col": (9, 4)}
+KERNELS = ["fwd", "bwd_row", "bwd_col", "bob_row", "bob_col"]
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=48,
-                   help="heads of the workload the oracle baseline runs on")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the extra workloads (B4 H12 N4096 step, flushed GPT-2-Small "
+                        "layer, GProj on/off)")
     p.add_argument("--sweep", action="store_true",
                    help="time fwd, bwd and BoB separately over N = 1k .. 256k and the other "
                         "workload shapes (one JSON line per case) instead of the step")
@@ -73,16 +88,129 @@ def parse():
                         "sweep-N262144 for a counter run on the longest sequence")
     p.add_argument("--fp8", action="store_true",
                    help="time the FP8 forward (rotated quantisation pre-pass + E4M3 forward) on "
-                        "the step's workload instead of the step (one JSON line)")
-    p.add_argument("--workload", default="bob-B4H12N4096",
-                   choices=["bob-B4H12N4096", "gpt2s-layer-B8H12N1024"],
-                   help="workload the step runs on: the BoB workload (the reported line) or "
-                        "the GPT-2-Small layer shape, where each kernel is short and the "
-                        "memory traffic matters (for counter runs)")
+                        "the B4 H12 N4096 workload instead of the step (one JSON line)")
+    p.add_argument("--workload", default=HEADLINE,
+                   choices=[HEADLINE, "bob-B4H12N4096", "gpt2s-layer-B8H12N1024"],
+                   help="workload the step runs on: the long-context workload (the reported "
+                        "line), the B4 H12 N4096 BoB workload, or the GPT-2-Small layer "
+                        "shape (for counter runs)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a plain copy "
                         "kernel of known size, to calibrate memory counters)")
     return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def workload(name):
+    import synthetic
+    return {x.name: x for x in synthetic.WORKLOADS.values()}[name]
+
+
+class Step:
+    """Device tensors and the five launches of one step on workload w."""
+
+    def __init__(self, w, x, dev):
+        import torch
+        import fwd_bwd_double_amd as fbd
+        self.fbd, self.w = fbd, w
+        B, H, N = w.B, w.H, w.N
+        self.g = {k: v.to(dev) for k, v in x.items()}
+        q = self.g["q"]
+        self.o = torch.empty_like(q)
+        self.lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+        self.dq, self.dk, self.dv = (torch.empty_like(q) for _ in range(3))
+        self.has_bob = "g_dq" in self.g
+        if self.has_bob:
+            self.gq, self.gk, self.gv, self.gdo = (torch.empty_like(q) for _ in range(4))
+            self.ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
+        self.ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
+        self.names = KERNELS if self.has_bob else KERNELS[:3]
+
+    def launch(self, name, gproj=True):
+        g, sc, f = self.g, self.w.scale, self.fbd
+        if name == "fwd":
+            f.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=sc, out=self.o, lse=self.lse)
+        elif name.startswith("bwd"):
+            f.attn_bwd(g["q"], g["k"], g["v"], self.o, self.lse, g["do"], causal=True, scale=sc,
+                       gproj=gproj, workspace=self.ws_b, outs=(self.dq, self.dk, self.dv),
+                       passes=1 if name == "bwd_row" else 2)
+        else:
+            f.attn_bob(g["q"], g["k"], g["v"], self.o, self.lse, g["do"], g["g_dq"], g["g_dk"],
+                       g["g_dv"], causal=True, scale=sc, workspace=self.ws_bb,
+                       outs=(self.gq, self.gk, self.gv, self.gdo),
+                       passes=1 if name == "bob_row" else 2)
+
+    def run(self, ev=None, gproj=True, flush=None):
+        """One step; ev: HIP events recorded around each kernel (on torch's
+        current stream, the one the library launches on); flush: a buffer
+        written before every kernel (outside the events)."""
+        for i, n in enumerate(self.names):
+            if flush is not None:
+                flush.fill_(i + 1)
+            if ev is not None:
+                ev[2 * i].record()
+            self.launch(n, gproj)
+            if ev is not None:
+                ev[2 * i + 1].record()
+
+
+def timed_steps(st, steps, warmup, gproj=True, flush=None, wall=True):
+    """W untimed then K timed steps; returns (wall ms per step, {kernel: mean
+    event ms}).  The timed region is bracketed by device synchronisations."""
+    import numpy as np
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(st.names))]
+           for _ in range(max(steps, 1))]
+    for _ in range(warmup):
+        st.run(gproj=gproj, flush=flush)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        st.run(evs[s], gproj=gproj, flush=flush)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = {n: float(np.mean([e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs[:steps]]))
+            for i, n in enumerate(st.names)}
+    kmed = {n: float(np.median([e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs[:steps]]))
+            for i, n in enumerate(st.names)}
+    return (t1 - t0) * 1e3 / max(steps, 1), kern, kmed
+
+
+def report(w, names, kern_ms, ms_step, elt, gproj=True):
+    """Per-kernel and per-operation rates of one step on workload w."""
+    d = w.d
+    pairs = w.B * w.H * w.N * (w.N + 1) / 2      # unmasked causal pairs over all heads
+    unit = 2 * d * pairs                         # FLOP of one N x N x d contraction unit
+    units = dict(UNITS, **({} if gproj else UNITS_NO_GPROJ))
+    t_b, r_b = w.B * w.H * w.N * d * elt, w.B * w.H * w.N * 4
+    per_kernel = {}
+    for n in names:
+        ms = kern_ms[n]
+        ex = units[n] * unit / (ms * 1e-3) / 1e12
+        a, b = ALG_BYTES[n]
+        ab = a * t_b + b * r_b
+        per_kernel[n] = {"ms": ms, "executed_tflops": ex, "frac_mfma_peak": ex / PEAK_BF16_TFLOPS,
+                         "flop_per_launch": units[n] * unit, "alg_bytes": ab,
+                         "alg_gbs": ab / (ms * 1e-3) / 1e9,
+                         "frac_hbm_peak": ab / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    op_ms = {"fwd": kern_ms["fwd"], "bwd": kern_ms["bwd_row"] + kern_ms["bwd_col"]}
+    if "bob_row" in names:
+        op_ms["bob"] = kern_ms["bob_row"] + kern_ms["bob_col"]
+    per_op = {}
+    for op, ms in op_ms.items():
+        per_op[op] = {"ms": ms, "conv_tflops": CONV[op] * d * pairs / (ms * 1e-3) / 1e12,
+                      "min_work_tflops": CONV_MIN[op] * d * pairs / (ms * 1e-3) / 1e12}
+        per_op[op]["frac_mfma_peak"] = per_op[op]["conv_tflops"] / PEAK_BF16_TFLOPS
+    out = {"per_kernel": per_kernel, "per_op": per_op, "pairs": pairs}
+    if ms_step is not None:
+        out["ms_per_step"] = ms_step
+        out["value"] = sum(CONV[op] for op in op_ms) * d * pairs / (ms_step * 1e-3) / 1e12
+        out["value_min_work"] = (sum(CONV_MIN[op] for op in op_ms) * d * pairs /
+                                 (ms_step * 1e-3) / 1e12)
+    return out
 
 
 def main():
@@ -97,46 +225,16 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import fwd_bwd_double_amd as fbd
     import synthetic
 
-    w = {x.name: x for x in synthetic.WORKLOADS.values()}[args.workload]
-    B, H, N, d = w.B, w.H, w.N, w.d
+    w = workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    log(f"{w.name}: drawing the seeded inputs")
     x = synthetic.make_inputs(w)
-    g = {k: v.to(dev) for k, v in x.items()}
-    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    gq, gk, gv, gdo = (torch.empty_like(q) for _ in range(4))
-    ws_b = torch.empty(fbd.bwd_workspace_bytes(B, H, N) // 4, device=dev)
-    ws_bb = torch.empty(fbd.bob_workspace_bytes(B, H, N) // 4, device=dev)
-    sc = w.scale
-
-    names = ["fwd", "bwd_row", "bwd_col", "bob_row", "bob_col"]
-
-    def step(ev):
-        ev[0].record()
-        fbd.attn_fwd(q, k, v, causal=True, scale=sc, out=o, lse=lse)
-        ev[1].record()
-        fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=sc, gproj=True, workspace=ws_b,
-                     outs=(dq, dk, dv), passes=1)
-        ev[2].record()
-        fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=sc, gproj=True, workspace=ws_b,
-                     outs=(dq, dk, dv), passes=2)
-        ev[3].record()
-        fbd.attn_bob(q, k, v, o, lse, do, g["g_dq"], g["g_dk"], g["g_dv"], causal=True,
-                     scale=sc, workspace=ws_bb, outs=(gq, gk, gv, gdo), passes=1)
-        ev[4].record()
-        fbd.attn_bob(q, k, v, o, lse, do, g["g_dq"], g["g_dk"], g["g_dv"], causal=True,
-                     scale=sc, workspace=ws_bb, outs=(gq, gk, gv, gdo), passes=2)
-        ev[5].record()
-
+    st = Step(w, x, dev)
     if args.copy_mb > 0:
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -144,69 +242,109 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
-           for _ in range(max(args.steps, 1))]
-    for _ in range(args.warmup):
-        step(evs[0])
-    torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
-          flush=True)
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
-    kern_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs[:args.steps]]))
-               for i, n in enumerate(names)}
-
-    pairs = B * H * N * (N + 1) / 2          # unmasked causal pairs over all heads
-    unit = 2 * d * pairs                     # FLOP of one N x N x d contraction unit
-    step_flop = sum(CONV.values()) * d * pairs
-    value = step_flop / (ms_step * 1e-3) / 1e12
-    per_kernel = {n: {"ms": kern_ms[n],
-                      "executed_tflops": UNITS[n] * unit / (kern_ms[n] * 1e-3) / 1e12}
-                  for n in names}
-    # algorithmic bytes: one touch of every input and output, in units of one
-    # (B, H, N, d) tensor (t) and one (B, H, N) fp32 row-statistic array (r)
-    t_b, r_b = B * H * N * d * x["q"].element_size(), B * H * N * 4
-    alg_bytes = {n: a * t_b + b * r_b for n, (a, b) in ALG_BYTES.items()}
-    for n in names:
-        per_kernel[n]["frac_mfma_peak"] = per_kernel[n]["executed_tflops"] / PEAK_BF16_TFLOPS
-        per_kernel[n]["alg_bytes"] = alg_bytes[n]
-        per_kernel[n]["alg_gbs"] = alg_bytes[n] / (kern_ms[n] * 1e-3) / 1e9
-        per_kernel[n]["frac_hbm_peak"] = per_kernel[n]["alg_gbs"] / HBM_PEAK_GBS
-    op_ms = {"fwd": kern_ms["fwd"], "bwd": kern_ms["bwd_row"] + kern_ms["bwd_col"],
-             "bob": kern_ms["bob_row"] + kern_ms["bob_col"]}
-    per_op = {op: {"ms": op_ms[op],
-                   "conv_tflops": CONV[op] * d * pairs / (op_ms[op] * 1e-3) / 1e12}
-              for op in op_ms}
-    for op in per_op:
-        per_op[op]["frac_mfma_peak"] = per_op[op]["conv_tflops"] / PEAK_BF16_TFLOPS
-    dom = max(names, key=lambda n: kern_ms[n])
-    ach = per_kernel[dom]["executed_tflops"]
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+    log(f"{w.name}: {args.warmup} warm-up + {args.steps} timed steps")
+    ms_step, kern_ms, _ = timed_steps(st, args.steps, args.warmup)
+    rep = report(w, st.names, kern_ms, ms_step, x["q"].element_size())
+    log(f"{w.name}: {ms_step:.3f} ms per step, {rep['value']:.1f} TFLOP/s")
+    dom = max(st.names, key=lambda n: kern_ms[n])
+    pk = rep["per_kernel"][dom]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": pk["executed_tflops"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": pk["executed_tflops"] / PEAK_BF16_TFLOPS,
                 "traffic": stored_traffic(dom, w.name), "traffic_unit": "bytes per launch",
-                "flop_per_launch": UNITS[dom] * unit}
+                "flop_per_launch": pk["flop_per_launch"], "ms_per_launch": pk["ms"]}
+    peak_mem = torch.cuda.max_memory_allocated() / 1e9
+
+    extra = None
+    if not args.no_extra:
+        extra = {"gproj_overhead": {w.name: gproj_overhead(st, 3 if w.N > 65536 else 20)}}
+        del st
+        torch.cuda.empty_cache()
+        extra.update(extra_workloads(dev, w.name, extra["gproj_overhead"]))
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, w, min(args.cpu_heads, B * H))
+        log("cpu baseline (oracle on a bounded sample)")
+        cpu = cpu_baseline(x, w)
 
     line = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC, "value": rep["value"], "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": True,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
                    "gproj": True, "step": "fwd + bwd(row, col) + bob(row, col)",
                    "parallelism": "single GPU"},
-        "roofline": roofline, "cpu_baseline": cpu, "per_kernel": per_kernel, "per_op": per_op,
-        "peak_mem_gb": torch.cuda.max_memory_allocated() / 1e9,
+        "value_min_work": rep["value_min_work"],
+        "roofline": roofline, "cpu_baseline": cpu, "per_kernel": rep["per_kernel"],
+        "per_op": rep["per_op"], "peak_mem_gb": peak_mem, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def gproj_overhead(st, reps):
+    """The backward (row + column pass) with GProj off and on, alternating,
+    `reps` times each: median ms and the relative cost of the projection."""
+    import numpy as np
+    import torch
+    res = {False: [], True: []}
+    for _ in range(reps):
+        for gp in (False, True):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            st.launch("bwd_row", gp)
+            ev[1].record()
+            st.launch("bwd_col", gp)
+            ev[2].record()
+            torch.cuda.synchronize()
+            res[gp].append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])))
+    med = {gp: np.median(np.array(v), axis=0) for gp, v in res.items()}
+    off, on = float(med[False].sum()), float(med[True].sum())
+    out = {"reps": reps, "bwd_ms_gproj_off": off, "bwd_ms_gproj_on": on,
+           "bwd_row_ms": [float(med[False][0]), float(med[True][0])],
+           "bwd_col_ms": [float(med[False][1]), float(med[True][1])],
+           "bwd_overhead_frac": on / off - 1.0}
+    log(f"{st.w.name}: bwd {off:.3f} ms without GProj, {on:.3f} ms with (+{100 * (on / off - 1):.1f}%)")
+    return out
+
+
+def extra_workloads(dev, headline, gp):
+    """The B4 H12 N4096 step (20 steps after 5 warm-ups), its GProj cost, and
+    the GPT-2-Small layer shape B8 H12 N1024 (forward + backward) with a
+    512 MiB buffer written before every kernel so that each reads its inputs
+    from HBM (median of 20 steps)."""
+    import torch
+    import synthetic
+    out = {}
+    if headline != "bob-B4H12N4096":
+        w = workload("bob-B4H12N4096")
+        x = synthetic.make_inputs(w)
+        st = Step(w, x, dev)
+        ms, kern, _ = timed_steps(st, 20, 5)
+        rep = report(w, st.names, kern, ms, 2)
+        rep["stored_traffic"] = {n: stored_traffic(n, w.name) for n in st.names}
+        out[w.name] = rep
+        gp[w.name] = gproj_overhead(st, 20)
+        log(f"{w.name}: {ms:.3f} ms per step, {rep['value']:.1f} TFLOP/s")
+        del st
+    w = workload("gpt2s-layer-B8H12N1024")
+    x = synthetic.make_inputs(w, ("q", "k", "v", "do"))
+    st = Step(w, x, dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    _, kern_warm, _ = timed_steps(st, 20, 5)
+    _, _, kern_cold = timed_steps(st, 20, 3, flush=flush)
+    rep = report(w, st.names, kern_cold, None, 2)
+    rep["flushed_bytes_before_each_kernel"] = FLUSH_BYTES
+    rep["per_kernel_warm_ms"] = kern_warm
+    rep["stored_traffic"] = {n: stored_traffic(n, w.name) for n in st.names}
+    rep["floor_us"] = {n: v["alg_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6
+                       for n, v in rep["per_kernel"].items()}
+    out[w.name + " (flushed)"] = rep
+    log(f"{w.name} flushed: " + ", ".join(
+        f"{n} {v['ms'] * 1e3:.1f} us ({v['alg_gbs']:.0f} GB/s)" for n, v in rep["per_kernel"].items()))
+    del st, flush
+    torch.cuda.empty_cache()
+    return out
 
 
 def fp8_bench(args):
@@ -225,7 +363,7 @@ def fp8_bench(args):
     import fwd_bwd_double_amd as fbd
     import synthetic
 
-    w = {x.name: x for x in synthetic.WORKLOADS.values()}[args.workload]
+    w = workload("bob-B4H12N4096")
     B, H, N, d = w.B, w.H, w.N, w.d
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -462,8 +600,17 @@ def stored_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(x, w, nheads):
-    """The fp64 oracle (fwd + bwd + BoB, untuned) on the first `nheads` heads."""
+def cpu_baseline(x, w):
+    """The fp64 oracle (untuned) on a bounded sample of workload w, on this
+    host's cores.  Long sequences (N > 8192): the first 2048 rows of every
+    head (fwd, bwd and BoB of the causal prefix, which depends only on its
+    own keys), 16 seeded random rows of every head beyond them (each row's
+    outputs from its own definition) and the key-side BoB outputs of the last
+    32 keys of heads 0, 5 and 11 (only the last 32 rows see them).  Shorter
+    sequences: whole heads, as many as take about 10 s.  The rate counts the
+    (query, key) pairs the sample evaluates under the same FLOP convention
+    (52d per pair where fwd, bwd and BoB quantities are formed, 42d for the
+    key-side columns, which need no first-order gradients)."""
     import numpy as np
     import oracle
     from synthetic import to_f64
@@ -472,18 +619,48 @@ def cpu_baseline(x, w, nheads):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    heads = [(hh // w.H, hh % w.H) for hh in range(nheads)]
-    a = {k: to_f64(v) for k, v in x.items()}
+    d = w.d
+    conv_all = sum(CONV.values()) * d
+    flop = 0.0
     t0 = time.perf_counter()
-    oracle.bob(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"], heads=heads,
-               with_bwd=True)
+    if w.N > 8192:
+        n0 = 2048
+        pre = {k: to_f64(v[:, :, :n0]) for k, v in x.items()}
+        oracle.bob(pre["q"], pre["k"], pre["v"], pre["do"], pre["g_dq"], pre["g_dk"],
+                   pre["g_dv"], with_bwd=True)
+        flop += conv_all * w.B * w.H * n0 * (n0 + 1) / 2
+        rng = np.random.default_rng(5005)
+        rows = np.sort(rng.choice(np.arange(n0, w.N), 16, replace=False))
+        for h in range(w.H):
+            a = {k: to_f64(v[:, h:h + 1, : rows[-1] + 1]) for k, v in x.items()}
+            oracle.rows(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                        row_idx=rows)
+            flop += conv_all * float((rows + 1).sum())
+        for h in (0, 5, 11):
+            a = {k: to_f64(v[:, h:h + 1]) for k, v in x.items()}
+            oracle.last_columns(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"],
+                                a["g_dv"], ncols_tail=32, chunk=32)
+            flop += (CONV["fwd"] + CONV["bob"]) * d * 32 * w.N
+        sample = (f"{w.name}: rows 0..2047 of all {w.H} heads (fwd+bwd+BoB), 16 random rows "
+                  f"per head beyond them, BoB key-side outputs of the last 32 keys of 3 heads")
+    else:
+        per_head = w.N * (w.N + 1) / 2
+        nheads = max(1, min(w.B * w.H, int(10.0 * 2e10 / (conv_all * per_head))))
+        heads = [(hh // w.H, hh % w.H) for hh in range(nheads)]
+        a = {k: to_f64(v) for k, v in x.items()}
+        if "g_dq" in a:
+            oracle.bob(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                       heads=heads, with_bwd=True)
+            flop += conv_all * nheads * per_head
+            sample = f"{nheads} of {w.B * w.H} heads of {w.name}: fwd+bwd+BoB"
+        else:
+            oracle.bwd(a["q"], a["k"], a["v"], a["do"], heads=heads)
+            flop += (CONV["fwd"] + CONV["bwd"]) * d * nheads * per_head
+            sample = f"{nheads} of {w.B * w.H} heads of {w.name}: fwd+bwd"
     dt = time.perf_counter() - t0
-    pairs = nheads * w.N * (w.N + 1) / 2
-    flop = sum(CONV.values()) * w.d * pairs
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"{nheads} of {w.B * w.H} heads of {w.name}: fwd+bwd+BoB in fp64 NumPy, "
-                      f"same FLOP convention"}
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": dt,
+            "sample": sample + " in fp64 NumPy, same FLOP convention"}
 
 
 if __name__ == "__main__":
