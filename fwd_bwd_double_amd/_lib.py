@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_passes.restype = i32
     lib.attn_bob_passes.argtypes = [i32] + lib.attn_bob.argtypes
     lib.attn_bob_passes.restype = i32
+    lib.attn_bob_noalloc.argtypes = lib.attn_bob.argtypes[:-3] + [vp]
+    lib.attn_bob_noalloc.restype = i32
     for fn in (lib.attn_bwd_ex_workspace_bytes, lib.attn_bob_ex_workspace_bytes):
         fn.argtypes = [i64, i64, i64, i64]
         fn.restype = sz
@@ -331,6 +333,39 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
     else:
         st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bob", st)
+    return gq, gk, gv, gdo
+
+
+# Largest B * H * N attn_bob_noalloc accepts (its row states live in a
+# library-owned device array of this many rows).
+BOB_NOALLOC_MAX_ROWS = 3 << 20
+
+
+def attn_bob_noalloc(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
+                     scale: Optional[float] = None, outs=None
+                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """attn_bob without a workspace: the row states live in the library's
+    own device array (multi-head only, B * H * N <= BOB_NOALLOC_MAX_ROWS).
+    With `outs` given, the call allocates nothing.  Calls that overlap in
+    time on one GPU share that array and race."""
+    lib = load()
+    _check("q", q, q)
+    for n, t in (("k", k), ("v", v), ("o", o), ("do", do), ("g_dq", g_dq), ("g_dk", g_dk),
+                 ("g_dv", g_dv)):
+        _check(n, t, q)
+    B, H, N, d = q.shape
+    _check("lse", lse, q, torch.float32, (B, H, N))
+    if outs is None:
+        outs = tuple(torch.empty_like(q) for _ in range(4))
+    for n, t in zip(("g_q", "g_k", "g_v", "g_do"), outs):
+        _check(n, t, q)
+    gq, gk, gv, gdo = outs
+    st = lib.attn_bob_noalloc(_dt(q), B, H, N, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              o.data_ptr(), lse.data_ptr(), do.data_ptr(), g_dq.data_ptr(),
+                              g_dk.data_ptr(), g_dv.data_ptr(), 1 if causal else 0,
+                              _scale(q, scale), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+                              gdo.data_ptr(), _stream(q.device))
+    _raise("attn_bob_noalloc", st)
     return gq, gk, gv, gdo
 
 

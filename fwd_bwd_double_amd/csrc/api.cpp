@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "../../include/fbd.h"
@@ -528,3 +529,69 @@ attn_status attn_fwd_fp8(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward-over-backward without a caller workspace.  Its row states live in
+// a file-scope device array, one copy per GPU the library runs on, held until
+// the process ends.  Host code never passes the array's name to a kernel (in
+// host code the name is a stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device.
+static __device__ __align__(256) float scratch[ATTN_BOB_NOALLOC_MAX_ROWS * 5];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the null stream).
+attn_status scratch_on(void* stream, float** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return finish(e);
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return finish(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return finish(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return finish(e);
+    if (e2 != hipSuccess) return finish(e2);
+    if (!p) return ATTN_EHIP;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch[dev];
+  return ATTN_OK;
+}
+}  // namespace
+
+extern "C" attn_status attn_bob_noalloc(attn_dtype dt, int64_t B, int64_t H, int64_t N,
+                                        int64_t d, const void* Q, const void* K, const void* V,
+                                        const void* O, const float* LSE, const void* dO,
+                                        const void* g_dQ, const void* g_dK, const void* g_dV,
+                                        int causal, float scale, void* g_Q, void* g_K, void* g_V,
+                                        void* g_dO, void* stream) {
+  attn_status st = check_shape(dt, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)N > (uint64_t)ATTN_BOB_NOALLOC_MAX_ROWS)
+    return ATTN_EWORKSPACE;
+  // the caller's pointers first, so argument errors are reported as such
+  // before any device query
+  const size_t t = (size_t)B * H * N * d * elem_size(dt), s = (size_t)B * H * N * sizeof(float);
+  st = check_ptrs({{Q, t}, {K, t}, {V, t}, {O, t}, {LSE, s}, {dO, t}, {g_dQ, t}, {g_dK, t},
+                   {g_dV, t}},
+                  {{g_Q, t}, {g_K, t}, {g_V, t}, {g_dO, t}});
+  if (st != ATTN_OK) return st;
+  float* ws = nullptr;
+  if ((st = scratch_on(stream, &ws)) != ATTN_OK) return st;
+  // the multi-head workspace size: the unsplit column pass, as attn_bob with
+  // attn_bob_workspace_bytes; every row state is written by the row pass
+  // before the column pass reads it, so nothing needs clearing
+  return bob_impl(3, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, 0,
+                  nullptr, nullptr, scale, g_Q, g_K, g_V, g_dO, ws,
+                  attn_bob_workspace_bytes(B, H, N), stream);
+}

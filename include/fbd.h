@@ -145,6 +145,30 @@ attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * attn_bob for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, arguments, kernels and errors as attn_bob with no
+ * workspace argument.  The row states live in a library-owned device array
+ * of ATTN_BOB_NOALLOC_MAX_ROWS * 5 floats (60 MiB), one copy per GPU the
+ * library runs on, held until the process ends; its device address is looked
+ * up once per device, on the first call there.  The call allocates and frees
+ * nothing.  B * H * N above ATTN_BOB_NOALLOC_MAX_ROWS (12 heads at N = 262144)
+ * returns ATTN_EWORKSPACE before anything is enqueued.  Every call on one GPU
+ * uses that GPU's array, so calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller;
+ * calls on one stream are ordered.  Nothing in the array needs clearing: the
+ * row pass writes every state the column pass reads.  Multi-head only (the
+ * extended forms take a workspace).
+ */
+#define ATTN_BOB_NOALLOC_MAX_ROWS 3145728
+attn_status attn_bob_noalloc(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d,
+                             const void* Q, const void* K, const void* V, const void* O,
+                             const float* LSE, const void* dO,
+                             const void* g_dQ, const void* g_dK, const void* g_dV,
+                             int causal, float scale,
+                             void* g_Q, void* g_K, void* g_V, void* g_dO, void* stream);
+
+/*
  * The two passes of attn_bwd / attn_bob as separate calls, for callers that
  * schedule or time them on their own.  `passes` is 1 (row-block pass only),
  * 2 (column-block pass only) or 3 (both; identical to attn_bwd / attn_bob).

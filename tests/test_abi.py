@@ -230,3 +230,25 @@ def test_binding_rejects_strided_q(op, view):
             fbd.attn_bob(q, t, t, t, lse, t, t, t, t, outs=(t, t, t, t))
         else:
             fbd.attn_hvp(q, t, t, t, t, t, t)
+
+
+def test_bob_noalloc_rejects_bad_arguments_before_any_device_call(lib):
+    # attn_bob_noalloc: the size limit of the library's row-state array, then
+    # the caller's pointers, are checked before the device is queried
+    p = [FAKE * (i + 1) for i in range(13)]
+
+    def call(B=1, H=1, N=8, ptrs=None, dt=0):
+        a = p if ptrs is None else ptrs
+        return lib.attn_bob_noalloc(dt, B, H, N, 64, *a[:6], a[6], a[7], a[8], 1, 0.125,
+                                    a[9], a[10], a[11], a[12], None)
+
+    assert fbd.BOB_NOALLOC_MAX_ROWS == 3 << 20
+    assert call(B=1, H=13, N=262144) == 4           # 13 * 262144 rows > 12 * 262144
+    assert call(B=2, H=12, N=262144) == 4
+    assert call(B=1, H=12, N=262145) == 4
+    assert call(ptrs=[0] + p[1:]) == 1              # null input
+    assert call(ptrs=p[:9] + [0] + p[10:]) == 1     # null output
+    assert call(ptrs=[FAKE + 8] + p[1:]) == 3       # misaligned
+    assert call(ptrs=p[:9] + [p[0]] + p[10:]) == 1  # output aliases an input
+    assert call(dt=5) == 2
+    assert call(N=0) == 1
