@@ -299,16 +299,16 @@ def test_long_context_bob_sampled():
     for key in ("gQ", "gdO"):
         check(key, r[key][:, :, :n0], ref[key], 5e-2)
     rng = np.random.default_rng(5005)
-    rows = np.sort(rng.choice(np.arange(n0, w.N), 24, replace=False))
-    say(f"  24 random rows per head in [{n0}, N)")
+    rows = np.sort(rng.choice(np.arange(n0, w.N), 256, replace=False))
+    say(f"  256 random rows per head in [{n0}, N)")
     for h in range(w.H):
         a = {k: to_f64(v[:, h:h + 1, : rows[-1] + 1]) for k, v in x.items()}
         rr = oracle.rows(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
                          row_idx=rows)
         for key, t in (("O", 2e-2), ("LSE", 2e-2), ("gQ", 5e-2), ("gdO", 5e-2)):
             check(f"h{h} {key}", r[key][0, h][rows], rr[key][0], t)
-    say("  last 256 columns of heads 0, 5, 11")
-    for h in (0, 5, 11):
+    say("  last 256 columns of every head")
+    for h in range(w.H):
         a = {k: to_f64(v[:, h:h + 1]) for k, v in x.items()}
         tl = oracle.last_columns(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"],
                                  a["g_dv"], ncols_tail=256, chunk=32)
