@@ -133,6 +133,10 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
       // whole sub-block's matrix and vector work
       auto sub = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
+        // the compiler's single-wave interleave of matrix products and LDS
+        // reads (one wave per SIMD leaves no other wave to hide latency),
+        // measured 3% faster than its default schedule here
+        __builtin_amdgcn_iglp_opt(1);
       f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
