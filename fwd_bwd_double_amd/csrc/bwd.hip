@@ -29,13 +29,17 @@
 
 namespace fbd {
 
-template <class T, int BN, bool GPROJ, bool CAUSAL, bool DOCS, bool BMASK>
-__global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
+// NW waves per workgroup: 4 (128 query rows), or 8 (256 rows) for long
+// sequences without a block mask
+template <class T, int BN, int NW, bool GPROJ, bool CAUSAL, bool DOCS, bool BMASK>
+__global__ __launch_bounds__(64 * NW, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     T* __restrict__ dQ, float* __restrict__ Dws, float* __restrict__ Rws, float* __restrict__ Lws,
     int N, int BH, int H, int grp, int win, const int* __restrict__ DS,
     const uint8_t* __restrict__ BMK, int nblk, float scale) {
+  constexpr int ROWS = NW * WROWS;   // query rows per workgroup
+  static_assert(!BMASK || ROWS == 128, "a workgroup owns one 128-row block of the block-sparse mask");
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   __shared__ __attribute__((aligned(16))) T K0[BN * HD];
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   const auto rk = make_rsrc(K + kvoff, hbytes);
   const auto rv = make_rsrc(V + kvoff, hbytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q0 = wk.blk * BLK;
+  const int q0 = wk.blk * ROWS;
   const int qw = q0 + wave * WROWS;
   const int my_i = qw + (lane & 31);
   const int h = lane >> 5;
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
   const int rs_w = DOCS ? __builtin_amdgcn_readlane(rs, 31) : 0;      // the wave's largest
   const int rs0 = DOCS ? row_start(ds, q0, win, N) : q0 - win + 1;
   const int jbeg = CAUSAL ? min(max(0, rs0), q0) / BN * BN : 0;
-  const int jend = CAUSAL ? min(N, q0 + BLK) : N;
+  const int jend = CAUSAL ? min(N, q0 + ROWS) : N;
   const int ntiles = (jend - jbeg + BN - 1) / BN;
   // block-sparse mask (a compile-time variant): the workgroup's row of
   // 128 x 128 blocks; the loop visits every tile index, and a tile of a
@@ -93,8 +97,8 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     wait_dma();
     __syncthreads();   // tile t is in (Ks, Vs); every wave is done with (Kn, Vn)
     if (t + 1 < ntiles && kept(t + 1)) {
-      dma_tile<T, BN, NT / 64>(rk, j0 + BN, Kn, wave, lane);
-      dma_tile<T, BN, NT / 64>(rv, j0 + BN, Vn, wave, lane);
+      dma_tile<T, BN, NW>(rk, j0 + BN, Kn, wave, lane);
+      dma_tile<T, BN, NW>(rv, j0 + BN, Vn, wave, lane);
     }
     if (!kept(t)) return;
 #pragma unroll
@@ -144,8 +148,8 @@ __global__ __launch_bounds__(NT, FBD_BWD_ROW_OCC) void bwd_row_kernel(
     }
   };
   if (!BMASK || (ntiles > 0 && kept(0))) {
-    dma_tile<T, BN, NT / 64>(rk, jbeg, K0, wave, lane);
-    dma_tile<T, BN, NT / 64>(rv, jbeg, V0, wave, lane);
+    dma_tile<T, BN, NW>(rk, jbeg, K0, wave, lane);
+    dma_tile<T, BN, NW>(rv, jbeg, V0, wave, lane);
   }
   for (int t = 0; t < ntiles; t += 2) {
     tile(t, K0, V0, K1, V1);
@@ -419,13 +423,18 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BWD_BN : 64, BM = sizeof(T) == 2 ? FBD_BWD_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
-  // the block mask selects a compile-time kernel variant
-  auto row = [&](auto bmask) {
-    hipLaunchKernelGGL((bwd_row_kernel<T, BN, GPROJ, CAUSAL, DOCS, decltype(bmask)::value>),
-                       dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)O, LSE, (const T*)dO, (T*)dQ, Dws, Rws, Lws, N, BH, H, grp, win,
-                       ds, bm, nblk, scale);
+  // the block mask selects a compile-time kernel variant; without one, bf16
+  // row passes over long sequences take 8-wave workgroups
+  auto row = [&](auto nw, auto bmask) {
+    constexpr int NW = decltype(nw)::value;
+    const int nrb = (N + NW * WROWS - 1) / (NW * WROWS);
+    hipLaunchKernelGGL((bwd_row_kernel<T, BN, NW, GPROJ, CAUSAL, DOCS, decltype(bmask)::value>),
+                       dim3(nrb * BH), dim3(64 * NW), 0, st, (const T*)Q, (const T*)K,
+                       (const T*)V, (const T*)O, LSE, (const T*)dO, (T*)dQ, Dws, Rws, Lws, N, BH,
+                       H, grp, win, ds, bm, nrb, scale);
   };
+  using W4 = std::integral_constant<int, 4>;
+  using W8 = std::integral_constant<int, 8>;
   auto col = [&](auto bmask) {
     hipLaunchKernelGGL((bwd_col_kernel<T, BM, GPROJ, CAUSAL, DOCS, decltype(bmask)::value>),
                        dim3(nblk * (BH / grp) * nsl), dim3(NT), 0, st, (const T*)Q,
@@ -434,8 +443,11 @@ static hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, cons
                        ds, bm, scale, nsl, Part);
   };
   if (passes & 1) {
-    if (bm) row(std::true_type{});
-    else row(std::false_type{});
+    bool wide = false;
+    if constexpr (sizeof(T) == 2) wide = !bm && N >= FBD_WIDE_N;
+    if (bm) row(W4{}, std::true_type{});
+    else if (!wide) row(W4{}, std::false_type{});
+    else if constexpr (sizeof(T) == 2) row(W8{}, std::false_type{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -29,7 +29,7 @@
 // the copy of tile t+1 runs while tile t is computed.  V is read along the
 // key index with the transposing LDS read, so both stay row-major.
 //
-// Layout: FWD_WAVES waves per workgroup, FWD_G groups of 32 queries per wave,
+// Layout: NW waves per workgroup, FWD_G groups of 32 queries per wave,
 // one query per lane in each group (4 x 1 measured fastest on MI355X: more
 // groups per wave halve LDS reads per FLOP but cost occupancy).  The row sum
 // l adds the bf16-rounded probabilities -- the values the P V product uses --
@@ -41,14 +41,12 @@
 
 namespace fbd {
 
-constexpr int FWD_WAVES = FBD_FWD_WAVES;
-constexpr int FWD_NT = 64 * FWD_WAVES;
-constexpr int FWD_G = FBD_FWD_G;                      // 32-query groups per wave
-constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;    // query rows per workgroup
-static_assert(FWD_BLK == 128, "a workgroup owns one 128-row block of the block-sparse mask");
+constexpr int FWD_G = FBD_FWD_G;   // 32-query groups per wave
 
-template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK>
-__global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __restrict__ Q,
+// NW waves per workgroup: 4 (128 query rows), or 8 (256 rows) for long
+// sequences without a block mask
+template <class T, int BN, int NW, bool CAUSAL, bool DOCS, bool BMASK>
+__global__ __launch_bounds__(64 * NW, FBD_FWD_OCC) void fwd_kernel(const T* __restrict__ Q,
                                                      const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ O,
                                                      float* __restrict__ LSE, int N, int BH,
@@ -56,6 +54,10 @@ __global__ __launch_bounds__(FWD_NT, FBD_FWD_OCC) void fwd_kernel(const T* __res
                                                      const int* __restrict__ DS,
                                                      const uint8_t* __restrict__ BMK, int nblk,
                                                      float scale) {
+  constexpr int FWD_WAVES = NW;
+  constexpr int FWD_BLK = FWD_WAVES * FWD_G * WROWS;   // query rows per workgroup
+  static_assert(!BMASK || FWD_BLK == 128,
+                "a workgroup owns one 128-row block of the block-sparse mask");
   // two buffers as separate objects, used in a loop unrolled by two, so the
   // compiler can tell the copy of the next tile never aliases the reads of
   // the current one (and places no wait between them)
@@ -296,23 +298,38 @@ static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void
                                int BH, int H, int grp, int win, const int* ds,
                                const uint8_t* bm, int N, float scale, hipStream_t st) {
   constexpr int BN = sizeof(T) == 2 ? FBD_FWD_BN : 64;
-  const int nblk = (N + FWD_BLK - 1) / FWD_BLK;
-  auto run = [&](auto docs, auto bmask) {
-    hipLaunchKernelGGL((fwd_kernel<T, BN, CAUSAL, decltype(docs)::value, decltype(bmask)::value>),
-                       dim3(nblk * BH), dim3(FWD_NT), 0, st, (const T*)Q, (const T*)K,
-                       (const T*)V, (T*)O, LSE, N, BH, H, grp, win, ds, bm, nblk, scale);
+  auto run = [&](auto nw, auto docs, auto bmask) {
+    constexpr int NW = decltype(nw)::value;
+    constexpr int ROWS = NW * FWD_G * WROWS;
+    const int nblk = (N + ROWS - 1) / ROWS;
+    hipLaunchKernelGGL(
+        (fwd_kernel<T, BN, NW, CAUSAL, decltype(docs)::value, decltype(bmask)::value>),
+        dim3(nblk * BH), dim3(64 * NW), 0, st, (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE,
+        N, BH, H, grp, win, ds, bm, nblk, scale);
   };
   using Y = std::true_type;
   using F = std::false_type;
+  using W4 = std::integral_constant<int, 4>;
+  using W8 = std::integral_constant<int, 8>;
+  // without a block mask, bf16 operands and long sequences: 8-wave workgroups
+  auto run_unmasked = [&](auto docs) {
+    if constexpr (sizeof(T) == 2) {
+      if (N >= FBD_WIDE_N) {
+        run(W8{}, docs, F{});
+        return;
+      }
+    }
+    run(W4{}, docs, F{});
+  };
   if constexpr (CAUSAL) {
     if (ds) {
-      if (bm) run(Y{}, Y{});
-      else run(Y{}, F{});
+      if (bm) run(W4{}, Y{}, Y{});
+      else run_unmasked(Y{});
       return hipGetLastError();
     }
   }
-  if (bm) run(F{}, Y{});
-  else run(F{}, F{});
+  if (bm) run(W4{}, F{}, Y{});
+  else run_unmasked(F{});
   return hipGetLastError();
 }
 

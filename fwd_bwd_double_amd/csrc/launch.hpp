@@ -10,12 +10,17 @@
 #ifndef FBD_FWD_BN
 #define FBD_FWD_BN 64
 #endif
-// forward: waves per workgroup and 32-query groups per wave
-#ifndef FBD_FWD_WAVES
-#define FBD_FWD_WAVES 4
-#endif
+// forward: 32-query groups per wave
 #ifndef FBD_FWD_G
 #define FBD_FWD_G 1
+#endif
+// Sequence length from which the forward and the backward row pass run
+// 8-wave workgroups over 256-row blocks (no block mask, bf16): each streamed
+// key tile then serves twice the queries, which halves the L2-miss traffic
+// of the long key streams (measured 5% and 3% faster at N = 262144; slower
+// below N = 32768, where fewer, longer workgroups leave a longer tail).
+#ifndef FBD_WIDE_N
+#define FBD_WIDE_N 65536
 #endif
 // forward: minimum waves per SIMD the register budget must allow.  At 4 the
 // bf16 kernel fits 128 registers without spilling (the compiler alone picks

@@ -319,11 +319,12 @@ def bob_gqa(Q, K, V, dO, gdQ, gdK, gdV, causal=True, scale=None, with_bwd=False,
 
 
 def rows(Q, K, V, dO=None, gdQ=None, gdK=None, gdV=None, row_idx=None,
-         causal=True, scale=None, heads=None):
+         causal=True, scale=None, heads=None, window=0, docs=None):
     """Row outputs (O, LSE, D, dQ, alpha, beta, gQ, gdO) for selected rows of
     selected heads, each row computed exactly from its own definition.
-    ``row_idx`` is a sorted 1-D array of query positions.  Returns a dict of
-    arrays shaped (len(heads), len(row_idx)[, d])."""
+    ``row_idx`` is a sorted 1-D array of query positions; ``window`` and
+    ``docs`` (each batch row's document starts) are the masks of ``fwd``.
+    Returns a dict of arrays shaped (len(heads), len(row_idx)[, d])."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, H, N, d = Q.shape
     c = 1.0 / np.sqrt(d) if scale is None else float(scale)
@@ -335,7 +336,8 @@ def rows(Q, K, V, dO=None, gdQ=None, gdK=None, gdV=None, row_idx=None,
     for n, (b, h) in enumerate(heads):
         g = lambda X: None if X is None else _f64(X[b, h])
         r, _ = _head(Q[b, h], K[b, h], V[b, h], g(dO), g(gdQ), g(gdK), g(gdV),
-                     row_idx, causal, c, want_bwd, want_bob)
+                     row_idx, causal, c, want_bwd, want_bob, window,
+                     None if docs is None else np.asarray(docs)[b])
         for key, val in r.items():
             if key in _ROW_KEYS:
                 res.setdefault(key, []).append(val)
@@ -343,11 +345,12 @@ def rows(Q, K, V, dO=None, gdQ=None, gdK=None, gdV=None, row_idx=None,
 
 
 def last_columns(Q, K, V, dO, gdQ=None, gdK=None, gdV=None, ncols_tail=256,
-                 scale=None, heads=None, chunk=256):
+                 scale=None, heads=None, chunk=256, window=0, docs=None):
     """Column outputs for the last ``ncols_tail`` keys of a causal head: dK and
     dV, or gK and gV when the cotangents are given.  Under the causal mask key j is
-    seen only by queries i >= j, so the rows N - ncols_tail .. N - 1 hold every
-    contribution to these columns.  Returns arrays (len(heads), ncols_tail, d)."""
+    seen only by queries i >= j (a window or document mask only removes some of
+    them), so the rows N - ncols_tail .. N - 1 hold every contribution to these
+    columns.  Returns arrays (len(heads), ncols_tail, d)."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     B, H, N, d = Q.shape
     c = 1.0 / np.sqrt(d) if scale is None else float(scale)
@@ -361,7 +364,8 @@ def last_columns(Q, K, V, dO, gdQ=None, gdK=None, gdV=None, ncols_tail=256,
         for r0 in range(n0, N, chunk):
             idx = np.arange(r0, min(N, r0 + chunk))
             r, ncols = _head(Q[b, h], K[b, h], V[b, h], g(dO), g(gdQ), g(gdK),
-                             g(gdV), idx, True, c, not want_bob, want_bob)
+                             g(gdV), idx, True, c, not want_bob, want_bob, window,
+                             None if docs is None else np.asarray(docs)[b])
             for key, val in r.items():
                 if key in _COL_KEYS:
                     tail = np.zeros((ncols_tail, d))

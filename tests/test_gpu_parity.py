@@ -572,6 +572,49 @@ def test_document_masks(N, mean_len, window, H, Hkv, dtype):
             check(k, f64(t), ref[k], t2)
 
 
+
+# ------------------------ long sequences: 8-wave forward and backward row passes
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", ["causal", "full", "window", "docs"])
+def test_wide_row_blocks_long_sequence(case):
+    """From 65536 keys on, bf16 without a block mask, the forward and the
+    backward row pass run 8-wave workgroups over 256-row blocks.  B1 H2 N65536:
+    O, LSE and dQ (GProj off and on) on 256 seeded rows of each head against
+    each row's own definition, and dK, dV on the last 256 keys of each head
+    (the causal masks: only the last rows see those keys)."""
+    import fwd_bwd_double_amd as fbd
+    N = 65536
+    causal = case != "full"
+    w = synthetic.Workload(f"wide-{case}", 1, 2, N, 64, "bf16", 9900 + len(case), causal=causal,
+                           qkv_std=1.0)
+    x, g, a = inputs(w, ("q", "k", "v", "do"))
+    window = 3000 if case == "window" else 0
+    docs = doc_starts(1, N, 9901, 9000) if case == "docs" else None
+    ds = torch.from_numpy(docs.astype(np.int32)).cuda() if docs is not None else None
+    say(f"[gpu] wide row blocks: {case} B=1 H=2 N={N} window={window}")
+    o, lse = fbd.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, window=window,
+                          doc_start=ds)
+    rng = np.random.default_rng(9902)
+    rows = np.sort(np.concatenate([rng.choice(np.arange(N), 252, replace=False),
+                                   [0, 255, 256, N - 1]]))
+    rows = np.unique(rows)
+    ref = oracle.rows(a["q"], a["k"], a["v"], a["do"], row_idx=rows, causal=causal,
+                      scale=w.scale, window=window, docs=docs)
+    tail = (oracle.last_columns(a["q"], a["k"], a["v"], a["do"], ncols_tail=256,
+                                scale=w.scale, window=window, docs=docs) if causal else None)
+    f64 = synthetic.to_f64
+    check("O", f64(o)[0][:, rows], ref["O"], 2e-2)
+    check("LSE", f64(lse)[0][:, rows], ref["LSE"], 2e-2)
+    for gproj in (False, True):
+        dq, dk, dv = fbd.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal,
+                                  scale=w.scale, gproj=gproj, window=window, doc_start=ds)
+        torch.cuda.synchronize()
+        say(f"  gproj={gproj}")
+        check("dQ", f64(dq)[0][:, rows], ref["dQ"], 2e-2)
+        if causal:
+            check("dK last 256 keys", f64(dk)[0][:, -256:], tail["dK"], 2e-2)
+            check("dV last 256 keys", f64(dv)[0][:, -256:], tail["dV"], 2e-2)
+
 # ------------------------------------------ block-sparse masks (128 x 128 blocks)
 def block_masks(B, N, seed, density, keep_diag):
     """Seeded (B, nb, nb) uint8 block mask, nb = ceil(N / 128): each block kept

@@ -393,6 +393,32 @@ def test_rows_and_last_columns_match_dense():
     assert np.all(h["gK"][0, 0] == 0.0)
 
 
+
+@pytest.mark.parametrize("window,with_docs", [(33, False), (0, True), (20, True)])
+def test_rows_and_last_columns_match_dense_under_masks(window, with_docs):
+    """The row and column samplers with a sliding window or document starts
+    give the dense oracle's rows and last columns (the masks only drop keys,
+    so the last rows still hold every contribution to the last keys)."""
+    Q, K, V, dO, A, Bk, C = inputs(1, 2, 200, 8, 211)
+    starts = None
+    if with_docs:
+        starts = np.zeros((1, 200), dtype=np.int64)
+        starts[0, 70:] = 70
+        starts[0, 150:] = 150
+    full = oracle.bob(Q, K, V, dO, A, Bk, C, with_bwd=True, chunk=37, window=window,
+                      docs=starts)
+    idx = np.array([0, 5, 69, 70, 100, 149, 150, 199])
+    r = oracle.rows(Q, K, V, dO, A, Bk, C, row_idx=idx, window=window, docs=starts)
+    for key in ("O", "LSE", "D", "dQ", "alpha", "beta", "gQ", "gdO"):
+        assert np.allclose(r[key], full[key][0][:, idx], atol=1e-12), key
+    t = oracle.last_columns(Q, K, V, dO, ncols_tail=64, chunk=16, window=window, docs=starts)
+    for key in ("dK", "dV"):
+        assert np.allclose(t[key], full[key][0][:, -64:], atol=1e-12), key
+    t = oracle.last_columns(Q, K, V, dO, A, Bk, C, ncols_tail=64, chunk=16, window=window,
+                            docs=starts)
+    for key in ("gK", "gV"):
+        assert np.allclose(t[key], full[key][0][:, -64:], atol=1e-11), key
+
 # ---------------------------------------------------------------- GProj
 def test_gproj_projection_properties():
     Q, K = rnd((1, 2, 30, 8), 220), rnd((1, 2, 30, 8), 221)
