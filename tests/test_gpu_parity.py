@@ -575,33 +575,44 @@ def test_document_masks(N, mean_len, window, H, Hkv, dtype):
 
 # ------------------------ long sequences: 8-wave forward and backward row passes
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("case", ["causal", "full", "window", "docs"])
+@pytest.mark.parametrize("case", ["causal", "full", "window", "docs", "gqa"])
 def test_wide_row_blocks_long_sequence(case):
     """From 65536 keys on, bf16 without a block mask, the forward and the
     backward row pass run 8-wave workgroups over 256-row blocks.  B1 H2 N65536:
     O, LSE and dQ (GProj off and on) on 256 seeded rows of each head against
     each row's own definition, and dK, dV on the last 256 keys of each head
-    (the causal masks: only the last rows see those keys)."""
+    (the causal masks: only the last rows see those keys).  The grouped-query
+    case shares each key/value head between two query heads: its dK, dV are
+    the group sums."""
     import fwd_bwd_double_amd as fbd
     N = 65536
     causal = case != "full"
-    w = synthetic.Workload(f"wide-{case}", 1, 2, N, 64, "bf16", 9900 + len(case), causal=causal,
+    H, Hkv = (4, 2) if case == "gqa" else (2, 2)
+    grp = H // Hkv
+    w = synthetic.Workload(f"wide-{case}", 1, H, N, 64, "bf16", 9900 + len(case), causal=causal,
                            qkv_std=1.0)
     x, g, a = inputs(w, ("q", "k", "v", "do"))
+    for n in ("k", "v"):
+        g[n] = g[n][:, :Hkv].contiguous()
+        a[n] = a[n][:, :Hkv]
     window = 3000 if case == "window" else 0
     docs = doc_starts(1, N, 9901, 9000) if case == "docs" else None
     ds = torch.from_numpy(docs.astype(np.int32)).cuda() if docs is not None else None
-    say(f"[gpu] wide row blocks: {case} B=1 H=2 N={N} window={window}")
+    say(f"[gpu] wide row blocks: {case} B=1 H={H} Hkv={Hkv} N={N} window={window}")
     o, lse = fbd.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, window=window,
                           doc_start=ds)
     rng = np.random.default_rng(9902)
     rows = np.sort(np.concatenate([rng.choice(np.arange(N), 252, replace=False),
                                    [0, 255, 256, N - 1]]))
     rows = np.unique(rows)
-    ref = oracle.rows(a["q"], a["k"], a["v"], a["do"], row_idx=rows, causal=causal,
-                      scale=w.scale, window=window, docs=docs)
-    tail = (oracle.last_columns(a["q"], a["k"], a["v"], a["do"], ncols_tail=256,
-                                scale=w.scale, window=window, docs=docs) if causal else None)
+    kx, vx = oracle.expand_kv(a["k"], grp), oracle.expand_kv(a["v"], grp)
+    ref = oracle.rows(a["q"], kx, vx, a["do"], row_idx=rows, causal=causal, scale=w.scale,
+                      window=window, docs=docs)
+    tail = None
+    if causal:
+        tail = oracle.last_columns(a["q"], kx, vx, a["do"], ncols_tail=256, scale=w.scale,
+                                   window=window, docs=docs)
+        tail = {k: oracle.reduce_kv(v[None], grp)[0] for k, v in tail.items()}
     f64 = synthetic.to_f64
     check("O", f64(o)[0][:, rows], ref["O"], 2e-2)
     check("LSE", f64(lse)[0][:, rows], ref["LSE"], 2e-2)
