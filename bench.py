@@ -604,7 +604,7 @@ def cpu_baseline(x, w):
     """The fp64 oracle (untuned) on a bounded sample of workload w, on this
     host's cores.  Long sequences (N > 8192): the first 2048 rows of every
     head (fwd, bwd and BoB of the causal prefix, which depends only on its
-    own keys), 48 seeded random rows of every head beyond them (each row's
+    own keys), 128 seeded random rows of every head beyond them (each row's
     outputs from its own definition) and the key-side BoB outputs of the last
     64 keys of heads 0, 4, 7 and 11 (only the last 64 rows see them).  Shorter
     sequences: whole heads, as many as take about 10 s.  The rate counts the
@@ -630,7 +630,7 @@ def cpu_baseline(x, w):
                    pre["g_dv"], with_bwd=True)
         flop += conv_all * w.B * w.H * n0 * (n0 + 1) / 2
         rng = np.random.default_rng(5005)
-        rows = np.sort(rng.choice(np.arange(n0, w.N), 48, replace=False))
+        rows = np.sort(rng.choice(np.arange(n0, w.N), 128, replace=False))
         for h in range(w.H):
             a = {k: to_f64(v[:, h:h + 1, : rows[-1] + 1]) for k, v in x.items()}
             oracle.rows(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
@@ -641,7 +641,7 @@ def cpu_baseline(x, w):
             oracle.last_columns(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"],
                                 a["g_dv"], ncols_tail=64, chunk=64)
             flop += (CONV["fwd"] + CONV["bob"]) * d * 64 * w.N
-        sample = (f"{w.name}: rows 0..2047 of all {w.H} heads (fwd+bwd+BoB), 48 random rows "
+        sample = (f"{w.name}: rows 0..2047 of all {w.H} heads (fwd+bwd+BoB), 128 random rows "
                   f"per head beyond them, BoB key-side outputs of the last 64 keys of 4 heads")
     else:
         per_head = w.N * (w.N + 1) / 2
