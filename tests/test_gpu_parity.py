@@ -575,7 +575,8 @@ def test_document_masks(N, mean_len, window, H, Hkv, dtype):
 
 # ------------------------ long sequences: 8-wave forward and backward row passes
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("case", ["causal", "full", "window", "docs", "gqa"])
+@pytest.mark.parametrize("case", ["causal", "full", "window", "docs", "gqa", "ragged",
+                                  "ragged-full"])
 def test_wide_row_blocks_long_sequence(case):
     """From 65536 keys on, bf16 without a block mask, the forward and the
     backward row pass run 8-wave workgroups over 256-row blocks.  B1 H2 N65536:
@@ -583,10 +584,10 @@ def test_wide_row_blocks_long_sequence(case):
     each row's own definition, and dK, dV on the last 256 keys of each head
     (the causal masks: only the last rows see those keys).  The grouped-query
     case shares each key/value head between two query heads: its dK, dV are
-    the group sums."""
+    the group sums.  The ragged cases end in a partly filled 256-row block."""
     import fwd_bwd_double_amd as fbd
-    N = 65536
-    causal = case != "full"
+    N = 65536 + 77 if case.startswith("ragged") else 65536
+    causal = case not in ("full", "ragged-full")
     H, Hkv = (4, 2) if case == "gqa" else (2, 2)
     grp = H // Hkv
     w = synthetic.Workload(f"wide-{case}", 1, H, N, 64, "bf16", 9900 + len(case), causal=causal,
@@ -602,8 +603,8 @@ def test_wide_row_blocks_long_sequence(case):
     o, lse = fbd.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, window=window,
                           doc_start=ds)
     rng = np.random.default_rng(9902)
-    rows = np.sort(np.concatenate([rng.choice(np.arange(N), 252, replace=False),
-                                   [0, 255, 256, N - 1]]))
+    rows = np.sort(np.concatenate([rng.choice(np.arange(N), 250, replace=False),
+                                   [0, 255, 256, N - 78, N - 77, N - 1]]))
     rows = np.unique(rows)
     kx, vx = oracle.expand_kv(a["k"], grp), oracle.expand_kv(a["v"], grp)
     ref = oracle.rows(a["q"], kx, vx, a["do"], row_idx=rows, causal=causal, scale=w.scale,
