@@ -17,7 +17,11 @@ duration against the bf16 dense MFMA peak; `cpu_baseline` is the fp64 oracle
 timed on a bounded sample of the same workload on this host.  `extra` holds
 the B4 H12 N4096 step, the GPT-2-Small layer shape B8 H12 N1024 timed with
 the caches flushed before every kernel (HBM-bound: achieved GB/s of its
-algorithmic bytes), and the backward's time with GProj off and on.
+algorithmic bytes), the backward's time with GProj off and on, and the same
+step's outputs from the one Hessian-vector-product call (`hvp_fused`:
+attn_hvp with the BoB cotangents as the direction, whose single row pass
+finishes BoB's row outputs and the backward's dQ together), with its time and
+whether its outputs equal the separate calls'.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
                     [--no-extra] [--workload NAME]
@@ -258,6 +262,7 @@ def main():
     extra = None
     if not args.no_extra:
         extra = {"gproj_overhead": {w.name: gproj_overhead(st, 3 if w.N > 65536 else 20)}}
+        extra["hvp_fused"] = {w.name: hvp_fused(st, 3 if w.N > 65536 else 20, ms_step, rep)}
         del st
         torch.cuda.empty_cache()
         extra.update(extra_workloads(dev, w.name, extra["gproj_overhead"]))
@@ -280,6 +285,46 @@ def main():
         "per_op": rep["per_op"], "peak_mem_gb": peak_mem, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def hvp_fused(st, reps, ms_sep, rep):
+    """The same step's outputs from the one Hessian-vector-product call
+    (attn_hvp with v = the BoB cotangents, GProj on): forward, one row pass
+    that finishes BoB's row outputs and the backward's dQ together, then the
+    backward's and BoB's column passes.  Median ms of `reps` calls (HIP events
+    on the launch stream), the rate under the same FLOP convention as the
+    step, and the comparison of its outputs with the separate calls' (the
+    step just run): O, LSE, dQ, dK, dV, Hv_K, Hv_V, Hv_dO bit for bit, Hv_Q
+    as rel-L2."""
+    import numpy as np
+    import torch
+    g, f, w = st.g, st.fbd, st.w
+    ws = torch.empty(f.hvp_workspace_bytes(w.B, w.H, w.N) // 4, device=g["q"].device)
+    call = lambda: f.attn_hvp(g["q"], g["k"], g["v"], g["do"], g["g_dq"], g["g_dk"], g["g_dv"],
+                              causal=True, scale=w.scale, gproj=True, workspace=ws)
+    r = call()
+    st.run()          # the separate calls, for the comparison
+    torch.cuda.synchronize()
+    same = {k: bool(torch.equal(r[k], t)) for k, t in (
+        ("O", st.o), ("LSE", st.lse), ("dQ", st.dq), ("dK", st.dk), ("dV", st.dv),
+        ("Hv_k", st.gk), ("Hv_v", st.gv), ("Hv_do", st.gdo))}
+    dif = (r["Hv_q"].double() - st.gq.double()).norm() / st.gq.double().norm()
+    del r
+    times = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        call()
+        ev[1].record()
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]))
+    ms = float(np.median(times))
+    conv = sum(CONV[op] for op in ("fwd", "bwd", "bob")) * w.d * rep["pairs"]
+    out = {"ms": ms, "conv_tflops": conv / (ms * 1e-3) / 1e12, "separate_ms_per_step": ms_sep,
+           "speedup": ms_sep / ms, "bit_identical": same, "hv_q_rel_l2_vs_separate": float(dif)}
+    log(f"{w.name} fused HVP: {ms:.3f} ms ({out['conv_tflops']:.1f} TFLOP/s), "
+        f"{out['speedup']:.3f}x the separate calls; identical {same}; Hv_q rel-L2 {dif:.2e}")
+    return out
 
 
 def gproj_overhead(st, reps):
@@ -309,7 +354,8 @@ def gproj_overhead(st, reps):
 
 
 def extra_workloads(dev, headline, gp):
-    """The B4 H12 N4096 step (20 steps after 5 warm-ups), its GProj cost, and
+    """The B4 H12 N4096 step (20 steps after 5 warm-ups), its GProj cost, the
+    same outputs from the fused Hessian-vector-product call, and
     the GPT-2-Small layer shape B8 H12 N1024 (forward + backward) with a
     512 MiB buffer written before every kernel so that each reads its inputs
     from HBM (median of 20 steps)."""
@@ -326,6 +372,7 @@ def extra_workloads(dev, headline, gp):
         out[w.name] = rep
         gp[w.name] = gproj_overhead(st, 20)
         log(f"{w.name}: {ms:.3f} ms per step, {rep['value']:.1f} TFLOP/s")
+        rep["hvp_fused"] = hvp_fused(st, 20, ms, rep)
         del st
     w = workload("gpt2s-layer-B8H12N1024")
     x = synthetic.make_inputs(w, ("q", "k", "v", "do"))

@@ -361,12 +361,17 @@ attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, 
                          g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
+// BoB's five row states and the backward's GProj row sums r
 size_t attn_hvp_workspace_bytes(int64_t B, int64_t H, int64_t N) {
-  return attn_bob_workspace_bytes(B, H, N);
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)6 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
 size_t attn_hvp_ex_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N) {
-  return attn_bob_ex_workspace_bytes(B, H, Hkv, N);
+  if (B <= 0 || H <= 0 || N <= 0 || check_heads(H, Hkv) != ATTN_OK) return 0;
+  const size_t base = attn_hvp_workspace_bytes(B, H, N);
+  const int nsl = col_slices(B, H, Hkv, N);
+  return nsl > 1 ? round256(base) + part_bytes(B, Hkv, N, nsl) : base;
 }
 
 attn_status attn_hvp_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
@@ -383,10 +388,10 @@ attn_status attn_hvp_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
   if ((st = check_window(causal, window, &win)) != ATTN_OK) return st;
   const int ngrad = (dQ != nullptr) + (dK != nullptr) + (dV != nullptr);
   if (ngrad != 0 && ngrad != 3) return ATTN_EINVAL;
-  // the backward's row states (D, r, -LSE log2(e)) and then BoB's (D, alpha,
-  // beta, -LSE log2(e), -kappa) share the front of the workspace; the split
-  // column passes' partial sums, when the workspace holds them, follow BoB's
-  size_t need = attn_bob_workspace_bytes(B, H, N);
+  // BoB's row states (D, alpha, beta, -LSE log2(e), -kappa) and the
+  // backward's r fill the front of the workspace; the split column passes'
+  // partial sums, when the workspace holds them, follow
+  size_t need = attn_hvp_workspace_bytes(B, H, N);
   if (!ws || ws_bytes < need) return ATTN_EWORKSPACE;
   int nsl = col_slices(B, H, Hkv, N);
   const size_t poff = round256(need);
@@ -410,16 +415,34 @@ attn_status attn_hvp_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
   const size_t bhn = (size_t)B * H * N;
   float* w0 = static_cast<float*>(ws);
   float* part = nsl > 1 ? (float*)((char*)ws + poff) : nullptr;
+  float *Dw = w0, *Aw = w0 + bhn, *Bw = w0 + 2 * bhn, *Lw = w0 + 3 * bhn, *Kw = w0 + 4 * bhn,
+        *Rw = w0 + 5 * bhn;
+  const int gp = gproj ? 1 : 0;
   hipError_t e = fbd::launch_fwd((int)dt, Q, K, V, O, LSE, bh, h, grp, win, doc_start,
                                  block_mask, n, c, scale, hs);
+  if (ngrad == 3 && dt == ATTN_BF16) {
+    // bf16 with the gradient: one row pass for both (its R(dS) K and R(P) K
+    // products are the backward's dQ terms), then the two column passes
+    if (e == hipSuccess)
+      e = fbd::launch_bob_row_grad(Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_dO, dQ, Dw, Aw,
+                                   Bw, Lw, Kw, Rw, bh, h, grp, win, doc_start, block_mask, n, c,
+                                   scale, gp, hs);
+    if (e == hipSuccess)
+      e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dw, Rw, Lw, bh, h, grp, win,
+                          doc_start, block_mask, n, c, scale, gp, 2, nsl, part, hs);
+    if (e == hipSuccess)
+      e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO,
+                          Dw, Aw, Bw, Lw, Kw, bh, h, grp, win, doc_start, block_mask, n, c, scale,
+                          2, nsl, part, hs);
+    return finish(e);
+  }
   if (e == hipSuccess && ngrad == 3)
-    e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, w0, w0 + bhn, w0 + 2 * bhn, bh,
-                        h, grp, win, doc_start, block_mask, n, c, scale, gproj ? 1 : 0, 3, nsl,
-                        part, hs);
+    e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dw, Rw, Lw, bh, h, grp, win,
+                        doc_start, block_mask, n, c, scale, gp, 3, nsl, part, hs);
   if (e == hipSuccess)
-    e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, w0,
-                        w0 + bhn, w0 + 2 * bhn, w0 + 3 * bhn, w0 + 4 * bhn, bh, h, grp, win,
-                        doc_start, block_mask, n, c, scale, 3, nsl, part, hs);
+    e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, Dw,
+                        Aw, Bw, Lw, Kw, bh, h, grp, win, doc_start, block_mask, n, c, scale, 3,
+                        nsl, part, hs);
   return finish(e);
 }
 

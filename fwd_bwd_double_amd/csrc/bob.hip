@@ -25,4 +25,18 @@ hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const
 #undef FBD_BOB_ARGS
 }
 
+hipError_t launch_bob_row_grad(const void* Q, const void* K, const void* V, const void* O,
+                               const float* LSE, const void* dO, const void* gdQ, const void* gdK,
+                               const void* gdV, void* gQ, void* gdO, void* dQ, float* Dws,
+                               float* Aws, float* Bws, float* Lws, float* Kws, float* Rws, int BH,
+                               int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
+                               int causal, float scale, int gproj, hipStream_t st) {
+#define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gdO, Dws, Aws, Bws, Lws, Kws, BH, H, \
+                     grp, win, ds, bm, N, scale, dQ, Rws, gproj, st
+  if (!causal) return launch_bob_row_t<bf16, false, false, true>(FBD_BOB_ARGS);
+  return ds ? launch_bob_row_t<bf16, true, true, true>(FBD_BOB_ARGS)
+            : launch_bob_row_t<bf16, true, false, true>(FBD_BOB_ARGS);
+#undef FBD_BOB_ARGS
+}
+
 }  // namespace fbd

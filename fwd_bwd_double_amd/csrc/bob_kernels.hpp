@@ -29,6 +29,15 @@
 //   gQ = scale (XE - alpha Z - beta Y),   gdO = FG - alpha O
 // (sum_j P_ij V_j = O_i).  It writes gQ, gdO and the row states D, alpha, beta.
 //
+// Fused with the first backward's row pass (when the cotangents are known
+// before the backward runs, as in a Hessian-vector product), Z is taken over
+// R(dS) instead: since P dP = dS + D P, alpha Z moves its alpha D Y part into
+// the Y term, gQ = scale (XE - alpha Z' - kappa Y) with kappa = alpha D + beta.
+// Z' = sum_j R(dS) K and Y = sum_j R(P) K are then exactly the backward row
+// pass's two accumulators, so the same registers also give
+//   dQ = scale (Z' - r Y)  with GProj (r_i = sum_j R(dS_ij)),  scale Z' without,
+// for one row sum of the packed bf16 dS values per tile.
+//
 // Column pass (lane = key j).  K, V, Bk, C of the workgroup's keys stay in
 // registers; query blocks stream past them with their row states, and
 // gK, gV are accumulated and written once.
@@ -44,7 +53,8 @@
 
 namespace fbd {
 
-template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK>
+// EMIT: also write the first backward's dQ and its GProj row sums r (Rws)
+template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK, bool EMIT>
 __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
@@ -52,7 +62,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     T* __restrict__ gQ, T* __restrict__ gdO, float* __restrict__ Dws, float* __restrict__ Aws,
     float* __restrict__ Bws, float* __restrict__ Lws, float* __restrict__ Kws, int N, int BH,
     int H, int grp, int win, const int* __restrict__ DS, const uint8_t* __restrict__ BMK,
-    int nblk, float scale) {
+    int nblk, float scale, T* __restrict__ dQ, float* __restrict__ Rws, int gproj) {
   // two buffers as separate objects (loop unrolled by two): the copy of the
   // next tile provably never aliases the reads of the current one
   struct Buf {
@@ -91,7 +101,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
 
   f32x16 X0 = zero16(), X1 = zero16(), Y0 = zero16(), Y1 = zero16();
   f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
-  float alpha = 0.f, xsum = 0.f;
+  float alpha = 0.f, xsum = 0.f, r = 0.f;
 
   // keys of the block's rows: causal j <= i, from each row's start (sliding
   // window, document); the block's first row has the smallest start
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         alpha += pw;
         xs[v] = pv * (W * dpd + u[v]);
         xsum += xs[v];
-        zs[v] = pv * dp[v];
+        if constexpr (!EMIT) zs[v] = pv * dp[v];
         es[v] = pv * dpd;
         fs[v] = pw;
       }
@@ -175,8 +185,10 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const Frag<T> xf = pack8<T>(xs + 8 * tt), pf = pack8<T>(ps + 8 * tt);
-        const Frag<T> zf = pack8<T>(zs + 8 * tt), ef = pack8<T>(es + 8 * tt);
+        const Frag<T> ef = pack8<T>(es + 8 * tt);
+        const Frag<T> zf = EMIT ? ef : pack8<T>(zs + 8 * tt);
         const Frag<T> ff = pack8<T>(fs + 8 * tt);
+        if constexpr (EMIT) r = frag_acc_sum(ef, r);   // v_dot2 on the bf16 pairs
         {
           const Frag<T> a0 = ld_tr(Ks, 0, jt + tt, lane), a1 = ld_tr(Ks, 32, jt + tt, lane);
           mma(X0, a0, xf);
@@ -217,14 +229,36 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   alpha = half_sum(alpha);
   // b = sum_j P (W dP + U) = sum_j x + alpha D, so beta = b - 2 alpha D = sum_j x - alpha D
   xsum = half_sum(xsum);
-  const float beta = xsum - alpha * Di;
+  // beta and kappa = alpha D + beta as explicit fused multiply-adds, so that
+  // every variant of the pass rounds them alike (the column pass reads -kappa)
+  const float beta = __builtin_fmaf(-alpha, Di, xsum);
+  const float kappa = __builtin_fmaf(alpha, Di, beta);
+  const float ycoef = EMIT ? kappa : beta;   // Z over R(dS): kappa
   float out[16], ov[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - beta * Y0[v]);
+  for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - ycoef * Y0[v]);
   st_cols(gQ + hoff, N, qw, 0, lane, out);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = scale * (X1[v] - alpha * Z1[v] - beta * Y1[v]);
+  for (int v = 0; v < 16; ++v) out[v] = scale * (X1[v] - alpha * Z1[v] - ycoef * Y1[v]);
   st_cols(gQ + hoff, N, qw, 32, lane, out);
+  if constexpr (EMIT) {
+    r = half_sum(r);
+    if (gproj) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) out[v] = scale * (Z0[v] - r * Y0[v]);
+      st_cols(dQ + hoff, N, qw, 0, lane, out);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) out[v] = scale * (Z1[v] - r * Y1[v]);
+      st_cols(dQ + hoff, N, qw, 32, lane, out);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) out[v] = scale * Z0[v];
+      st_cols(dQ + hoff, N, qw, 0, lane, out);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) out[v] = scale * Z1[v];
+      st_cols(dQ + hoff, N, qw, 32, lane, out);
+    }
+  }
   ld_cols(O + hoff, N, qw, 0, lane, ov);
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = F0[v] - alpha * ov[v];
@@ -238,7 +272,8 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     Aws[soff + my_i] = alpha;
     Bws[soff + my_i] = beta;
     Lws[soff + my_i] = -lse2;
-    Kws[soff + my_i] = -(alpha * Di + beta);   // -kappa: the column pass's U starts there
+    Kws[soff + my_i] = -kappa;   // the column pass's U starts there
+    if constexpr (EMIT) Rws[soff + my_i] = r;
   }
 }
 
@@ -460,6 +495,30 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   else st_cols(pv, N, kw, 32, lane, out);
 }
 
+// Row pass (EMIT: fused with the first backward's row pass, writing dQ and r).
+template <class T, bool CAUSAL, bool DOCS, bool EMIT>
+static hipError_t launch_bob_row_t(const void* Q, const void* K, const void* V, const void* O,
+                                   const float* LSE, const void* dO, const void* gdQ,
+                                   const void* gdK, const void* gdV, void* gQ, void* gdO,
+                                   float* Dws, float* Aws, float* Bws, float* Lws, float* Kws,
+                                   int BH, int H, int grp, int win, const int* ds,
+                                   const uint8_t* bm, int N, float scale, void* dQ, float* Rws,
+                                   int gproj, hipStream_t st) {
+  // fp32 operands take twice the LDS per row: they keep the smallest tiles
+  constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32;
+  const int nblk = (N + BLK - 1) / BLK;
+  auto row = [&](auto bmask) {
+    hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS, decltype(bmask)::value, EMIT>),
+                       dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                       (const T*)O, LSE, (const T*)dO, (const T*)gdQ, (const T*)gdK,
+                       (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws, Lws, Kws, N, BH, H, grp, win,
+                       ds, bm, nblk, scale, (T*)dQ, Rws, gproj);
+  };
+  if (bm) row(std::true_type{});
+  else row(std::false_type{});
+  return hipGetLastError();
+}
+
 template <class T, bool CAUSAL, bool DOCS>
 static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
@@ -467,23 +526,12 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
                                float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
                                int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
                                float scale, int passes, int nsl, float* Part, hipStream_t st) {
-  // fp32 operands take twice the LDS per row: they keep the smallest tiles
-  constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32, BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
+  constexpr int BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
-    if (bm)
-      hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS, true>), dim3(nblk * BH), dim3(NT),
-                         0, st, (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE,
-                         (const T*)dO, (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ,
-                         (T*)gdO, Dws, Aws, Bws, Lws, Kws, N, BH, H, grp, win, ds, bm, nblk,
-                         scale);
-    else
-      hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS, false>), dim3(nblk * BH), dim3(NT),
-                         0, st, (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE,
-                         (const T*)dO, (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ,
-                         (T*)gdO, Dws, Aws, Bws, Lws, Kws, N, BH, H, grp, win, ds, bm, nblk,
-                         scale);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_bob_row_t<T, CAUSAL, DOCS, false>(
+        Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gdO, Dws, Aws, Bws, Lws, Kws, BH, H, grp, win, ds,
+        bm, N, scale, nullptr, nullptr, 0, st);
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;

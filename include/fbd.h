@@ -301,10 +301,19 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
  *      derivative of <v, (dQ, dK, dV)> with respect to dO, the term a
  *      network-level product adds through dO's own dependence on the inputs.
  * dQ, dK and dV are all NULL (gradient not computed) or all set.  Every
- * output is overwritten.  ws must hold attn_hvp_workspace_bytes(B, H, N)
- * bytes; afterwards it holds the BoB row states as after attn_bob.  Shapes,
- * layouts, ownership and errors as for attn_bob (the v_* are read-only
- * inputs); a partial set of gradient pointers is ATTN_EINVAL.
+ * output is overwritten.  With bf16 operands and the gradient requested, the
+ * backward's row pass is not run on its own: the BoB row pass takes its
+ * query-side sum over the bf16 dS values, sum_j R(dS_ij) K_j, in place of
+ * sum_j R(P_ij dP_ij) K_j (P dP = dS + D P, so the difference moves into the
+ * R(P) K term's coefficient), and those two sums are exactly the backward row
+ * pass's dQ terms; it writes dQ, then the backward's and BoB's column passes
+ * run.  dQ, dK, dV come out as attn_bwd's; H v agrees with attn_bob's within
+ * rounding.  ws must hold attn_hvp_workspace_bytes(B, H, N) bytes (six fp32
+ * values per row); afterwards it starts with the BoB row states as after
+ * attn_bob (D, alpha, beta, -LSE log2(e), -kappa), followed by the GProj row
+ * sums r when the gradient was computed.  Shapes, layouts, ownership and
+ * errors as for attn_bob (the v_* are read-only inputs); a partial set of
+ * gradient pointers is ATTN_EINVAL.
  */
 size_t attn_hvp_workspace_bytes(int64_t B, int64_t H, int64_t N);
 

@@ -121,7 +121,9 @@ def hvp_call(lib, grad=(FAKE * 11, FAKE * 12, FAKE * 13), ws_bytes=None, **kw):
 
 
 def test_hvp_rejects_bad_arguments_before_launch(lib):
-    assert fbd.hvp_workspace_bytes(2, 3, 5) == fbd.bob_workspace_bytes(2, 3, 5)
+    # BoB's five row states and the backward's r: six fp32 values per row
+    assert fbd.hvp_workspace_bytes(2, 3, 5) == 6 * 2 * 3 * 5 * 4
+    assert fbd.bob_workspace_bytes(2, 3, 5) == 5 * 2 * 3 * 5 * 4
     assert hvp_call(lib, d=32) == 2
     assert hvp_call(lib, grad=(FAKE * 11, None, FAKE * 13)) == 1     # partial gradient set
     assert hvp_call(lib, ws_bytes=fbd.hvp_workspace_bytes(1, 1, 8) - 4) == 4
@@ -136,7 +138,16 @@ def test_hvp_ex_rejects_bad_arguments_before_launch(lib):
         need = fbd.load().attn_hvp_ex_workspace_bytes(1, H, max(Hkv, 1), 8)
         return lib.attn_hvp_ex(0, 1, H, Hkv, 8, d, *p, causal, window, ds, bm, 0.125, 0, *out,
                                FAKE * 40, need if ws_bytes is None else ws_bytes, None)
-    assert lib.attn_hvp_ex_workspace_bytes(1, 4, 2, 8) == fbd.bob_ex_workspace_bytes(1, 4, 2, 8)
+    # the split column passes' partial sums follow the row states, 256-byte
+    # aligned, as in attn_bob_ex's workspace
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, H, Hkv, N in ((1, 4, 2, 8), (1, 8, 1, 4096), (3, 6, 2, 100)):
+        parts = fbd.bob_ex_workspace_bytes(B, H, Hkv, N) - fbd.bob_workspace_bytes(B, H, N)
+        want = fbd.hvp_workspace_bytes(B, H, N)
+        if parts:
+            parts = fbd.bob_ex_workspace_bytes(B, H, Hkv, N) - r256(fbd.bob_workspace_bytes(B, H, N))
+            want = r256(want) + parts
+        assert lib.attn_hvp_ex_workspace_bytes(B, H, Hkv, N) == want, (B, H, Hkv, N)
     assert lib.attn_hvp_ex_workspace_bytes(2, 3, 3, 5) == fbd.hvp_workspace_bytes(2, 3, 5)
     for H, Hkv in ((4, 3), (4, 0), (4, 8)):
         assert call(H=H, Hkv=Hkv) == 1

@@ -1,0 +1,112 @@
+"""The Hessian-vector product call with bf16 operands and the gradient
+requested runs one row pass for the first backward and BoB together: the BoB
+row pass sums R(dS) K (not R(P o dP) K) and R(P) K, which are the backward
+row pass's dQ terms.  These tests hold that call to the separate attn_fwd,
+attn_bwd and attn_bob calls on the same inputs:
+
+- O, LSE, dQ, dK and dV bit for bit (the same products over the same bf16
+  values, accumulated in the same order; the backward's column pass reads the
+  same D, r and -LSE log2(e));
+- Hv_K, Hv_V and Hv_dO bit for bit (BoB's column pass reads the same alpha
+  and kappa, and the gdO sum is unchanged);
+- Hv_Q, whose alpha term is regrouped (P dP = dS + D P), within rounding of
+  attn_bob's and within the BoB tolerance of the fp64 oracle where the oracle
+  is run.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_util import check, inputs, rel_l2, say
+from test_gpu_parity import block_masks, doc_starts
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: B, H, Hkv, N, causal, window, mean_len, density, gproj, oracle
+    "causal": (2, 3, 3, 300, True, 0, 0, 0.0, True, True),
+    "causal-no-gproj": (2, 3, 3, 300, True, 0, 0, 0.0, False, True),
+    "full": (2, 3, 3, 200, False, 0, 0, 0.0, True, True),
+    "gqa-window": (2, 4, 2, 333, True, 100, 0, 0.0, True, True),
+    "docs": (2, 4, 4, 300, True, 0, 60, 0.0, True, True),
+    "block-sparse": (2, 2, 2, 1000, True, 0, 0, 0.5, True, True),
+    # the backward's row pass takes 8-wave (256-row) blocks from N = 65536
+    # and a partly filled last block here; the fused pass keeps 128-row blocks
+    "long": (1, 2, 2, 65613, True, 0, 0, 0.0, True, False),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", list(CASES))
+def test_fused_hvp_matches_separate_calls(case):
+    import fwd_bwd_double_amd as fbd
+    B, H, Hkv, N, causal, window, mean_len, density, gproj, with_oracle = CASES[case]
+    w = synthetic.Workload(f"hvp-fused-{case}", B, H, N, 64, "bf16", 7100 + N + H + Hkv,
+                           causal=causal, qkv_std=0.5)
+    x, g, a = inputs(w)
+    for n in ("k", "v", "g_dk", "g_dv"):
+        g[n] = g[n][:, :Hkv].contiguous()
+        a[n] = a[n][:, :Hkv]
+    docs = doc_starts(B, N, 77 + N, mean_len) if mean_len else None
+    bm = block_masks(B, N, 88 + N, density, True) if density else None
+    masks = dict(window=window,
+                 doc_start=torch.from_numpy(docs.astype(np.int32)).cuda() if docs is not None else None,
+                 block_mask=torch.from_numpy(bm).cuda() if bm is not None else None)
+    say(f"[gpu] fused attn_hvp vs separate calls: {case} B={B} H={H} Hkv={Hkv} N={N} "
+        f"causal={causal} window={window} mean_len={mean_len} density={density} gproj={gproj}")
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    vq, vk, vv = g["g_dq"], g["g_dk"], g["g_dv"]
+    ws_h = torch.empty(fbd.load().attn_hvp_ex_workspace_bytes(B, H, Hkv, N) // 4, device="cuda")
+    ws_b = torch.empty(fbd.bob_ex_workspace_bytes(B, H, Hkv, N) // 4, device="cuda")
+    ws_g = torch.empty(fbd.bwd_ex_workspace_bytes(B, H, Hkv, N) // 4, device="cuda")
+    r = fbd.attn_hvp(q, k, v, do, vq, vk, vv, causal=causal, scale=w.scale, gproj=gproj,
+                     workspace=ws_h, **masks)
+    o, lse = fbd.attn_fwd(q, k, v, causal=causal, scale=w.scale, **masks)
+    dq, dk, dv = fbd.attn_bwd(q, k, v, o, lse, do, causal=causal, scale=w.scale, gproj=gproj,
+                              workspace=ws_g, **masks)
+    gq, gk, gv, gdo = fbd.attn_bob(q, k, v, o, lse, do, vq, vk, vv, causal=causal,
+                                   scale=w.scale, workspace=ws_b, **masks)
+    torch.cuda.synchronize()
+    # the fp32 row states both row passes leave behind (D, alpha, beta,
+    # -LSE log2(e), -kappa), and the backward's GProj row sums r: any rounding
+    # difference shows here, before a bf16 rounding can hide it
+    bhn = B * H * N
+    for i, name in enumerate(("D", "alpha", "beta", "-LSE log2(e)", "-kappa")):
+        same = torch.equal(ws_h[i * bhn:(i + 1) * bhn], ws_b[i * bhn:(i + 1) * bhn])
+        say(f"    row state {name}: bit-identical {same}")
+        assert same, name
+    if gproj:
+        same = torch.equal(ws_h[5 * bhn:6 * bhn], ws_g[bhn:2 * bhn])
+        say(f"    GProj row sums r: bit-identical {same}")
+        assert same, "r"
+    for name, got, ref in (("O", r["O"], o), ("LSE", r["LSE"], lse), ("dQ", r["dQ"], dq),
+                           ("dK", r["dK"], dk), ("dV", r["dV"], dv), ("Hv_k", r["Hv_k"], gk),
+                           ("Hv_v", r["Hv_v"], gv), ("Hv_do", r["Hv_do"], gdo)):
+        same = torch.equal(got, ref)
+        say(f"    {name}: bit-identical {same}")
+        assert same, name
+    f64 = synthetic.to_f64
+    # the two groupings of Hv_Q's alpha term differ by bf16 roundings of terms
+    # of Hv_Q's own size: whole-tensor rel-L2 here.  Each row's bound is taken
+    # against the oracle below; on rows with a single visible key, whose exact
+    # Hv_Q is zero, the two groupings leave different rounding residues.
+    e = rel_l2(f64(r["Hv_q"]), f64(gq))
+    say(f"    Hv_q against attn_bob: rel-L2 {e:.3e} (tol 1e-02)")
+    assert e <= 1e-2
+    if with_oracle:
+        ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                             causal=causal, window=window, docs=docs, block_mask=bm)
+        check("Hv_q against the oracle", f64(r["Hv_q"]), ref["gQ"], 5e-2)
+        check("attn_bob gQ against the oracle", f64(gq), ref["gQ"], 5e-2)
+    else:
+        # seeded rows, the first row and the last (partly filled) blocks
+        rng = np.random.default_rng(7101)
+        rows = np.unique(np.concatenate([rng.choice(np.arange(N), 250, replace=False),
+                                         [0, 1, 127, 128, N - 78, N - 1]]))
+        ref = oracle.rows(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                          row_idx=rows, causal=causal, scale=w.scale)
+        check("Hv_q rows against the oracle", f64(r["Hv_q"])[0][:, rows], ref["gQ"], 5e-2)
+        check("attn_bob gQ rows against the oracle", f64(gq)[0][:, rows], ref["gQ"], 5e-2)
+        check("dQ rows against the oracle", f64(r["dQ"])[0][:, rows], ref["dQ"], 2e-2)
