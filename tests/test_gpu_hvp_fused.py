@@ -19,19 +19,22 @@ import torch
 
 import oracle
 import synthetic
-from gpu_util import check, inputs, rel_l2, say
+from gpu_util import check, inputs, say
 from test_gpu_parity import block_masks, doc_starts
 
 pytestmark = pytest.mark.gpu
 
 CASES = {
     # name: B, H, Hkv, N, causal, window, mean_len, density, gproj, oracle
+    "one-token": (2, 3, 3, 1, True, 0, 0, 0.0, True, True),
     "causal": (2, 3, 3, 300, True, 0, 0, 0.0, True, True),
     "causal-no-gproj": (2, 3, 3, 300, True, 0, 0, 0.0, False, True),
     "full": (2, 3, 3, 200, False, 0, 0, 0.0, True, True),
     "gqa-window": (2, 4, 2, 333, True, 100, 0, 0.0, True, True),
     "docs": (2, 4, 4, 300, True, 0, 60, 0.0, True, True),
     "block-sparse": (2, 2, 2, 1000, True, 0, 0, 0.5, True, True),
+    # diagonal blocks dropped too: rows with no visible key (LSE = -inf)
+    "block-sparse-empty-rows": (1, 2, 2, 700, True, 0, 0, -0.4, True, True),
     # the backward's row pass takes 8-wave (256-row) blocks from N = 65536
     # and a partly filled last block here; the fused pass keeps 128-row blocks
     "long": (1, 2, 2, 65613, True, 0, 0, 0.0, True, False),
@@ -50,7 +53,9 @@ def test_fused_hvp_matches_separate_calls(case):
         g[n] = g[n][:, :Hkv].contiguous()
         a[n] = a[n][:, :Hkv]
     docs = doc_starts(B, N, 77 + N, mean_len) if mean_len else None
-    bm = block_masks(B, N, 88 + N, density, True) if density else None
+    # a negative density keeps each block with probability |density| and
+    # drops the diagonal blocks' guarantee
+    bm = block_masks(B, N, 88 + N, abs(density), density > 0) if density else None
     masks = dict(window=window,
                  doc_start=torch.from_numpy(docs.astype(np.int32)).cuda() if docs is not None else None,
                  block_mask=torch.from_numpy(bm).cuda() if bm is not None else None)
@@ -89,11 +94,17 @@ def test_fused_hvp_matches_separate_calls(case):
         assert same, name
     f64 = synthetic.to_f64
     # the two groupings of Hv_Q's alpha term differ by bf16 roundings of terms
-    # of Hv_Q's own size: whole-tensor rel-L2 here.  Each row's bound is taken
-    # against the oracle below; on rows with a single visible key, whose exact
-    # Hv_Q is zero, the two groupings leave different rounding residues.
-    e = rel_l2(f64(r["Hv_q"]), f64(gq))
-    say(f"    Hv_q against attn_bob: rel-L2 {e:.3e} (tol 1e-02)")
+    # of Hv_Q's own size: whole-tensor relative L2 here.  On rows with few
+    # visible keys Hv_Q is formed from much larger terms that cancel (its
+    # exact value is zero at one key), and each grouping leaves its own bf16
+    # residue there, up to about 0.07 RMS per element; the norm is therefore
+    # floored at 0.1 RMS per element, which binds only when nearly every row
+    # is such a row (N = 1).  Each row's bound is taken against the oracle
+    # below.
+    hq, gq64 = f64(r["Hv_q"]), f64(gq)
+    den = max(float(np.linalg.norm(gq64)), 0.1 * np.sqrt(gq64.size))
+    e = float(np.linalg.norm(hq - gq64)) / den
+    say(f"    Hv_q against attn_bob: relative L2 {e:.3e} (tol 1e-02)")
     assert e <= 1e-2
     if with_oracle:
         ref = oracle.bob_gqa(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
