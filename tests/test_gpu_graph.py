@@ -1,5 +1,6 @@
 """The library's calls under HIP graph capture (torch.cuda.graph): a captured
-forward, backward (GProj) and backward-over-backward, multi-head and
+forward, backward (GProj) and backward-over-backward, or the same outputs from
+one Hessian-vector-product call (its fused row pass), multi-head and
 grouped-query (split column passes, whose partial sums another kernel adds),
 replayed several times with new inputs written in between and eager work
 between the replays; every replay must equal the eager calls on the same
@@ -21,8 +22,15 @@ def step(fbd, x, Hkv):
     return [o, lse, dq, dk, dv, gq, gk, gv, gdo]
 
 
+def hvp_step(fbd, x, Hkv):
+    q, k, v, do, a, bk, c = x
+    r = fbd.attn_hvp(q, k, v, do, a, bk, c, causal=True, scale=0.125, gproj=True)
+    return [r[n] for n in ("O", "LSE", "dQ", "dK", "dV", "Hv_q", "Hv_k", "Hv_v", "Hv_do")]
+
+
+@pytest.mark.parametrize("mode", ["calls", "hvp"])
 @pytest.mark.parametrize("H,Hkv,N", [(4, 4, 700), (6, 2, 513)])
-def test_graph_replays_match_eager(H, Hkv, N):
+def test_graph_replays_match_eager(H, Hkv, N, mode):
     import fwd_bwd_double_amd as fbd
     B = 1
     gen = torch.Generator(device="cuda").manual_seed(3000 + N)
@@ -34,7 +42,8 @@ def test_graph_replays_match_eager(H, Hkv, N):
 
     x = [torch.empty(B, h, N, 64, device="cuda", dtype=torch.bfloat16) for h in shapes]
     fill(x)
-    say(f"[gpu] graph capture B={B} H={H} Hkv={Hkv} N={N}")
+    say(f"[gpu] graph capture B={B} H={H} Hkv={Hkv} N={N} mode={mode}")
+    step = globals()["hvp_step" if mode == "hvp" else "step"]
     step(fbd, x, Hkv)                                  # warm-up (library load, allocator)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
