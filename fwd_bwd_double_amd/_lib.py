@@ -79,7 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_ex.argtypes = a[:3] + [i64] + a[3:12] + [i64, vp, vp] + a[12:]
     lib.attn_bwd_ex.restype = i32
     a = lib.attn_bob.argtypes
-    lib.attn_bob_ex.argtypes = a[:3] + [i64] + a[3:15] + [i64, vp, vp] + a[15:]
+    lib.attn_bob_ex.argtypes = a[:3] + [i64] + a[3:15] + [i64, vp, vp] + a[15:16] + [i32] + a[16:]
     lib.attn_bob_ex.restype = i32
     lib.attn_hvp_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_hvp_workspace_bytes.restype = sz
@@ -287,13 +287,14 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = 
 def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
              scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, outs=None,
              passes: int = 3, window: int = 0, doc_start: Optional[torch.Tensor] = None,
-             block_mask: Optional[torch.Tensor] = None
+             block_mask: Optional[torch.Tensor] = None, gproj: bool = False
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """g_Q, g_K, g_V, g_dO: the VJP of (q, k, v, do) -> (dQ, dK, dV) with
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
     beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) afterwards; when none is
     given, grouped-query heads get one of bob_ex_workspace_bytes (split column
-    pass)."""
+    pass).  `gproj` projects the residual row sum of g_Q's bf16 key weights
+    (attn_bob_ex)."""
     lib = load()
     _check("q", q, q)
     Hkv = _kv_heads(q, k)
@@ -313,9 +314,10 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
         _check(n, t, q)
     for n, t in (("g_k", gk), ("g_v", gv)):
         _check(n, t, q, shape=kvs)
-    ext = Hkv != H or window != 0 or doc_start is not None or block_mask is not None
+    ext = (Hkv != H or window != 0 or doc_start is not None or block_mask is not None
+           or bool(gproj))
     if ext and passes != 3:
-        raise ValueError("grouped-query or masked BoB runs both passes (passes=3)")
+        raise ValueError("grouped-query, masked or projected BoB runs both passes (passes=3)")
     need = lib.attn_bob_ex_workspace_bytes(B, H, Hkv, N)
     if workspace is None:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
@@ -329,7 +331,8 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
     c = 1 if causal else 0
     if ext:
         st = lib.attn_bob_ex(_dt(q), B, H, Hkv, N, d, *ptrs, c, int(window),
-                             _docs(q, doc_start), _bmask(q, block_mask), *rest)
+                             _docs(q, doc_start), _bmask(q, block_mask), rest[0],
+                             1 if gproj else 0, *rest[1:])
     else:
         st = lib.attn_bob_passes(passes, _dt(q), B, H, N, d, *ptrs, c, *rest)
     _raise("attn_bob", st)

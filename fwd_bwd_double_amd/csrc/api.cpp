@@ -291,7 +291,7 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             const void* O, const float* LSE, const void* dO, const void* g_dQ,
                             const void* g_dK, const void* g_dV, int causal, int64_t window,
                             const int32_t* doc_start, const uint8_t* block_mask, float scale,
-                            void* g_Q, void* g_K, void* g_V, void* g_dO, void* ws,
+                            int gproj, void* g_Q, void* g_K, void* g_V, void* g_dO, void* ws,
                             size_t ws_bytes, void* stream) {
   if (passes < 1 || passes > 3) return ATTN_EINVAL;
   attn_status st = check_shape(dt, B, H, N, d, scale);
@@ -328,7 +328,7 @@ static attn_status bob_impl(int passes, attn_dtype dt, int64_t B, int64_t H, int
                                 g_dO, Dws, Aws, Bws, Lws, Kws, (int)(B * H), (int)H,
                                 (int)(H / Hkv), win, doc_start, block_mask, (int)N,
                                 causal ? 1 : 0, scale, passes, nsl,
-                                nsl > 1 ? (float*)((char*)ws + poff) : nullptr,
+                                nsl > 1 ? (float*)((char*)ws + poff) : nullptr, gproj ? 1 : 0,
                                 (hipStream_t)stream));
 }
 
@@ -338,7 +338,7 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
                             const void* g_dV, int causal, float scale, void* g_Q, void* g_K,
                             void* g_V, void* g_dO, void* ws, size_t ws_bytes, void* stream) {
   return bob_impl(passes, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, 0,
-                  nullptr, nullptr, scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
+                  nullptr, nullptr, scale, 0, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
 attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
@@ -346,10 +346,10 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
                         const float* LSE, const void* dO, const void* g_dQ, const void* g_dK,
                         const void* g_dV, int causal, int64_t window,
                         const int32_t* doc_start, const uint8_t* block_mask, float scale,
-                        void* g_Q, void* g_K, void* g_V, void* g_dO, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        int gproj, void* g_Q, void* g_K, void* g_V, void* g_dO, void* ws,
+                        size_t ws_bytes, void* stream) {
   return bob_impl(3, dt, B, H, Hkv, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, window,
-                  doc_start, block_mask, scale, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
+                  doc_start, block_mask, scale, gproj, g_Q, g_K, g_V, g_dO, ws, ws_bytes, stream);
 }
 
 attn_status attn_bob(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d, const void* Q,
@@ -426,14 +426,14 @@ attn_status attn_hvp_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
     if (e == hipSuccess)
       e = fbd::launch_bob_row_grad(Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_dO, dQ, Dw, Aw,
                                    Bw, Lw, Kw, Rw, bh, h, grp, win, doc_start, block_mask, n, c,
-                                   scale, gp, hs);
+                                   scale, gp, gp, hs);
     if (e == hipSuccess)
       e = fbd::launch_bwd((int)dt, Q, K, V, O, LSE, dO, dQ, dK, dV, Dw, Rw, Lw, bh, h, grp, win,
                           doc_start, block_mask, n, c, scale, gp, 2, nsl, part, hs);
     if (e == hipSuccess)
       e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO,
                           Dw, Aw, Bw, Lw, Kw, bh, h, grp, win, doc_start, block_mask, n, c, scale,
-                          2, nsl, part, hs);
+                          2, nsl, part, gp, hs);
     return finish(e);
   }
   if (e == hipSuccess && ngrad == 3)
@@ -442,7 +442,7 @@ attn_status attn_hvp_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
   if (e == hipSuccess)
     e = fbd::launch_bob((int)dt, Q, K, V, O, LSE, dO, v_Q, v_K, v_V, Hv_Q, Hv_K, Hv_V, Hv_dO, Dw,
                         Aw, Bw, Lw, Kw, bh, h, grp, win, doc_start, block_mask, n, c, scale, 3,
-                        nsl, part, hs);
+                        nsl, part, gp, hs);
   return finish(e);
 }
 
@@ -615,6 +615,6 @@ extern "C" attn_status attn_bob_noalloc(attn_dtype dt, int64_t B, int64_t H, int
   // attn_bob_workspace_bytes; every row state is written by the row pass
   // before the column pass reads it, so nothing needs clearing
   return bob_impl(3, dt, B, H, H, N, d, Q, K, V, O, LSE, dO, g_dQ, g_dK, g_dV, causal, 0,
-                  nullptr, nullptr, scale, g_Q, g_K, g_V, g_dO, ws,
+                  nullptr, nullptr, scale, 0, g_Q, g_K, g_V, g_dO, ws,
                   attn_bob_workspace_bytes(B, H, N), stream);
 }

@@ -11,7 +11,7 @@ hipError_t launch_bob_f32(const void* Q, const void* K, const void* V, const voi
                           int win, const int* ds, const uint8_t* bm, int N, int causal,
                           float scale, int passes, int nsl, float* Part, hipStream_t st) {
 #define FBD_BOB_ARGS Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gK, gV, gdO, Dws, Aws, Bws, Lws, Kws, \
-                     BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, st
+                     BH, H, grp, win, ds, bm, N, scale, passes, nsl, Part, 0, st
   if (!causal) return launch_bob_t<float, false, false>(FBD_BOB_ARGS);
   return ds ? launch_bob_t<float, true, true>(FBD_BOB_ARGS)
             : launch_bob_t<float, true, false>(FBD_BOB_ARGS);

@@ -38,6 +38,19 @@
 //   dQ = scale (Z' - r Y)  with GProj (r_i = sum_j R(dS_ij)),  scale Z' without,
 // for one row sum of the packed bf16 dS values per tile.
 //
+// GProj for g_Q (PROJ; the GProj page's projection, section "How a zero sum
+// turns into a false gradient", carried over to this pass).  The K-side
+// weights of g_Q, Sh = P (W (dP - D) + U) - alpha P dP - beta P, sum to
+// exactly zero over a row (sum_j P dP = D, sum_j P = 1), but the pass feeds
+// their three parts to the matrix cores as separate bf16 operands and
+// combines them after the sums; the residual row sum of those operands,
+//   r_Sh = sum R(x) - alpha sum R(P dP) - beta sum R(P)
+// (R(dS) and kappa in place of R(P dP) and beta when fused), carries a false
+// multiple of the keys' mean into g_Q, large when the keys share a large mean
+// and rows are near one-hot.  With PROJ it is removed along R(P) K:
+//   g_Q = scale (XE - alpha Z - (beta + r_Sh) Y),
+// three (fused: two more) v_dot2 row sums over operands the pass packs anyway.
+//
 // Column pass (lane = key j).  K, V, Bk, C of the workgroup's keys stay in
 // registers; query blocks stream past them with their row states, and
 // gK, gV are accumulated and written once.
@@ -53,8 +66,9 @@
 
 namespace fbd {
 
-// EMIT: also write the first backward's dQ and its GProj row sums r (Rws)
-template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK, bool EMIT>
+// EMIT: also write the first backward's dQ and its GProj row sums r (Rws);
+// PROJ: project the residual row sum of g_Q's K-side weights (above)
+template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK, bool EMIT, bool PROJ>
 __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
@@ -102,6 +116,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   f32x16 X0 = zero16(), X1 = zero16(), Y0 = zero16(), Y1 = zero16();
   f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
   float alpha = 0.f, xsum = 0.f, r = 0.f;
+  float sx = 0.f, sz = 0.f, sp = 0.f;   // row sums of the bf16 operands (PROJ)
 
   // keys of the block's rows: causal j <= i, from each row's start (sliding
   // window, document); the block's first row has the smallest start
@@ -189,6 +204,11 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         const Frag<T> zf = EMIT ? ef : pack8<T>(zs + 8 * tt);
         const Frag<T> ff = pack8<T>(fs + 8 * tt);
         if constexpr (EMIT) r = frag_acc_sum(ef, r);   // v_dot2 on the bf16 pairs
+        if constexpr (PROJ) {
+          sx = frag_acc_sum(xf, sx);
+          sp = frag_acc_sum(pf, sp);
+          if constexpr (!EMIT) sz = frag_acc_sum(zf, sz);
+        }
         {
           const Frag<T> a0 = ld_tr(Ks, 0, jt + tt, lane), a1 = ld_tr(Ks, 32, jt + tt, lane);
           mma(X0, a0, xf);
@@ -233,7 +253,10 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   // every variant of the pass rounds them alike (the column pass reads -kappa)
   const float beta = __builtin_fmaf(-alpha, Di, xsum);
   const float kappa = __builtin_fmaf(alpha, Di, beta);
-  const float ycoef = EMIT ? kappa : beta;   // Z over R(dS): kappa
+  if constexpr (EMIT) r = half_sum(r);
+  float ycoef = EMIT ? kappa : beta;   // Z over R(dS): kappa
+  if constexpr (PROJ)
+    ycoef += half_sum(sx) - alpha * (EMIT ? r : half_sum(sz)) - ycoef * half_sum(sp);
   float out[16], ov[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - ycoef * Y0[v]);
@@ -242,7 +265,6 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   for (int v = 0; v < 16; ++v) out[v] = scale * (X1[v] - alpha * Z1[v] - ycoef * Y1[v]);
   st_cols(gQ + hoff, N, qw, 32, lane, out);
   if constexpr (EMIT) {
-    r = half_sum(r);
     if (gproj) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) out[v] = scale * (Z0[v] - r * Y0[v]);
@@ -495,7 +517,8 @@ __global__ __launch_bounds__(NT, FBD_BOB_COL_OCC) void bob_col_kernel(
   else st_cols(pv, N, kw, 32, lane, out);
 }
 
-// Row pass (EMIT: fused with the first backward's row pass, writing dQ and r).
+// Row pass (EMIT: fused with the first backward's row pass, writing dQ and r;
+// proj: the g_Q projection, bf16 only: fp32 operands are not rounded).
 template <class T, bool CAUSAL, bool DOCS, bool EMIT>
 static hipError_t launch_bob_row_t(const void* Q, const void* K, const void* V, const void* O,
                                    const float* LSE, const void* dO, const void* gdQ,
@@ -503,19 +526,28 @@ static hipError_t launch_bob_row_t(const void* Q, const void* K, const void* V, 
                                    float* Dws, float* Aws, float* Bws, float* Lws, float* Kws,
                                    int BH, int H, int grp, int win, const int* ds,
                                    const uint8_t* bm, int N, float scale, void* dQ, float* Rws,
-                                   int gproj, hipStream_t st) {
+                                   int gproj, int proj, hipStream_t st) {
   // fp32 operands take twice the LDS per row: they keep the smallest tiles
   constexpr int BN = sizeof(T) == 2 ? FBD_BOB_BN : 32;
   const int nblk = (N + BLK - 1) / BLK;
-  auto row = [&](auto bmask) {
-    hipLaunchKernelGGL((bob_row_kernel<T, BN, CAUSAL, DOCS, decltype(bmask)::value, EMIT>),
-                       dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const T*)O, LSE, (const T*)dO, (const T*)gdQ, (const T*)gdK,
-                       (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws, Lws, Kws, N, BH, H, grp, win,
-                       ds, bm, nblk, scale, (T*)dQ, Rws, gproj);
+  auto row = [&](auto bmask, auto pj) {
+    hipLaunchKernelGGL(
+        (bob_row_kernel<T, BN, CAUSAL, DOCS, decltype(bmask)::value, EMIT, decltype(pj)::value>),
+        dim3(nblk * BH), dim3(NT), 0, st, (const T*)Q, (const T*)K, (const T*)V, (const T*)O, LSE,
+        (const T*)dO, (const T*)gdQ, (const T*)gdK, (const T*)gdV, (T*)gQ, (T*)gdO, Dws, Aws, Bws,
+        Lws, Kws, N, BH, H, grp, win, ds, bm, nblk, scale, (T*)dQ, Rws, gproj);
   };
-  if (bm) row(std::true_type{});
-  else row(std::false_type{});
+  using Y = std::true_type;
+  using F = std::false_type;
+  if (sizeof(T) == 2 && proj) {
+    if constexpr (sizeof(T) == 2) {
+      if (bm) row(Y{}, Y{});
+      else row(F{}, Y{});
+    }
+  } else {
+    if (bm) row(Y{}, F{});
+    else row(F{}, F{});
+  }
   return hipGetLastError();
 }
 
@@ -525,13 +557,14 @@ static hipError_t launch_bob_t(const void* Q, const void* K, const void* V, cons
                                const void* gdV, void* gQ, void* gK, void* gV, void* gdO,
                                float* Dws, float* Aws, float* Bws, float* Lws, float* Kws, int BH,
                                int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
-                               float scale, int passes, int nsl, float* Part, hipStream_t st) {
+                               float scale, int passes, int nsl, float* Part, int proj,
+                               hipStream_t st) {
   constexpr int BM = sizeof(T) == 2 ? FBD_BOB_BM : 64;
   const int nblk = (N + BLK - 1) / BLK;
   if (passes & 1) {
     hipError_t e = launch_bob_row_t<T, CAUSAL, DOCS, false>(
         Q, K, V, O, LSE, dO, gdQ, gdK, gdV, gQ, gdO, Dws, Aws, Bws, Lws, Kws, BH, H, grp, win, ds,
-        bm, N, scale, nullptr, nullptr, 0, st);
+        bm, N, scale, nullptr, nullptr, 0, proj, st);
     if (e != hipSuccess) return e;
   }
   if (!(passes & 2)) return hipSuccess;

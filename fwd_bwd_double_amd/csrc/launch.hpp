@@ -97,24 +97,26 @@ hipError_t launch_bwd(int dt, const void* Q, const void* K, const void* V, const
                       int nsl, float* Part, hipStream_t st);
 
 // BoB workspace: D, alpha, beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) per row.
+// proj != 0 projects g_Q's residual row sum (bf16 operands only).
 hipError_t launch_bob(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                       const void* gdV, void* gQ, void* gK, void* gV, void* gdO, float* Dws,
                       float* Aws, float* Bws, float* Lws, float* Kws, int BH, int H, int grp,
                       int win, const int* ds, const uint8_t* bm, int N, int causal, float scale,
-                      int passes, int nsl, float* Part, hipStream_t st);
+                      int passes, int nsl, float* Part, int proj, hipStream_t st);
 
 // BoB's row pass fused with the first backward's row pass, for bf16 operands
 // whose BoB cotangents are known before the backward runs (a Hessian-vector
 // product): the row pass of launch_bob, which also writes the backward's dQ
 // (with GProj when gproj != 0) and the GProj row sums r into Rws.  Dws and Lws
-// are then the backward column pass's D and -LSE*log2(e), Rws its r.
+// are then the backward column pass's D and -LSE*log2(e), Rws its r; proj as
+// for launch_bob.
 hipError_t launch_bob_row_grad(const void* Q, const void* K, const void* V, const void* O,
                                const float* LSE, const void* dO, const void* gdQ, const void* gdK,
                                const void* gdV, void* gQ, void* gdO, void* dQ, float* Dws,
                                float* Aws, float* Bws, float* Lws, float* Kws, float* Rws, int BH,
                                int H, int grp, int win, const int* ds, const uint8_t* bm, int N,
-                               int causal, float scale, int gproj, hipStream_t st);
+                               int causal, float scale, int gproj, int proj, hipStream_t st);
 
 // The fp32 half of launch_bob (same arguments, dt implied).
 hipError_t launch_bob_f32(const void* Q, const void* K, const void* V, const void* O,

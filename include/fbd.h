@@ -246,8 +246,23 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
  * LSE = -infinity and zero gradients and BoB outputs (the oracle's
  * convention for an empty softmax row).
  *
- * With Hkv == H, window == 0, no doc_start and no block_mask these equal
- * attn_fwd / attn_bwd / attn_bob.  Hkv outside the range above, window < 0 or
+ * gproj != 0 in attn_bob_ex carries GProj (GProj page, section "How a zero
+ * sum turns into a false gradient") over to g_Q.  The weights of K in g_Q,
+ *   Sh = P o (W o (dP - D) + U) - alpha P o dP - beta P,
+ * sum to exactly zero over each row, but the row pass sends their three
+ * parts to the matrix cores as separate bf16 operands and combines them after
+ * the sums over keys; the residual row sum r_Sh of those operands (taken over
+ * exactly the bf16 values) would carry a false multiple of the keys' mean into
+ * g_Q, large where the keys share a large mean and rows are near one-hot (the
+ * GProj page's large-key regime).  With gproj it is removed along R(P) K:
+ *   g_Q = scale * (sum_j R(x) K + R(dS) B_K - alpha sum_j R(P o dP) K
+ *                  - (beta + r_Sh) sum_j R(P) K).
+ * It changes g_Q only, costs three row sums per tile of the row pass, and has
+ * no effect on fp32 operands (nothing is rounded there); exact arithmetic
+ * gives r_Sh = 0.
+ *
+ * With Hkv == H, window == 0, no doc_start, no block_mask and gproj == 0 these
+ * equal attn_fwd / attn_bwd / attn_bob.  Hkv outside the range above, window < 0 or
  * a doc_start or block_mask that overlaps an output is ATTN_EINVAL; a
  * misaligned doc_start is ATTN_EALIGN;
  * window > 0 or doc_start with causal == 0 is ATTN_EUNSUPPORTED; other
@@ -281,7 +296,7 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
                         const float* LSE, const void* dO,
                         const void* g_dQ, const void* g_dK, const void* g_dV,
                         int causal, int64_t window, const int32_t* doc_start,
-                        const uint8_t* block_mask, float scale,
+                        const uint8_t* block_mask, float scale, int gproj,
                         void* g_Q, void* g_K, void* g_V, void* g_dO,
                         void* ws, size_t ws_bytes, void* stream);
 
@@ -297,7 +312,7 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
  * One call runs
  *   attn_fwd                 -> O, LSE
  *   attn_bwd (if dQ != NULL) -> dQ, dK, dV   (GProj when gproj != 0)
- *   attn_bob                 -> Hv_Q, Hv_K, Hv_V = H v, and Hv_dO = the
+ *   attn_bob_ex              -> Hv_Q, Hv_K, Hv_V = H v, and Hv_dO = the
  *      derivative of <v, (dQ, dK, dV)> with respect to dO, the term a
  *      network-level product adds through dO's own dependence on the inputs.
  * dQ, dK and dV are all NULL (gradient not computed) or all set.  Every
@@ -307,8 +322,10 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
  * sum_j R(P_ij dP_ij) K_j (P dP = dS + D P, so the difference moves into the
  * R(P) K term's coefficient), and those two sums are exactly the backward row
  * pass's dQ terms; it writes dQ, then the backward's and BoB's column passes
- * run.  dQ, dK, dV come out as attn_bwd's; H v agrees with attn_bob's within
- * rounding.  ws must hold attn_hvp_workspace_bytes(B, H, N) bytes (six fp32
+ * run.  dQ, dK, dV come out as attn_bwd's; H v agrees with attn_bob_ex's
+ * within rounding.  gproj != 0 also applies attn_bob_ex's projection of
+ * Hv_Q's residual row sum (the same flag as attn_bob_ex's gproj; with the
+ * fused row pass its residual is taken over R(dS) and kappa).  ws must hold attn_hvp_workspace_bytes(B, H, N) bytes (six fp32
  * values per row); afterwards it starts with the BoB row states as after
  * attn_bob (D, alpha, beta, -LSE log2(e), -kappa), followed by the GProj row
  * sums r when the gradient was computed.  Shapes, layouts, ownership and

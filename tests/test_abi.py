@@ -263,3 +263,42 @@ def test_bob_noalloc_rejects_bad_arguments_before_any_device_call(lib):
     assert call(ptrs=p[:9] + [p[0]] + p[10:]) == 1  # output aliases an input
     assert call(dt=5) == 2
     assert call(N=0) == 1
+
+
+def declared_parameter_counts():
+    """Number of parameters of every function include/fbd.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(attn_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else len(params.split(","))
+    return out
+
+
+def test_binding_argument_counts_match_the_header(lib):
+    # every function the binding gives a signature must take exactly the
+    # header's number of parameters (a stale ctypes list would shift every
+    # argument after the first difference)
+    counts = declared_parameter_counts()
+    checked = 0
+    for name, n in counts.items():
+        argtypes = getattr(getattr(lib, name), "argtypes", None)
+        if argtypes is None:
+            continue
+        assert len(argtypes) == n, (name, len(argtypes), n)
+        checked += 1
+    assert checked >= 20, checked
+
+
+def test_bob_ex_rejects_bad_arguments_before_launch(lib):
+    # Q K V O LSE dO gdQ gdK gdV, then gQ gK gV gdO, then ws
+    p = [FAKE * (i + 1) for i in range(9)]
+    out = [FAKE * (20 + i) for i in range(4)]
+    def call(H=4, Hkv=2, causal=1, window=0, gproj=1, d=64, ws_bytes=None):
+        need = lib.attn_bob_ex_workspace_bytes(1, H, max(Hkv, 1), 8)
+        return lib.attn_bob_ex(0, 1, H, Hkv, 8, d, *p, causal, window, None, None, 0.125, gproj,
+                               *out, FAKE * 40, need if ws_bytes is None else ws_bytes, None)
+    assert call(d=32) == 2
+    assert call(H=4, Hkv=3) == 1
+    assert call(causal=0, window=4) == 2
+    assert call(ws_bytes=fbd.bob_workspace_bytes(1, 4, 8) - 4) == 4

@@ -33,7 +33,9 @@ def oracle_backed(monkeypatch):
         return tuple(torch.from_numpy(r[n]) for n in ("dQ", "dK", "dV"))
 
     def bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal=True, scale=None, workspace=None,
-            outs=None, passes=3, window=0, doc_start=None, block_mask=None):
+            outs=None, passes=3, window=0, doc_start=None, block_mask=None, gproj=False):
+        # (the projections only remove bf16 rounding residuals: exact
+        # arithmetic needs none)
         r = oracle.bob_gqa(_np(q), _np(k), _np(v), _np(do), _np(g_dq), _np(g_dk), _np(g_dv),
                            causal=causal, scale=scale, window=window, docs=_np(doc_start),
                            block_mask=_np(block_mask))

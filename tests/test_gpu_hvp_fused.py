@@ -10,7 +10,8 @@ attn_bwd and attn_bob calls on the same inputs:
 - Hv_K, Hv_V and Hv_dO bit for bit (BoB's column pass reads the same alpha
   and kappa, and the gdO sum is unchanged);
 - Hv_Q, whose alpha term is regrouped (P dP = dS + D P), within rounding of
-  attn_bob's and within the BoB tolerance of the fp64 oracle where the oracle
+  attn_bob's (both with the same gproj, which also projects g_Q's residual
+  row sum) and within the BoB tolerance of the fp64 oracle where the oracle
   is run.
 """
 import numpy as np
@@ -72,7 +73,7 @@ def test_fused_hvp_matches_separate_calls(case):
     dq, dk, dv = fbd.attn_bwd(q, k, v, o, lse, do, causal=causal, scale=w.scale, gproj=gproj,
                               workspace=ws_g, **masks)
     gq, gk, gv, gdo = fbd.attn_bob(q, k, v, o, lse, do, vq, vk, vv, causal=causal,
-                                   scale=w.scale, workspace=ws_b, **masks)
+                                   scale=w.scale, workspace=ws_b, gproj=gproj, **masks)
     torch.cuda.synchronize()
     # the fp32 row states both row passes leave behind (D, alpha, beta,
     # -LSE log2(e), -kappa), and the backward's GProj row sums r: any rounding
@@ -121,3 +122,67 @@ def test_fused_hvp_matches_separate_calls(case):
         check("Hv_q rows against the oracle", f64(r["Hv_q"])[0][:, rows], ref["gQ"], 5e-2)
         check("attn_bob gQ rows against the oracle", f64(gq)[0][:, rows], ref["gQ"], 5e-2)
         check("dQ rows against the oracle", f64(r["dQ"])[0][:, rows], ref["dQ"], 2e-2)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("tau_key", ["tau", "tau_strict"])
+def test_gproj_projection_of_bob_gq_in_the_large_key_regime(tau_key):
+    """The large-key regime (keys shifted by one shared vector of norm 8,
+    queries scaled by the power of two that makes most rows near one-hot,
+    from the committed oracle fixture), B1 H2 N1024 against the fp64 oracle on
+    full tensors.  There g_Q is formed from large terms that nearly cancel, and
+    the residual row sum of its bf16 key weights carries a false multiple of
+    the keys' large mean into it (the GProj page's mechanism, in BoB's row
+    pass).  Asserted:
+      * with the projection (attn_bob with gproj, and attn_hvp with gproj,
+        whose fused pass takes its weights over R(dS)): g_Q within the BoB
+        bound of the oracle, row by row;
+      * without it (attn_bob): the worst row at least 3 times further off;
+      * the fused call's other outputs bit for bit equal to the separate
+        calls'; g_K, g_V, g_dO within the BoB bound as whole tensors (their
+        worst rows are printed: the column pass rounds each weight once, so
+        this mechanism does not reach them)."""
+    import json
+    import os
+    import fwd_bwd_double_amd as fbd
+    from gpu_util import rel_l2, row_errors
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "large_key_tau.json")))
+    w = synthetic.Workload(f"bob-large-key-{tau_key}", 1, 2, 1024, 64, "bf16", 7300,
+                           qkv_std=1.0, do_std=1.0, cot_std=1.0, mean_norm=8.0,
+                           tau=float(gold[tau_key]))
+    x, g, a = inputs(w)
+    say(f"[gpu] BoB g_Q projection, large-key regime: tau={w.tau} B1 H2 N1024")
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    vq, vk, vv = g["g_dq"], g["g_dk"], g["g_dv"]
+    r = fbd.attn_hvp(q, k, v, do, vq, vk, vv, causal=True, scale=w.scale, gproj=True)
+    o, lse = fbd.attn_fwd(q, k, v, causal=True, scale=w.scale)
+    dq, dk, dv = fbd.attn_bwd(q, k, v, o, lse, do, causal=True, scale=w.scale, gproj=True)
+    gq, gk, gv, gdo = fbd.attn_bob(q, k, v, o, lse, do, vq, vk, vv, causal=True,
+                                   scale=w.scale, gproj=True)
+    gq0, gk0, gv0, gdo0 = fbd.attn_bob(q, k, v, o, lse, do, vq, vk, vv, causal=True,
+                                       scale=w.scale)
+    torch.cuda.synchronize()
+    for name, got, ref in (("O", r["O"], o), ("LSE", r["LSE"], lse), ("dQ", r["dQ"], dq),
+                           ("dK", r["dK"], dk), ("dV", r["dV"], dv), ("Hv_k", r["Hv_k"], gk),
+                           ("Hv_v", r["Hv_v"], gv), ("Hv_do", r["Hv_do"], gdo),
+                           ("g_K without projection", gk0, gk), ("g_V", gv0, gv),
+                           ("g_dO", gdo0, gdo)):
+        assert torch.equal(got, ref), name
+    say("    the projection changes g_Q only; the fused call's other outputs equal the "
+        "separate calls' bit for bit")
+    f64 = synthetic.to_f64
+    ref = oracle.bob(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
+                     causal=True, scale=w.scale)
+    check("Hv_q (fused, projected) against the oracle", f64(r["Hv_q"]), ref["gQ"], 5e-2)
+    check("attn_bob g_Q (projected) against the oracle", f64(gq), ref["gQ"], 5e-2)
+    w0 = float(row_errors(f64(gq0), ref["gQ"]).max())
+    w1 = float(row_errors(f64(gq), ref["gQ"]).max())
+    say(f"    attn_bob g_Q without the projection: rel-L2 {rel_l2(f64(gq0), ref['gQ']):.3e}, "
+        f"worst row {w0:.3e} ({w0 / w1:.1f} x the projected)")
+    assert w0 >= 3 * w1, (w0, w1)
+    for key, got in (("g_K", gk), ("g_V", gv), ("g_dO", gdo)):
+        e = rel_l2(f64(got), ref[key[0] + key[2:]])
+        say(f"    {key}: rel-L2 {e:.3e} (tol 5e-02), worst row "
+            f"{float(row_errors(f64(got), ref[key[0] + key[2:]]).max()):.3e}")
+        assert e <= 5e-2, key
