@@ -293,8 +293,8 @@ def attn_bob(q, k, v, o, lse, do, g_dq, g_dk, g_dv, causal: bool = True,
     cotangents (g_dq, g_dk, g_dv).  `workspace` holds the row states D, alpha,
     beta, -LSE*log2(e) and -kappa = -(alpha*D + beta) afterwards; when none is
     given, grouped-query heads get one of bob_ex_workspace_bytes (split column
-    pass).  `gproj` projects the residual row sum of g_Q's bf16 key weights
-    (attn_bob_ex)."""
+    pass).  `gproj` projects the residual row sums of g_Q's bf16 key weights
+    and g_dO's value weights (attn_bob_ex)."""
     lib = load()
     _check("q", q, q)
     Hkv = _kv_heads(q, k)

@@ -91,8 +91,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     """O = softmax(scale q k^T + mask) v for q (B, H, N, 64) and k, v (B, Hkv,
     N, 64), bf16 or fp32 on the GPU, differentiable twice through the
     library's kernels (first backward: `attn_bwd`, with GProj when `gproj`;
-    second: `attn_bob`, which then also projects the residual row sum of g_Q's
-    bf16 key weights).  The masks are those of `attn_fwd`.  With
+    second: `attn_bob`, which then also projects the residual row sums of
+    g_Q's and g_dO's bf16 weights).  The masks are those of `attn_fwd`.  With
     `return_lse`, the row log-sum-exp is returned too (not differentiable)."""
     opts = dict(causal=causal, scale=scale, gproj=gproj, window=int(window),
                 doc_start=doc_start, block_mask=block_mask)

@@ -48,8 +48,11 @@
 // (R(dS) and kappa in place of R(P dP) and beta when fused), carries a false
 // multiple of the keys' mean into g_Q, large when the keys share a large mean
 // and rows are near one-hot.  With PROJ it is removed along R(P) K:
-//   g_Q = scale (XE - alpha Z - (beta + r_Sh) Y),
-// three (fused: two more) v_dot2 row sums over operands the pass packs anyway.
+//   g_Q = scale (XE - alpha Z - (beta + r_Sh) Y).
+// g_dO's weights of V, P (W - alpha), sum to zero over a row as well; the pass
+// forms g_dO = sum R(P W) V + R(P) C - alpha O, so their residual is
+// r_H = sum R(P W) - alpha, removed along O:  g_dO = FG - (alpha + r_H) O.
+// Four (fused: three more) v_dot2 row sums over operands the pass packs anyway.
 //
 // Column pass (lane = key j).  K, V, Bk, C of the workgroup's keys stay in
 // registers; query blocks stream past them with their row states, and
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   f32x16 X0 = zero16(), X1 = zero16(), Y0 = zero16(), Y1 = zero16();
   f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
   float alpha = 0.f, xsum = 0.f, r = 0.f;
-  float sx = 0.f, sz = 0.f, sp = 0.f;   // row sums of the bf16 operands (PROJ)
+  float sx = 0.f, sz = 0.f, sp = 0.f, sf = 0.f;   // row sums of the bf16 operands (PROJ)
 
   // keys of the block's rows: causal j <= i, from each row's start (sliding
   // window, document); the block's first row has the smallest start
@@ -207,6 +210,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         if constexpr (PROJ) {
           sx = frag_acc_sum(xf, sx);
           sp = frag_acc_sum(pf, sp);
+          sf = frag_acc_sum(ff, sf);
           if constexpr (!EMIT) sz = frag_acc_sum(zf, sz);
         }
         {
@@ -255,8 +259,11 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   const float kappa = __builtin_fmaf(alpha, Di, beta);
   if constexpr (EMIT) r = half_sum(r);
   float ycoef = EMIT ? kappa : beta;   // Z over R(dS): kappa
-  if constexpr (PROJ)
+  float ocoef = alpha;                 // coefficient of O in g_dO
+  if constexpr (PROJ) {
     ycoef += half_sum(sx) - alpha * (EMIT ? r : half_sum(sz)) - ycoef * half_sum(sp);
+    ocoef = half_sum(sf);               // alpha + r_H
+  }
   float out[16], ov[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[v] = scale * (X0[v] - alpha * Z0[v] - ycoef * Y0[v]);
@@ -283,11 +290,11 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   }
   ld_cols(O + hoff, N, qw, 0, lane, ov);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = F0[v] - alpha * ov[v];
+  for (int v = 0; v < 16; ++v) out[v] = F0[v] - ocoef * ov[v];
   st_cols(gdO + hoff, N, qw, 0, lane, out);
   ld_cols(O + hoff, N, qw, 32, lane, ov);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) out[v] = F1[v] - alpha * ov[v];
+  for (int v = 0; v < 16; ++v) out[v] = F1[v] - ocoef * ov[v];
   st_cols(gdO + hoff, N, qw, 32, lane, out);
   if (h == 0 && my_i < N) {
     Dws[soff + my_i] = Di;

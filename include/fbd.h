@@ -257,9 +257,13 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
  * GProj page's large-key regime).  With gproj it is removed along R(P) K:
  *   g_Q = scale * (sum_j R(x) K + R(dS) B_K - alpha sum_j R(P o dP) K
  *                  - (beta + r_Sh) sum_j R(P) K).
- * It changes g_Q only, costs three row sums per tile of the row pass, and has
- * no effect on fp32 operands (nothing is rounded there); exact arithmetic
- * gives r_Sh = 0.
+ * g_dO's weights of V, P o (W - alpha), also sum to zero over each row; the
+ * pass forms g_dO = sum_j R(P o W) V + R(P) C - alpha O, and with gproj their
+ * residual r_H = sum_j R(P o W) - alpha is removed along O:
+ *   g_dO = sum_j R(P o W) V + R(P) C - (alpha + r_H) O.
+ * It changes g_Q and g_dO only, costs four row sums per tile of the row pass,
+ * and has no effect on fp32 operands (nothing is rounded there); exact
+ * arithmetic gives r_Sh = r_H = 0.
  *
  * With Hkv == H, window == 0, no doc_start, no block_mask and gproj == 0 these
  * equal attn_fwd / attn_bwd / attn_bob.  Hkv outside the range above, window < 0 or
@@ -323,9 +327,10 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
  * R(P) K term's coefficient), and those two sums are exactly the backward row
  * pass's dQ terms; it writes dQ, then the backward's and BoB's column passes
  * run.  dQ, dK, dV come out as attn_bwd's; H v agrees with attn_bob_ex's
- * within rounding.  gproj != 0 also applies attn_bob_ex's projection of
- * Hv_Q's residual row sum (the same flag as attn_bob_ex's gproj; with the
- * fused row pass its residual is taken over R(dS) and kappa).  ws must hold attn_hvp_workspace_bytes(B, H, N) bytes (six fp32
+ * within rounding.  gproj != 0 also applies attn_bob_ex's projections of
+ * Hv_Q's and Hv_dO's residual row sums (the same flag as attn_bob_ex's gproj;
+ * with the fused row pass Hv_Q's residual is taken over R(dS) and kappa).
+ * ws must hold attn_hvp_workspace_bytes(B, H, N) bytes (six fp32
  * values per row); afterwards it starts with the BoB row states as after
  * attn_bob (D, alpha, beta, -LSE log2(e), -kappa), followed by the GProj row
  * sums r when the gradient was computed.  Shapes, layouts, ownership and

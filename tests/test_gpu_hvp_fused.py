@@ -133,15 +133,16 @@ def test_gproj_projection_of_bob_gq_in_the_large_key_regime(tau_key):
     full tensors.  There g_Q is formed from large terms that nearly cancel, and
     the residual row sum of its bf16 key weights carries a false multiple of
     the keys' large mean into it (the GProj page's mechanism, in BoB's row
-    pass).  Asserted:
-      * with the projection (attn_bob with gproj, and attn_hvp with gproj,
-        whose fused pass takes its weights over R(dS)): g_Q within the BoB
-        bound of the oracle, row by row;
-      * without it (attn_bob): the worst row at least 3 times further off;
+    pass); g_dO, whose weights of V sum to zero too, the same along O.
+    Asserted:
+      * with the projections (attn_bob with gproj, and attn_hvp with gproj,
+        whose fused pass takes g_Q's weights over R(dS)): g_Q and g_dO
+        within the BoB bound of the oracle, row by row;
+      * without them (attn_bob): g_Q's worst row at least 3 times further
+        off, g_dO's further off;
       * the fused call's other outputs bit for bit equal to the separate
-        calls'; g_K, g_V, g_dO within the BoB bound as whole tensors (their
-        worst rows are printed: the column pass rounds each weight once, so
-        this mechanism does not reach them)."""
+        calls'; g_K, g_V (unchanged by the flag) within the BoB bound as
+        whole tensors, worst rows printed."""
     import json
     import os
     import fwd_bwd_double_amd as fbd
@@ -166,22 +167,28 @@ def test_gproj_projection_of_bob_gq_in_the_large_key_regime(tau_key):
     for name, got, ref in (("O", r["O"], o), ("LSE", r["LSE"], lse), ("dQ", r["dQ"], dq),
                            ("dK", r["dK"], dk), ("dV", r["dV"], dv), ("Hv_k", r["Hv_k"], gk),
                            ("Hv_v", r["Hv_v"], gv), ("Hv_do", r["Hv_do"], gdo),
-                           ("g_K without projection", gk0, gk), ("g_V", gv0, gv),
-                           ("g_dO", gdo0, gdo)):
+                           ("g_K without projection", gk0, gk), ("g_V", gv0, gv)):
         assert torch.equal(got, ref), name
-    say("    the projection changes g_Q only; the fused call's other outputs equal the "
-        "separate calls' bit for bit")
+    say("    the projections change g_Q and g_dO only; the fused call's other outputs "
+        "equal the separate calls' bit for bit")
     f64 = synthetic.to_f64
     ref = oracle.bob(a["q"], a["k"], a["v"], a["do"], a["g_dq"], a["g_dk"], a["g_dv"],
                      causal=True, scale=w.scale)
     check("Hv_q (fused, projected) against the oracle", f64(r["Hv_q"]), ref["gQ"], 5e-2)
     check("attn_bob g_Q (projected) against the oracle", f64(gq), ref["gQ"], 5e-2)
+    check("Hv_do (fused, projected) against the oracle", f64(r["Hv_do"]), ref["gdO"], 5e-2)
+    check("attn_bob g_dO (projected) against the oracle", f64(gdo), ref["gdO"], 5e-2)
     w0 = float(row_errors(f64(gq0), ref["gQ"]).max())
     w1 = float(row_errors(f64(gq), ref["gQ"]).max())
     say(f"    attn_bob g_Q without the projection: rel-L2 {rel_l2(f64(gq0), ref['gQ']):.3e}, "
         f"worst row {w0:.3e} ({w0 / w1:.1f} x the projected)")
     assert w0 >= 3 * w1, (w0, w1)
-    for key, got in (("g_K", gk), ("g_V", gv), ("g_dO", gdo)):
+    o0 = float(row_errors(f64(gdo0), ref["gdO"]).max())
+    o1 = float(row_errors(f64(gdo), ref["gdO"]).max())
+    say(f"    attn_bob g_dO without the projection: rel-L2 "
+        f"{rel_l2(f64(gdo0), ref['gdO']):.3e}, worst row {o0:.3e} ({o0 / o1:.1f} x the projected)")
+    assert o0 > o1, (o0, o1)
+    for key, got in (("g_K", gk), ("g_V", gv)):
         e = rel_l2(f64(got), ref[key[0] + key[2:]])
         say(f"    {key}: rel-L2 {e:.3e} (tol 5e-02), worst row "
             f"{float(row_errors(f64(got), ref[key[0] + key[2:]]).max()):.3e}")
