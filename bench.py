@@ -21,7 +21,7 @@ algorithmic bytes), the backward's time with GProj off and on, and the same
 step's outputs from the one Hessian-vector-product call (`hvp_fused`:
 attn_hvp with the BoB cotangents as the direction, whose single row pass
 finishes BoB's row outputs and the backward's dQ together), with its time and
-whether its outputs equal the separate calls'.
+how its outputs compare with the separate calls'.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
                     [--no-extra] [--workload NAME]
@@ -294,8 +294,10 @@ def hvp_fused(st, reps, ms_sep, rep):
     backward's and BoB's column passes.  Median ms of `reps` calls (HIP events
     on the launch stream), the rate under the same FLOP convention as the
     step, and the comparison of its outputs with the separate calls' (the
-    step just run): O, LSE, dQ, dK, dV, Hv_K, Hv_V, Hv_dO bit for bit, Hv_Q
-    as rel-L2."""
+    step just run): O, LSE, dQ, dK, dV, Hv_K, Hv_V bit for bit; Hv_Q and
+    Hv_dO as rel-L2 (GProj in the Hessian-vector product also projects
+    their bf16 weights' residual row sums, which the step's attn_bob does
+    not, and the fused pass regroups Hv_Q's alpha term)."""
     import numpy as np
     import torch
     g, f, w = st.g, st.fbd, st.w
@@ -307,8 +309,9 @@ def hvp_fused(st, reps, ms_sep, rep):
     torch.cuda.synchronize()
     same = {k: bool(torch.equal(r[k], t)) for k, t in (
         ("O", st.o), ("LSE", st.lse), ("dQ", st.dq), ("dK", st.dk), ("dV", st.dv),
-        ("Hv_k", st.gk), ("Hv_v", st.gv), ("Hv_do", st.gdo))}
-    dif = (r["Hv_q"].double() - st.gq.double()).norm() / st.gq.double().norm()
+        ("Hv_k", st.gk), ("Hv_v", st.gv))}
+    rel = lambda x, y: float((x.double() - y.double()).norm() / y.double().norm())
+    dif, dif_do = rel(r["Hv_q"], st.gq), rel(r["Hv_do"], st.gdo)
     del r
     times = []
     for _ in range(reps):
@@ -321,9 +324,11 @@ def hvp_fused(st, reps, ms_sep, rep):
     ms = float(np.median(times))
     conv = sum(CONV[op] for op in ("fwd", "bwd", "bob")) * w.d * rep["pairs"]
     out = {"ms": ms, "conv_tflops": conv / (ms * 1e-3) / 1e12, "separate_ms_per_step": ms_sep,
-           "speedup": ms_sep / ms, "bit_identical": same, "hv_q_rel_l2_vs_separate": float(dif)}
+           "speedup": ms_sep / ms, "bit_identical": same, "hv_q_rel_l2_vs_separate": dif,
+           "hv_do_rel_l2_vs_separate": dif_do}
     log(f"{w.name} fused HVP: {ms:.3f} ms ({out['conv_tflops']:.1f} TFLOP/s), "
-        f"{out['speedup']:.3f}x the separate calls; identical {same}; Hv_q rel-L2 {dif:.2e}")
+        f"{out['speedup']:.3f}x the separate calls; identical {same}; Hv_q rel-L2 {dif:.2e}, "
+        f"Hv_do rel-L2 {dif_do:.2e}")
     return out
 
 
