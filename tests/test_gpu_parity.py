@@ -264,6 +264,33 @@ def test_large_key_gproj(which):
     assert resid["gproj=0"] >= 3 * resid["gproj=1"], resid
 
 
+@pytest.mark.parametrize("which", ["tau", "tau_strict"])
+def test_large_key_gproj_full_tensors(which):
+    """The large-key regime at a size the oracle runs whole (B1 H2 N1024, the
+    same generator and tau as the 16384-token test): with GProj every row of
+    dQ and every key of dK, dV within 2e-2 and the per-row bound; without
+    it, dQ's worst row at least 5 times further off (the residual row mass
+    of the bf16 dS carried into dQ along the keys' mean)."""
+    import json
+    import os
+    from gpu_util import row_errors
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "large_key_tau.json")))
+    w = W[3].with_(name=f"large-key-full-{which}", H=2, N=1024, tau=float(gold[which]))
+    x, g, a = inputs(w, ("q", "k", "v", "do"))
+    ref = oracle.bwd(a["q"], a["k"], a["v"], a["do"], causal=True, scale=w.scale)
+    r0 = run_all(w, g, gproj=False, ops=("fwd", "bwd"))
+    r1 = run_all(w, g, gproj=True, ops=("fwd", "bwd"))
+    say(f"[gpu] large-key full tensors: tau={w.tau} B1 H2 N1024")
+    for key in ("dQ", "dK", "dV"):
+        check(f"{key} with GProj", r1[key], ref[key], 2e-2)
+    w0 = float(row_errors(r0["dQ"], ref["dQ"]).max())
+    w1 = float(row_errors(r1["dQ"], ref["dQ"]).max())
+    say(f"    dQ without GProj: rel-L2 {rel_l2(r0['dQ'], ref['dQ']):.3e}, worst row {w0:.3e} "
+        f"({w0 / w1:.0f} x with GProj)")
+    assert w0 >= 5 * w1, (w0, w1)
+
+
 # ------------------------- workload 5: BoB at N = 262144, sampled oracle
 @pytest.mark.timeout(600)
 def test_long_context_bob_sampled():
