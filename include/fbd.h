@@ -2,7 +2,8 @@
  * fbd.h -- exact causal multi-head softmax attention on MI355X (gfx950):
  * forward, backward (optionally with GProj), backward-over-backward and the
  * Hessian-vector product built from them; extended forms with shared keys
- * and values (grouped-query attention), a sliding window and document masks.
+ * and values (grouped-query attention), a sliding window, document masks and
+ * block-sparse masks; a forward on the E4M3 matrix cores.
  *
  * C ABI of libfbd.so.  No torch or C++ types cross this boundary: plain
  * integers, floats and pointers.
@@ -16,7 +17,8 @@
  * heads instead of H.  Only d = 64 is supported; any N >= 1 is.
  *
  * Pointers.  Every array pointer is a DEVICE pointer owned by the caller,
- * 16-byte aligned (the int32 doc_start of the extended forms: 4-byte).  The library never allocates, frees, synchronises, or reads
+ * 16-byte aligned (the int32 doc_start of the extended forms: 4-byte; the
+ * uint8 block_mask: any).  No call allocates, frees, synchronises, or reads
  * device memory from the host.  Inputs are never written.  Outputs are fully
  * overwritten (never accumulated into) and must not overlap any input, any
  * other output or the workspace.
