@@ -134,3 +134,38 @@ def run_all(w, g, gproj=False, ops=("fwd", "bwd", "bob")):
 def inputs(w, names=("q", "k", "v", "do", "g_dq", "g_dk", "g_dv")):
     x = make_inputs(w, names)
     return x, to_gpu(x), f64(x)
+
+
+def doc_starts(B, N, seed, mean_len):
+    """Seeded packed-document layout: (B, N) int first position of each row's
+    document, document lengths ~ geometric with the given mean (some of
+    length 1)."""
+    rng = np.random.default_rng(seed)
+    out = np.zeros((B, N), dtype=np.int64)
+    for b in range(B):
+        i = 0
+        while i < N:
+            n = int(min(N - i, rng.geometric(1.0 / mean_len)))
+            out[b, i:i + n] = i
+            i += n
+    return out
+
+
+def block_masks(B, N, seed, density, keep_diag):
+    """Seeded (B, nb, nb) uint8 block mask, nb = ceil(N / 128): each block kept
+    with the given probability; the diagonal blocks kept when asked."""
+    rng = np.random.default_rng(seed)
+    nb = (N + 127) // 128
+    m = (rng.random((B, nb, nb)) < density).astype(np.uint8)
+    if keep_diag:
+        m[:, np.arange(nb), np.arange(nb)] = 1
+    return m
+
+
+def check_lse_with_empty_rows(got, ref, t):
+    """Rows with no visible key have LSE = -inf on both sides; the others are
+    compared by rel-L2."""
+    empty = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), empty), "empty rows differ"
+    say(f"    empty rows: {int(empty.sum())}")
+    check("LSE", got[~empty], ref[~empty], t)

@@ -18,7 +18,7 @@ import torch
 import fwd_bwd_double_amd as fbd
 import oracle
 import synthetic
-from gpu_util import rel_l2, say
+from gpu_util import block_masks, doc_starts, rel_l2, say
 from oracle import fp8
 from synthetic import to_f64
 
@@ -258,7 +258,6 @@ MASK_CASES = [("window", 333, 50, 0, None, 2, 2), ("docs", 1000, 0, 150, None, 2
 def test_forward_masks(name, N, window, mean_len, density, H, Hkv, dtype):
     """The FP8 forward under the bf16 forward's masks: sliding window, packed
     documents, block-sparse (with rows left empty) and all three together."""
-    from test_gpu_parity import block_masks, doc_starts
     B = 2
     say(f"[gpu] fp8 masks {name} B={B} H={H} Hkv={Hkv} N={N} window={window} "
         f"docs={mean_len} density={density} {dtype}")

@@ -20,8 +20,7 @@ import torch
 
 import oracle
 import synthetic
-from gpu_util import check, inputs, say
-from test_gpu_parity import block_masks, doc_starts
+from gpu_util import block_masks, check, doc_starts, inputs, say
 
 pytestmark = pytest.mark.gpu
 

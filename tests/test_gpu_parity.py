@@ -7,7 +7,8 @@ import torch
 
 import oracle
 import synthetic
-from gpu_util import check, inputs, rel_l2, run_all, say, tol
+from gpu_util import (block_masks, check, check_lse_with_empty_rows, doc_starts, inputs,
+                      rel_l2, run_all, say, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -548,21 +549,6 @@ def test_sliding_window(N, window, H, Hkv, dtype):
 
 
 # -------------------------------------- document masks (packed sequences)
-def doc_starts(B, N, seed, mean_len):
-    """Seeded packed-document layout: (B, N) int first position of each row's
-    document, document lengths ~ geometric with the given mean (some of
-    length 1)."""
-    rng = np.random.default_rng(seed)
-    out = np.zeros((B, N), dtype=np.int64)
-    for b in range(B):
-        i = 0
-        while i < N:
-            n = int(min(N - i, rng.geometric(1.0 / mean_len)))
-            out[b, i:i + n] = i
-            i += n
-    return out
-
-
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("N,mean_len,window,H,Hkv", [(300, 40, 0, 2, 2), (1000, 150, 0, 4, 2),
                                                      (1000, 300, 64, 2, 1),
@@ -655,26 +641,6 @@ def test_wide_row_blocks_long_sequence(case):
             check("dV last 256 keys", f64(dv)[0][:, -256:], tail["dV"], 2e-2)
 
 # ------------------------------------------ block-sparse masks (128 x 128 blocks)
-def block_masks(B, N, seed, density, keep_diag):
-    """Seeded (B, nb, nb) uint8 block mask, nb = ceil(N / 128): each block kept
-    with the given probability; the diagonal blocks kept when asked."""
-    rng = np.random.default_rng(seed)
-    nb = (N + 127) // 128
-    m = (rng.random((B, nb, nb)) < density).astype(np.uint8)
-    if keep_diag:
-        m[:, np.arange(nb), np.arange(nb)] = 1
-    return m
-
-
-def check_lse_with_empty_rows(got, ref, t):
-    """Rows with no visible key have LSE = -inf on both sides; the others are
-    compared by rel-L2."""
-    empty = np.isneginf(ref)
-    assert np.array_equal(np.isneginf(got), empty), "empty rows differ"
-    say(f"    empty rows: {int(empty.sum())}")
-    check("LSE", got[~empty], ref[~empty], t)
-
-
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("N,causal,density,keep_diag,window,mean_len,H,Hkv", [
     (300, True, 0.6, True, 0, 0, 2, 2),
