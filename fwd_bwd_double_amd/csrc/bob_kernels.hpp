@@ -21,38 +21,42 @@
 // everything else is linear in them, so the pass accumulates four fp32
 // d-vectors per row
 //   XE = sum_j R(P (W (dP - D) + U)) K_j + R(dS) Bk_j,   Y = sum_j R(P) K_j,
-//   Z  = sum_j R(P dP) K_j,   FG = sum_j R(P W) V_j + R(P) C_j,
+//   Z  = sum_j R(dS) K_j,   FG = sum_j R(P W) V_j + R(P) C_j,
 // plus the row sums alpha_i and x_i = sum_j P (W (dP - D) + U) (the fp32
 // values whose bf16 roundings feed XE), and after the last key block applies
 // the corrections once:
 //   beta_i = b_i - 2 alpha_i D_i = x_i - alpha_i D_i   (b_i = sum_j P (W dP + U)),
-//   gQ = scale (XE - alpha Z - beta Y),   gdO = FG - alpha O
-// (sum_j P_ij V_j = O_i).  It writes gQ, gdO and the row states D, alpha, beta.
+//   kappa_i = alpha_i D_i + beta_i,
+//   gQ = scale (XE - alpha Z - kappa Y),   gdO = FG - alpha O
+// (sum_j P_ij V_j = O_i).  The alpha term of gQ is alpha sum_j P dP K_j; since
+// P dP = dS + D P it is taken as alpha (Z + D Y), with the D Y part joining
+// beta's Y term as kappa.  The Z operand is then the dS values the Bk product
+// packs anyway, and dS, unlike P dP, sums to zero over a row.  The pass
+// writes gQ, gdO and the row states D, alpha, beta, -kappa.
 //
-// Fused with the first backward's row pass (when the cotangents are known
-// before the backward runs, as in a Hessian-vector product), Z is taken over
-// R(dS) instead: since P dP = dS + D P, alpha Z moves its alpha D Y part into
-// the Y term, gQ = scale (XE - alpha Z' - kappa Y) with kappa = alpha D + beta.
-// Z' = sum_j R(dS) K and Y = sum_j R(P) K are then exactly the backward row
-// pass's two accumulators, so the same registers also give
-//   dQ = scale (Z' - r Y)  with GProj (r_i = sum_j R(dS_ij)),  scale Z' without,
+// Fused with the first backward's row pass (EMIT: when the cotangents are
+// known before the backward runs, as in a Hessian-vector product), Z and Y
+// are exactly the backward row pass's two accumulators, so the same
+// registers also give
+//   dQ = scale (Z - r Y)  with GProj (r_i = sum_j R(dS_ij)),  scale Z without,
 // for one row sum of the packed bf16 dS values per tile.
 //
 // GProj for g_Q (PROJ; the GProj page's projection, section "How a zero sum
 // turns into a false gradient", carried over to this pass).  The K-side
-// weights of g_Q, Sh = P (W (dP - D) + U) - alpha P dP - beta P, sum to
-// exactly zero over a row (sum_j P dP = D, sum_j P = 1), but the pass feeds
-// their three parts to the matrix cores as separate bf16 operands and
-// combines them after the sums; the residual row sum of those operands,
-//   r_Sh = sum R(x) - alpha sum R(P dP) - beta sum R(P)
-// (R(dS) and kappa in place of R(P dP) and beta when fused), carries a false
-// multiple of the keys' mean into g_Q, large when the keys share a large mean
-// and rows are near one-hot.  With PROJ it is removed along R(P) K:
-//   g_Q = scale (XE - alpha Z - (beta + r_Sh) Y).
+// weights of g_Q, Sh = P (W (dP - D) + U) - alpha dS - kappa P, sum to
+// exactly zero over a row (sum_j dS = 0, sum_j P = 1, sum_j P (W (dP - D) + U)
+// = beta + alpha D = kappa), but the pass feeds their three parts to the
+// matrix cores as separate bf16 operands and combines them after the sums;
+// the residual row sum of those operands,
+//   r_Sh = sum R(x) - alpha r - kappa sum R(P),
+// carries a false multiple of the keys' mean into g_Q, large when the keys
+// share a large mean and rows are near one-hot.  With PROJ it is removed
+// along R(P) K:
+//   g_Q = scale (XE - alpha Z - (kappa + r_Sh) Y).
 // g_dO's weights of V, P (W - alpha), sum to zero over a row as well; the pass
 // forms g_dO = sum R(P W) V + R(P) C - alpha O, so their residual is
 // r_H = sum R(P W) - alpha, removed along O:  g_dO = FG - (alpha + r_H) O.
-// Four (fused: three more) v_dot2 row sums over operands the pass packs anyway.
+// Four v_dot2 row sums over operands the pass packs anyway.
 //
 // Column pass (lane = key j).  K, V, Bk, C of the workgroup's keys stay in
 // registers; query blocks stream past them with their row states, and
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   f32x16 X0 = zero16(), X1 = zero16(), Y0 = zero16(), Y1 = zero16();
   f32x16 Z0 = zero16(), Z1 = zero16(), F0 = zero16(), F1 = zero16();
   float alpha = 0.f, xsum = 0.f, r = 0.f;
-  float sx = 0.f, sz = 0.f, sp = 0.f, sf = 0.f;   // row sums of the bf16 operands (PROJ)
+  float sx = 0.f, sp = 0.f, sf = 0.f;   // row sums of the bf16 operands (PROJ)
 
   // keys of the block's rows: causal j <= i, from each row's start (sliding
   // window, document); the block's first row has the smallest start
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         mma(dp, vr, dof[kb]);
         mma(u, ld_row(Cs, jb, kb, lane), dof[kb]);
       }
-      float xs[16], ps[16], zs[16], es[16], fs[16];
+      float xs[16], ps[16], es[16], fs[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) ps[v] = __builtin_amdgcn_exp2f(s[v] * sl2 - lse2);
       if constexpr (MASK) {
@@ -195,7 +199,6 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
         alpha += pw;
         xs[v] = pv * (W * dpd + u[v]);
         xsum += xs[v];
-        if constexpr (!EMIT) zs[v] = pv * dp[v];
         es[v] = pv * dpd;
         fs[v] = pw;
       }
@@ -204,14 +207,12 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
       for (int tt = 0; tt < 2; ++tt) {
         const Frag<T> xf = pack8<T>(xs + 8 * tt), pf = pack8<T>(ps + 8 * tt);
         const Frag<T> ef = pack8<T>(es + 8 * tt);
-        const Frag<T> zf = EMIT ? ef : pack8<T>(zs + 8 * tt);
         const Frag<T> ff = pack8<T>(fs + 8 * tt);
-        if constexpr (EMIT) r = frag_acc_sum(ef, r);   // v_dot2 on the bf16 pairs
+        if constexpr (EMIT || PROJ) r = frag_acc_sum(ef, r);   // v_dot2 on the bf16 pairs
         if constexpr (PROJ) {
           sx = frag_acc_sum(xf, sx);
           sp = frag_acc_sum(pf, sp);
           sf = frag_acc_sum(ff, sf);
-          if constexpr (!EMIT) sz = frag_acc_sum(zf, sz);
         }
         {
           const Frag<T> a0 = ld_tr(Ks, 0, jt + tt, lane), a1 = ld_tr(Ks, 32, jt + tt, lane);
@@ -219,8 +220,8 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
           mma(X1, a1, xf);
           mma(Y0, a0, pf);
           mma(Y1, a1, pf);
-          mma(Z0, a0, zf);
-          mma(Z1, a1, zf);
+          mma(Z0, a0, ef);
+          mma(Z1, a1, ef);
         }
         {
           const Frag<T> a0 = ld_tr(Bs, 0, jt + tt, lane), a1 = ld_tr(Bs, 32, jt + tt, lane);
@@ -257,11 +258,11 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   // every variant of the pass rounds them alike (the column pass reads -kappa)
   const float beta = __builtin_fmaf(-alpha, Di, xsum);
   const float kappa = __builtin_fmaf(alpha, Di, beta);
-  if constexpr (EMIT) r = half_sum(r);
-  float ycoef = EMIT ? kappa : beta;   // Z over R(dS): kappa
+  if constexpr (EMIT || PROJ) r = half_sum(r);
+  float ycoef = kappa;   // Z over R(dS)
   float ocoef = alpha;                 // coefficient of O in g_dO
   if constexpr (PROJ) {
-    ycoef += half_sum(sx) - alpha * (EMIT ? r : half_sum(sz)) - ycoef * half_sum(sp);
+    ycoef += half_sum(sx) - alpha * r - ycoef * half_sum(sp);
     ocoef = half_sum(sf);               // alpha + r_H
   }
   float out[16], ov[16];
