@@ -249,16 +249,18 @@ attn_status attn_bob_passes(int passes, attn_dtype dt, int64_t B, int64_t H, int
  * convention for an empty softmax row).
  *
  * gproj != 0 in attn_bob_ex carries GProj (GProj page, section "How a zero
- * sum turns into a false gradient") over to g_Q.  The weights of K in g_Q,
- *   Sh = P o (W o (dP - D) + U) - alpha P o dP - beta P,
- * sum to exactly zero over each row, but the row pass sends their three
- * parts to the matrix cores as separate bf16 operands and combines them after
- * the sums over keys; the residual row sum r_Sh of those operands (taken over
- * exactly the bf16 values) would carry a false multiple of the keys' mean into
- * g_Q, large where the keys share a large mean and rows are near one-hot (the
- * GProj page's large-key regime).  With gproj it is removed along R(P) K:
- *   g_Q = scale * (sum_j R(x) K + R(dS) B_K - alpha sum_j R(P o dP) K
- *                  - (beta + r_Sh) sum_j R(P) K).
+ * sum turns into a false gradient") over to g_Q.  The row pass writes the
+ * weights of K in g_Q as
+ *   Sh = P o (W o (dP - D) + U) - alpha dS - kappa P,   kappa = alpha D + beta
+ * (P o dP = dS + D P), three parts that sum to exactly zero over each row;
+ * it sends them to the matrix cores as separate bf16 operands, x = P o (W o
+ * (dP - D) + U), dS and P, and combines them after the sums over keys.  The
+ * residual row sum r_Sh of those operands (taken over exactly the bf16
+ * values) would carry a false multiple of the keys' mean into g_Q, large
+ * where the keys share a large mean and rows are near one-hot (the GProj
+ * page's large-key regime).  With gproj it is removed along R(P) K:
+ *   g_Q = scale * (sum_j R(x) K + R(dS) B_K - alpha sum_j R(dS) K
+ *                  - (kappa + r_Sh) sum_j R(P) K).
  * g_dO's weights of V, P o (W - alpha), also sum to zero over each row; the
  * pass forms g_dO = sum_j R(P o W) V + R(P) C - alpha O, and with gproj their
  * residual r_H = sum_j R(P o W) - alpha is removed along O:
@@ -323,15 +325,13 @@ attn_status attn_bob_ex(attn_dtype dt, int64_t B, int64_t H, int64_t Hkv, int64_
  *      network-level product adds through dO's own dependence on the inputs.
  * dQ, dK and dV are all NULL (gradient not computed) or all set.  Every
  * output is overwritten.  With bf16 operands and the gradient requested, the
- * backward's row pass is not run on its own: the BoB row pass takes its
- * query-side sum over the bf16 dS values, sum_j R(dS_ij) K_j, in place of
- * sum_j R(P_ij dP_ij) K_j (P dP = dS + D P, so the difference moves into the
- * R(P) K term's coefficient), and those two sums are exactly the backward row
- * pass's dQ terms; it writes dQ, then the backward's and BoB's column passes
- * run.  dQ, dK, dV come out as attn_bwd's; H v agrees with attn_bob_ex's
- * within rounding.  gproj != 0 also applies attn_bob_ex's projections of
- * Hv_Q's and Hv_dO's residual row sums (the same flag as attn_bob_ex's gproj;
- * with the fused row pass Hv_Q's residual is taken over R(dS) and kappa).
+ * backward's row pass is not run on its own: the BoB row pass already sums
+ * sum_j R(dS_ij) K_j and sum_j R(P_ij) K_j, which are exactly the backward
+ * row pass's dQ terms; it writes dQ, then the backward's and BoB's column
+ * passes run.  gproj != 0 also applies attn_bob_ex's projections of Hv_Q's
+ * and Hv_dO's residual row sums (the same flag as attn_bob_ex's gproj).  dQ,
+ * dK, dV come out as attn_bwd's, and H v as attn_bob_ex's with the same
+ * gproj, bit for bit.
  * ws must hold attn_hvp_workspace_bytes(B, H, N) bytes (six fp32
  * values per row); afterwards it starts with the BoB row states as after
  * attn_bob (D, alpha, beta, -LSE log2(e), -kappa), followed by the GProj row
