@@ -73,10 +73,22 @@
 
 namespace fbd {
 
+// Resident workgroups per CU of the row pass.  The bf16 causal forms without
+// a block mask run two (two waves per SIMD): their Q, dO and g_dQ fragments
+// then sit in LDS (48 KB per workgroup, 80 KB with the tile buffers) and are
+// read for each product, a latency the other wave hides.  The other forms keep
+// those fragments in registers at one wave per SIMD: with a block mask the
+// two-wave kernel spills a few registers, without the causal mask hundreds,
+// and with the fragments in LDS but one wave per SIMD the pass is slower.
+template <class T, bool CAUSAL, bool BMASK>
+constexpr int bob_row_occ() {
+  return (sizeof(T) == 2 && CAUSAL && !BMASK) ? 2 : FBD_BOB_ROW_OCC;
+}
+
 // EMIT: also write the first backward's dQ and its GProj row sums r (Rws);
 // PROJ: project the residual row sum of g_Q's K-side weights (above)
 template <class T, int BN, bool CAUSAL, bool DOCS, bool BMASK, bool EMIT, bool PROJ>
-__global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
+__global__ __launch_bounds__(NT, (bob_row_occ<T, CAUSAL, BMASK>())) void bob_row_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ O, const float* __restrict__ LSE, const T* __restrict__ dO,
     const T* __restrict__ A, const T* __restrict__ Bk, const T* __restrict__ C,
@@ -91,6 +103,9 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   };
   __shared__ __attribute__((aligned(16))) Buf B0;
   __shared__ __attribute__((aligned(16))) Buf B1;
+  // the Q, dO, g_dQ fragments of the two-wave form: [operand][wave][kb][lane]
+  constexpr bool OPS_LDS = bob_row_occ<T, CAUSAL, BMASK>() == 2;
+  __shared__ __attribute__((aligned(16))) Frag<T> Ops[OPS_LDS ? 3 : 1][NT / 64][4][64];
 
   const Work wk = row_work(BH, nblk);
   const size_t hoff = (size_t)wk.head * N * HD;
@@ -112,6 +127,27 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
   ld_frags(Q + hoff, N, qw, lane, qf);
   ld_frags(dO + hoff, N, qw, lane, dof);
   ld_frags(A + hoff, N, qw, lane, af);
+  if constexpr (OPS_LDS) {
+    // each lane reads back only what it wrote: no barrier needed
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      Ops[0][wave][kb][lane] = qf[kb];
+      Ops[1][wave][kb][lane] = dof[kb];
+      Ops[2][wave][kb][lane] = af[kb];
+    }
+  }
+  auto opq = [&](int kb) -> const Frag<T>& {
+    if constexpr (OPS_LDS) return Ops[0][wave][kb][lane];
+    else return qf[kb];
+  };
+  auto opdo = [&](int kb) -> const Frag<T>& {
+    if constexpr (OPS_LDS) return Ops[1][wave][kb][lane];
+    else return dof[kb];
+  };
+  auto opa = [&](int kb) -> const Frag<T>& {
+    if constexpr (OPS_LDS) return Ops[2][wave][kb][lane];
+    else return af[kb];
+  };
   float Di;
   {
     Frag<T> of[4];
@@ -166,19 +202,19 @@ __global__ __launch_bounds__(NT, FBD_BOB_ROW_OCC) void bob_row_kernel(
       auto sub = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // the compiler's single-wave interleave of matrix products and LDS
-        // reads (one wave per SIMD leaves no other wave to hide latency),
-        // measured 3% faster than its default schedule here
+        // reads (at one wave per SIMD no other wave hides latency), measured
+        // 3% faster than its default schedule there
         __builtin_amdgcn_iglp_opt(1);
       f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const Frag<T> kr = ld_row(Ks, jb, kb, lane);
-        mma(s, kr, qf[kb]);
-        mma(w, kr, af[kb]);
-        mma(w, ld_row(Bs, jb, kb, lane), qf[kb]);
+        mma(s, kr, opq(kb));
+        mma(w, kr, opa(kb));
+        mma(w, ld_row(Bs, jb, kb, lane), opq(kb));
         const Frag<T> vr = ld_row(Vs, jb, kb, lane);
-        mma(dp, vr, dof[kb]);
-        mma(u, ld_row(Cs, jb, kb, lane), dof[kb]);
+        mma(dp, vr, opdo(kb));
+        mma(u, ld_row(Cs, jb, kb, lane), opdo(kb));
       }
       float xs[16], ps[16], es[16], fs[16];
 #pragma unroll
