@@ -73,16 +73,16 @@
 
 namespace fbd {
 
-// Resident workgroups per CU of the row pass.  The bf16 causal forms without
-// a block mask run two (two waves per SIMD): their Q, dO and g_dQ fragments
-// then sit in LDS (48 KB per workgroup, 80 KB with the tile buffers) and are
-// read for each product, a latency the other wave hides.  The other forms keep
-// those fragments in registers at one wave per SIMD: with a block mask the
-// two-wave kernel spills a few registers, without the causal mask hundreds,
-// and with the fragments in LDS but one wave per SIMD the pass is slower.
+// Resident workgroups per CU of the row pass.  The bf16 causal forms run two
+// (two waves per SIMD): their Q, dO and g_dQ fragments then sit in LDS (48 KB
+// per workgroup, 80 KB with the tile buffers) and are read for each product,
+// a latency the other wave hides.  The other forms keep those fragments in
+// registers at one wave per SIMD: without the causal mask the two-wave kernel
+// spills hundreds of registers, and with the fragments in LDS but one wave
+// per SIMD the pass is slower.
 template <class T, bool CAUSAL, bool BMASK>
 constexpr int bob_row_occ() {
-  return (sizeof(T) == 2 && CAUSAL && !BMASK) ? 2 : FBD_BOB_ROW_OCC;
+  return (sizeof(T) == 2 && CAUSAL) ? 2 : FBD_BOB_ROW_OCC;
 }
 
 // EMIT: also write the first backward's dQ and its GProj row sums r (Rws);
