@@ -202,8 +202,10 @@ __global__ __launch_bounds__(NT, (bob_row_occ<T, CAUSAL, BMASK>())) void bob_row
       auto sub = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // the compiler's single-wave interleave of matrix products and LDS
-        // reads (at one wave per SIMD no other wave hides latency), measured
-        // 3% faster than its default schedule there
+        // reads: at one wave per SIMD (no other wave hides latency) 3% faster
+        // than its default schedule; in the two-wave form, whose score
+        // products read their query-side operand from LDS, the default
+        // schedule is more than twice as slow
         __builtin_amdgcn_iglp_opt(1);
       f32x16 s = zero16(), dp = zero16(), w = zero16(), u = zero16();
 #pragma unroll
